@@ -1,0 +1,100 @@
+"""Decode attention over the packed cache (oracle; test infrastructure).
+
+[Spec] "Optimization: Fused dequant-dot": pre-rotate the query once, take the dot
+product of the rotated query with the centroid look-ups of each cached key (no
+inverse transform per cached vector, because <q, R^T k'> = <R q, k'>), accumulate
+the softmax-weighted centroid look-ups of the values in the rotated domain, and
+inverse-rotate the output once.  [Rotor] "The QJL Estimator Formula" writes the
+same first term as norm * sum_d(Q_rot[d] * centroids[idx[s, d]]); the QJL term is
+not part of this path.
+
+``attend_fused`` computes exactly that in fp64:
+
+    q' = R q;  s_t = scale * sum_blk nK[t, blk] <q'_blk, cK[codeK_t, blk]>;
+    p = softmax(s over t < len);  o' = sum_t p_t nV[t, blk] cV[codeV_t, blk];
+    o = R^T o'.
+
+Readings: the GQA head map is g = floor(h / (Hq / Hkv)) (not on the pages); a
+sequence of length 0 gives an all-zero output; the scale is a caller argument
+(1/sqrt(128) for the pages' workloads).
+
+``attend_bruteforce`` is the plain definition softmax(scale q K_hat^T) V_hat on the
+decoded cache (``codec.decode_mse``), used to pin ``attend_fused``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import decode_mse, unpack
+from .rotation import QK, forward64, inverse64
+
+
+def _softmax64(s: np.ndarray) -> np.ndarray:
+    m = np.max(s)
+    e = np.exp(s - m)
+    return e / np.sum(e)
+
+
+def attend_fused(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits,
+                 k_centroids, v_centroids, s, scale, heads=None):
+    """fp64 fused rotated-domain attention.
+
+    q: [B, Hq, d] (any float dtype), k_codes/v_codes: [B, Hkv, T, nblk, cb] uint8,
+    k_norms/v_norms: [B, Hkv, T, nblk] float16, seq_lens: [B] ints.
+    ``heads`` optionally restricts the computation to a list of (b, h) pairs; the
+    rows not computed are left at zero.  Returns out [B, Hq, d] float64.
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_codes.shape[1]
+    grp = Hq // Hkv
+    nblk = d // QK
+    ck = np.asarray(k_centroids, np.float32).astype(np.float64)
+    cv = np.asarray(v_centroids, np.float32).astype(np.float64)
+    out = np.zeros((B, Hq, d), np.float64)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    cache = {}
+    for b, h in heads:
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        g = h // grp
+        if (b, g) not in cache:
+            kc = ck[unpack(k_codes[b, g, :L], k_bits)].reshape(L, nblk, QK)
+            vc = cv[unpack(v_codes[b, g, :L], v_bits)].reshape(L, nblk, QK)
+            kn = np.asarray(k_norms[b, g, :L], np.float16).astype(np.float64)
+            vn = np.asarray(v_norms[b, g, :L], np.float16).astype(np.float64)
+            cache = {(b, g): (kc, vc, kn, vn)}
+        kc, vc, kn, vn = cache[(b, g)]
+        qr = forward64(q[b, h], s).reshape(nblk, QK)
+        dots = np.einsum("tjc,jc->tj", kc, qr)
+        scores = scale * np.sum(kn * dots, axis=-1)
+        p = _softmax64(scores)
+        o_rot = np.einsum("t,tj,tjc->jc", p, vn, vc)
+        out[b, h] = inverse64(o_rot.reshape(d), s)
+    return out
+
+
+def attend_bruteforce(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits,
+                      k_centroids, v_centroids, s, scale):
+    """softmax(scale * q K_hat^T) V_hat on the decoded cache, fp64 (tiny inputs)."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_codes.shape[1]
+    grp = Hq // Hkv
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        for h in range(Hq):
+            g = h // grp
+            kh = decode_mse(unpack(k_codes[b, g, :L], k_bits), k_norms[b, g, :L], s,
+                            k_centroids)
+            vh = decode_mse(unpack(v_codes[b, g, :L], v_bits), v_norms[b, g, :L], s,
+                            v_centroids)
+            p = _softmax64(scale * (kh @ q[b, h]))
+            out[b, h] = p @ vh
+    return out

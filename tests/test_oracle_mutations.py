@@ -1,0 +1,79 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each test patches one plausible error into the oracle and checks that a pin that
+does not share the oracle's code fails on the patched version.
+"""
+
+import numpy as np
+from scipy.linalg import hadamard as scipy_hadamard
+
+from oracle import attention as att
+from oracle import codebook as cbm
+from oracle import codec
+from oracle import rotation as rot
+from oracle import signs as sg
+
+
+def test_dropped_fwht_stage_is_caught(monkeypatch):
+    real = rot.fwht_stages
+
+    def short(x, dtype=np.float64):
+        y = np.array(x, dtype=dtype, copy=True)
+        d = y.shape[-1]
+        length = 1
+        while length < d // 2:          # stops one stage early
+            shaped = y.reshape(y.shape[:-1] + (d // (2 * length), 2, length))
+            u, v = shaped[..., 0, :], shaped[..., 1, :]
+            y = np.stack((u + v, u - v), axis=-2).reshape(y.shape)
+            length <<= 1
+        return y, 0
+
+    monkeypatch.setattr(rot, "fwht_stages", short)
+    y, _ = rot.fwht_stages(np.eye(128))
+    assert not np.array_equal(y, scipy_hadamard(128).astype(np.float64))
+    monkeypatch.setattr(rot, "fwht_stages", real)
+
+
+def test_wrong_sign_placement_is_caught():
+    d = 128
+    s = sg.signs(42, d).astype(np.float64)
+    H = rot.hadamard(d) / np.sqrt(d)
+    e = np.zeros(d)
+    e[3] = 1.0
+    after = s * (H @ e)                    # D applied after H
+    assert not np.allclose(after, s[3] * H[:, 3])
+    np.testing.assert_allclose(rot.forward64(e, s), s[3] * H[:, 3], atol=1e-15)
+
+
+def test_cell_midpoint_instead_of_conditional_mean_is_caught(monkeypatch):
+    """Replacing the centroid (conditional mean) by the cell midpoint breaks the
+    printed turboq2 centroids."""
+    def midpoint_moment(a, b, m):
+        return 0.5 * (np.asarray(a) + np.asarray(b)) * cbm._mass(a, b, m)
+
+    monkeypatch.setattr(cbm, "_first_moment", midpoint_moment)
+    _, c = cbm.codebook(2, 128)
+    assert not np.array_equal(np.round(c.astype(np.float64), 3), [-0.133, -0.040, 0.040, 0.133])
+
+
+def test_upper_tie_rule_is_caught():
+    """Ties must go to the lower level: a value equal to a boundary."""
+    b, _ = cbm.codebook(4)
+    u = b[10:11]
+    assert np.searchsorted(b, u, side="left")[0] == 10
+    assert np.searchsorted(b, u, side="right")[0] == 11
+
+
+def test_transposed_attention_operand_is_caught():
+    """Using the value codes for the scores (a swapped operand) breaks the brute-force pin."""
+    rng = np.random.default_rng(0)
+    d, T = 128, 9
+    s = sg.signs(42, d)
+    bk, ck = cbm.codebook(4)
+    kc, kn, _ = codec.encode_mse(rng.standard_normal((1, 1, T, d)).astype(np.float32), s, bk)
+    vc, vn, _ = codec.encode_mse(rng.standard_normal((1, 1, T, d)).astype(np.float32), s, bk)
+    kc, vc = codec.pack(kc, 4), codec.pack(vc, 4)
+    q = rng.standard_normal((1, 1, d))
+    good = att.attend_bruteforce(q, kc, kn, vc, vn, [T], 4, 4, ck, ck, s, 0.3)
+    swapped = att.attend_fused(q, vc, vn, vc, vn, [T], 4, 4, ck, ck, s, 0.3)
+    assert np.max(np.abs(good - swapped)) > 1e-3

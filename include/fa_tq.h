@@ -1,0 +1,171 @@
+/*
+ * fa_tq.h -- C ABI of the MI355X (gfx950) TurboQuant MSE KV-cache library.
+ *
+ * Pages cited by title and section:
+ *   [Spec]   "TurboQuant KV Cache Compression -- Spec"
+ *   [turboq] "TurboQuant KV Cache (turboq2 / turboq3 / turboq4)"
+ *
+ * Every symbol has C linkage.  No C++ exception, abort or torch type crosses this
+ * boundary: pointers are plain host or device addresses and sizes are integers.
+ *
+ * Ownership: the caller allocates and frees every buffer.  The library keeps no
+ * device state and allocates nothing on the device; device entry points are
+ * asynchronous on the caller's stream (a hipStream_t passed as void*, NULL = the
+ * null stream) and never synchronize the host.
+ *
+ * Errors: arguments are checked on the host before any launch.  A non-OK status
+ * launches nothing and leaves a message readable with fa_tq_last_error() (per host
+ * thread).  FA_TQ_EINVAL: a bad size, pointer, alignment or table; FA_TQ_EUNSUPPORTED:
+ * a valid combination this build has no kernel for; FA_TQ_EHIP: the HIP runtime
+ * reported an error at launch.  Faults inside a kernel surface at the caller's next
+ * synchronization, as for any HIP kernel.
+ *
+ * Packed-cache layout (structure of arrays; QK = 128-element blocks, nblk = d/128):
+ *   codes[B][Hkv][T_max][nblk][cb]   uint8, cb = fa_tq_code_bytes(bits)
+ *   norms[B][Hkv][T_max][nblk]       uint16 holding IEEE binary16 bits
+ * Bits inside a block are packed least-significant first: 2-bit 4 codes per byte;
+ * 3-bit as two planes (32 bytes of low two bits, then 16 bytes of the high bit);
+ * 4-bit 2 codes per byte; 8-bit one code per byte ([Spec] "Step 3: Packing";
+ * [turboq] "Block structures").  Every code row starts on a 16-byte boundary.
+ */
+#ifndef FA_TQ_H
+#define FA_TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_TQ_QK 128          /* elements per block ([turboq] "Block structures") */
+#define FA_TQ_MAX_HEAD_DIM 2048
+
+typedef enum {
+    FA_TQ_OK = 0,
+    FA_TQ_EINVAL = 1,
+    FA_TQ_EUNSUPPORTED = 2,
+    FA_TQ_EHIP = 3
+} fa_tq_status;
+
+typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
+
+/*
+ * Scalar quantizer for one 128-element block ([Spec] "Step 2: Lloyd-Max Scalar
+ * Quantization": bits, levels, boundaries[15], centroids[16]; plus the dimension
+ * the table was built for).  Plain data, owned by the caller, passed by pointer
+ * and copied into the kernel arguments.  For bits 2..4 the code of a rotated,
+ * normalized coordinate u is #{j : boundaries[j] < u} and its value centroids[code].
+ * bits == 8 selects the uniform 256-level grid of [turboq] "At a glance" (turboq8):
+ * the arrays are unused and must be zero.
+ */
+typedef struct {
+    int32_t dim;            /* 128: tables are per QK block */
+    int32_t bits;           /* 2, 3, 4, or 8 */
+    int32_t levels;         /* 1 << bits */
+    float boundaries[15];   /* levels - 1 used, strictly ascending */
+    float centroids[16];    /* levels used, ascending */
+} fa_tq_codebook;
+
+/* Element strides of the (batch, head, token) axes of an input tensor; the channel
+ * stride is 1.  Each stride must be a multiple of 8 elements. */
+typedef struct {
+    int64_t stride_b;
+    int64_t stride_h;
+    int64_t stride_t;
+} fa_tq_layout;
+
+/*
+ * Lloyd-Max quantizer for the density of a rotated, L2-normalized coordinate,
+ * proportional to (1 - y^2)^(dim/2 - 1) on [-1, 1] (the Beta(d/2, d/2) law of
+ * [Spec] "Step 1"/"Step 2", with [Spec] "As-Built Notes" L2 normalization),
+ * built as in [Spec] "Codebook Generation": uniform start, centroids = conditional
+ * means, boundaries = midpoints, iterated to convergence (|change| < 1e-12) in fp64
+ * and stored as fp32.  dim in [4, 65536]; bits in {2, 3, 4, 8} (8: grid, arrays
+ * zeroed).  Host only: pure, deterministic, touches no device.
+ */
+fa_tq_status fa_tq_codebook_init(int32_t dim, int32_t bits, fa_tq_codebook *out);
+
+/*
+ * The random +/-1 diagonal of the rotation ([Spec] "Step 1": one head_dim array
+ * generated from the seed, shared by K, V, all heads and layers).  out[i] = -1 when
+ * bit 63 of the i-th output of SplitMix64 seeded with `seed` is set, else +1.
+ * Host only.  out: host array of head_dim int8.
+ */
+fa_tq_status fa_tq_signs(uint64_t seed, int32_t head_dim, int8_t *out);
+
+/* Packed bytes per 128-element block: 32, 48, 64, 128 for bits 2, 3, 4, 8; -1 else. */
+int32_t fa_tq_code_bytes(int32_t bits);
+
+/* Bytes of device workspace fa_tq_attn_decode needs for these sizes (0 on bad sizes). */
+size_t fa_tq_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t t_max, int32_t head_dim);
+
+/* Text describing the last non-OK status on the calling host thread. */
+const char *fa_tq_last_error(void);
+
+/*
+ * Encode ([Spec] "Overview" and "As-Built Notes"; [turboq] "Encode pipeline" steps
+ * 1-3): for every 128-block of every vector x[b][h][t][:] (t < n_tokens):
+ *   norm n = ||x_blk||, stored as fp16 in norms;
+ *   u = H (s * x_blk) / (sqrt(128) n)   (signs s from `seed`, block j uses s[128j..]);
+ *   code_i = #{j : boundaries[j] < u_i}, packed into codes.
+ * bits == 8: codes of the uniform grid with the block's absmax scale in norms.
+ * Arithmetic is fp32 in a fixed order, so codes and norms are reproducible bit for
+ * bit: squares summed pairwise over index bits 0..6; sqrt and division correctly
+ * rounded; butterflies in stage order 1, 2, ..., 64; u_i = h_i * (c / n) with
+ * c = fp32(1/sqrt(128)).
+ *   x: device, dtype x_dtype, element (b,h,t,c) at b*stride_b + h*stride_h +
+ *      t*stride_t + c; 16-byte aligned.
+ *   t0: device int32[batch] first cache position per sequence, or NULL for 0.
+ *      Vector t goes to cache position t0[b] + t; positions >= t_max are skipped.
+ *   codes, norms: device, SoA layout above with T_max = t_max, Hkv = n_kv_heads.
+ * batch, n_kv_heads or n_tokens == 0 is an OK no-op.
+ */
+fa_tq_status fa_tq_encode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_dim,
+                          const void *x, fa_tq_dtype x_dtype, fa_tq_layout x_layout,
+                          int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                          const int32_t *t0, int32_t t_max,
+                          uint8_t *codes, uint16_t *norms, void *stream);
+
+/*
+ * Decode ([Spec] "Overview": look up reconstruction values, then rotate back; the
+ * exact inverse R^T = D H / sqrt(d)):  x_hat = s * (H (n16 * c[code])) / sqrt(128)
+ * per block (bits 8: c[code] = (code - 127.5)/127.5 times the block scale).
+ *   codes: device [n_vec][nblk][cb]; norms: device [n_vec][nblk];
+ *   out: device float [n_vec][head_dim], 16-byte aligned.
+ */
+fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_dim,
+                          const uint8_t *codes, const uint16_t *norms, int64_t n_vec,
+                          float *out, void *stream);
+
+/*
+ * Single-query decode attention over the packed cache ([Spec] "Optimization: Fused
+ * dequant-dot"): per (b, query head h), with g = h / (n_q_heads / n_kv_heads):
+ *   q' = R q;  s_t = scale * n_K[t] * <q', c_K[code_K[t]]>  for t < seq_lens[b];
+ *   p = softmax(s);  o' = sum_t p_t n_V[t] c_V[code_V[t]];  out = R^T o'.
+ * seq_lens[b] == 0 gives zeros.  Accumulation in fp32.
+ *   q: device [batch][n_q_heads][head_dim] of q_dtype.
+ *   k_codes/k_norms/v_codes/v_norms: device, SoA layout above.
+ *   seq_lens: device int32[batch], each in [0, t_max] (larger values are clamped).
+ *   out: device float [batch][n_q_heads][head_dim].
+ *   workspace: device, >= fa_tq_attn_workspace_bytes(...), 16-byte aligned; holds
+ *   per-split partial results between the kernels of one call.
+ * This build supports head_dim == 128, key/value bits in {2, 3, 4} and
+ * n_q_heads / n_kv_heads <= 16.
+ */
+fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                               uint64_t seed, int32_t head_dim,
+                               const void *q, fa_tq_dtype q_dtype,
+                               const uint8_t *k_codes, const uint16_t *k_norms,
+                               const uint8_t *v_codes, const uint16_t *v_norms,
+                               const int32_t *seq_lens, int32_t batch,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t t_max,
+                               float scale, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_TQ_H */

@@ -1,0 +1,212 @@
+"""MI355X (gfx950) TurboQuant MSE KV-cache path: Python binding of ``libfa_tq.so``.
+
+The functions here have the names of the C ABI in ``include/fa_tq.h`` and only
+marshal arguments: torch tensors supply device memory and the current HIP stream;
+every step of the path runs in the library's HIP kernels.  There is no fallback:
+if the library is missing, ``load()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa_tq.so")
+
+FA_TQ_OK, FA_TQ_EINVAL, FA_TQ_EUNSUPPORTED, FA_TQ_EHIP = 0, 1, 2, 3
+FA_TQ_F32, FA_TQ_BF16 = 0, 1
+QK = 128
+
+_lib = None
+
+
+class FaTqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa_tq status {status}: {message}")
+        self.status = status
+
+
+class Codebook(ctypes.Structure):
+    """Mirror of ``fa_tq_codebook``."""
+    _fields_ = [("dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("levels", ctypes.c_int32),
+                ("boundaries", ctypes.c_float * 15), ("centroids", ctypes.c_float * 16)]
+
+    def arrays(self):
+        L = self.levels
+        if self.bits == 8:
+            return np.zeros(0, np.float32), np.zeros(0, np.float32)
+        return (np.array(self.boundaries[:L - 1], np.float32),
+                np.array(self.centroids[:L], np.float32))
+
+
+class Layout(ctypes.Structure):
+    """Mirror of ``fa_tq_layout`` (element strides of batch, head, token)."""
+    _fields_ = [("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_t", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "fa_tq_codebook_init": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Codebook)]),
+    "fa_tq_signs": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int32, _P]),
+    "fa_tq_code_bytes": (ctypes.c_int32, [ctypes.c_int32]),
+    "fa_tq_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 5),
+    "fa_tq_last_error": (ctypes.c_char_p, []),
+    "fa_tq_encode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
+                                    _P, ctypes.c_int, Layout, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
+    "fa_tq_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
+                                    _P, _P, ctypes.c_int64, _P, _P]),
+    "fa_tq_attn_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook),
+                                         ctypes.c_uint64, ctypes.c_int32, _P, ctypes.c_int,
+                                         _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
+                                         _P, ctypes.c_size_t, _P]),
+}
+
+
+def load(path: str | None = None):
+    """Load ``libfa_tq.so`` (built by ``kv_cache_vector_fa_amd.build``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FA_TQ_OK:
+        raise FaTqError(status, _lib.fa_tq_last_error().decode())
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+# --------------------------------------------------------------------------- host
+
+def codebook_init(dim: int, bits: int) -> Codebook:
+    lib = load()
+    cb = Codebook()
+    _check(lib.fa_tq_codebook_init(dim, bits, ctypes.byref(cb)))
+    return cb
+
+
+def codebook_from_arrays(bits: int, boundaries=None, centroids=None, dim: int = QK) -> Codebook:
+    """A ``Codebook`` filled from explicit tables (e.g. tables built elsewhere)."""
+    cb = Codebook()
+    cb.dim, cb.bits, cb.levels = dim, bits, 1 << bits
+    if bits != 8:
+        for i, v in enumerate(np.asarray(boundaries, np.float32)):
+            cb.boundaries[i] = float(v)
+        for i, v in enumerate(np.asarray(centroids, np.float32)):
+            cb.centroids[i] = float(v)
+    return cb
+
+
+def signs(seed: int, head_dim: int) -> np.ndarray:
+    lib = load()
+    out = np.zeros(head_dim, np.int8)
+    _check(lib.fa_tq_signs(seed, head_dim, out.ctypes.data))
+    return out
+
+
+def code_bytes(bits: int) -> int:
+    return int(load().fa_tq_code_bytes(bits))
+
+
+def attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim=QK) -> int:
+    return int(load().fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim))
+
+
+# ------------------------------------------------------------------------- device
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_TQ_BF16
+    if t.dtype == torch.float32:
+        return FA_TQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def cache_buffers(batch, n_kv_heads, t_max, head_dim, bits, device="cuda"):
+    """Allocate (codes, norms) for the packed SoA cache layout."""
+    import torch
+    nblk = head_dim // QK
+    codes = torch.empty((batch, n_kv_heads, t_max, nblk, code_bytes(bits)), dtype=torch.uint8,
+                        device=device)
+    norms = torch.empty((batch, n_kv_heads, t_max, nblk), dtype=torch.int16, device=device)
+    return codes, norms
+
+
+def encode(cb: Codebook, seed: int, x, t_max: int | None = None, t0=None, codes=None,
+           norms=None, stream=None):
+    """Encode x [B, Hkv, T, d] (bf16/fp32, channel stride 1) into the packed cache."""
+    lib = load()
+    B, H, T, d = x.shape
+    if x.stride(3) != 1:
+        raise ValueError("channel stride must be 1")
+    t_max = T if t_max is None else t_max
+    if codes is None or norms is None:
+        codes, norms = cache_buffers(B, H, t_max, d, cb.bits, x.device)
+    lay = Layout(x.stride(0), x.stride(1), x.stride(2))
+    _check(lib.fa_tq_encode(ctypes.byref(cb), seed, d, _ptr(x), _dtype_code(x), lay, B, H, T,
+                            _ptr(t0), t_max, _ptr(codes), _ptr(norms), _stream(stream)))
+    return codes, norms
+
+
+def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, stream=None):
+    """Decode packed blocks; codes [..., nblk, cb] -> float32 [..., head_dim]."""
+    import torch
+    lib = load()
+    nblk = head_dim // QK
+    n_vec = codes.numel() // (nblk * code_bytes(cb.bits))
+    if out is None:
+        out = torch.empty(tuple(codes.shape[:-2]) + (head_dim,), dtype=torch.float32,
+                          device=codes.device)
+    _check(lib.fa_tq_decode(ctypes.byref(cb), seed, head_dim, _ptr(codes), _ptr(norms), n_vec,
+                            _ptr(out), _stream(stream)))
+    return out
+
+
+def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,
+                v_norms, seq_lens, scale: float, out=None, workspace=None, stream=None):
+    """Single-query decode attention.  q [B, Hq, d]; caches [B, Hkv, T_max, nblk, cb]."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    need = attn_workspace_bytes(B, Hq, Hkv, t_max, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.fa_tq_attn_decode(ctypes.byref(cb_k), ctypes.byref(cb_v), seed, d, _ptr(q),
+                                 _dtype_code(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                 _ptr(v_norms), _ptr(seq_lens), B, Hq, Hkv, t_max,
+                                 float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return out

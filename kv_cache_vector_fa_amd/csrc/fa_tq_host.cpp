@@ -1,0 +1,378 @@
+// Host front-end of the C ABI declared in include/fa_tq.h: argument checks, the
+// Lloyd-Max codebook builder, the sign diagonal, and kernel launches.
+//
+// Pages cited: [Spec] "TurboQuant KV Cache Compression -- Spec";
+//              [turboq] "TurboQuant KV Cache (turboq2 / turboq3 / turboq4)".
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "fa_tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_tq_status fail(fa_tq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_tq_status ok() { return FA_TQ_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max for the density proportional to (1 - y^2)^m on [-1, 1], m = dim/2 - 1
+// ([Spec] "Step 2" and "Codebook Generation").  The cell mass is computed from the
+// regularized incomplete beta function (continued fraction, modified Lentz), the
+// first moment in closed form; only the positive half is iterated and mirrored.
+
+// Continued fraction for I_x(a, b), valid for x < (a + 1) / (a + b + 2).
+double beta_cf(double a, double b, double x) {
+  const double tiny = 1e-300;
+  const double qab = a + b, qap = a + 1.0, qam = a - 1.0;
+  double c = 1.0;
+  double d = 1.0 - qab * x / qap;
+  if (std::fabs(d) < tiny) d = tiny;
+  d = 1.0 / d;
+  double h = d;
+  for (int k = 1; k <= 100000; ++k) {
+    const double k2 = 2.0 * k;
+    double aa = k * (b - k) * x / ((qam + k2) * (a + k2));
+    d = 1.0 + aa * d;
+    if (std::fabs(d) < tiny) d = tiny;
+    c = 1.0 + aa / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    d = 1.0 / d;
+    h *= d * c;
+    aa = -(a + k) * (qab + k) * x / ((a + k2) * (qap + k2));
+    d = 1.0 + aa * d;
+    if (std::fabs(d) < tiny) d = tiny;
+    c = 1.0 + aa / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    d = 1.0 / d;
+    const double del = d * c;
+    h *= del;
+    if (std::fabs(del - 1.0) < 1e-16) break;
+  }
+  return h;
+}
+
+// Upper tail of the symmetric law: T(y) = P(Y > y) for y in [0, 1], where
+// (1 + Y) / 2 ~ Beta(p, p);  T(y) = I_{(1-y)/2}(p, p).
+double upper_tail(double y, double p, double lnB) {
+  if (y <= 0.0) return 0.5;
+  if (y >= 1.0) return 0.0;
+  const double x = 0.5 * (1.0 - y);
+  const double front = std::exp(p * std::log(x) + p * std::log1p(-x) - lnB) / p;
+  return front * beta_cf(p, p, x);
+}
+
+bool lloyd_max(int dim, int bits, float* boundaries, float* centroids) {
+  const int L = 1 << bits;
+  const int half = L / 2;
+  const double m = dim / 2.0 - 1.0;
+  const double p = m + 1.0;
+  const double lnB = 2.0 * std::lgamma(p) - std::lgamma(2.0 * p);
+  const double lnK = (2.0 * m + 1.0) * std::log(2.0) + lnB;  // mass = K * dT
+  const double K = std::exp(lnK);
+  std::vector<double> pos(half - 1), cent(half), edges(half + 1);
+  for (int k = 0; k < half - 1; ++k) pos[k] = 2.0 * (half + 1 + k) / L - 1.0;
+  auto centroids_of = [&](const std::vector<double>& bnd) {
+    edges[0] = 0.0;
+    for (int k = 0; k < half - 1; ++k) edges[k + 1] = bnd[k];
+    edges[half] = 1.0;
+    for (int j = 0; j < half; ++j) {
+      const double a = edges[j], b = edges[j + 1];
+      const double f1 = (std::pow(1.0 - a * a, p) - std::pow(1.0 - b * b, p)) / (2.0 * p);
+      const double f0 = K * (upper_tail(a, p, lnB) - upper_tail(b, p, lnB));
+      cent[j] = f1 / f0;
+    }
+  };
+  for (int it = 0; it < 100000; ++it) {
+    centroids_of(pos);
+    double delta = 0.0;
+    for (int k = 0; k < half - 1; ++k) {
+      const double nb = 0.5 * (cent[k] + cent[k + 1]);
+      delta = std::fmax(delta, std::fabs(nb - pos[k]));
+      pos[k] = nb;
+    }
+    if (delta < 1e-12) break;
+  }
+  centroids_of(pos);
+  for (int j = 0; j < half; ++j) {
+    if (!std::isfinite(cent[j])) return false;
+    centroids[half + j] = static_cast<float>(cent[j]);
+    centroids[half - 1 - j] = static_cast<float>(-cent[j]);
+  }
+  boundaries[half - 1] = 0.0f;
+  for (int k = 0; k < half - 1; ++k) {
+    boundaries[half + k] = static_cast<float>(pos[k]);
+    boundaries[half - 2 - k] = static_cast<float>(-pos[k]);
+  }
+  return true;
+}
+
+// SplitMix64 (Steele, Lea and Flood 2014), written from its published definition.
+struct SplitMix64 {
+  uint64_t state;
+  uint64_t next() {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+void make_signs(uint64_t seed, int head_dim, int8_t* out) {
+  SplitMix64 g{seed};
+  for (int i = 0; i < head_dim; ++i) out[i] = (g.next() >> 63) ? -1 : 1;
+}
+
+fatq::SignWords make_sign_words(uint64_t seed, int head_dim) {
+  std::vector<int8_t> s(head_dim);
+  make_signs(seed, head_dim, s.data());
+  fatq::SignWords sw;
+  std::memset(&sw, 0, sizeof(sw));
+  for (int j = 0; j < head_dim / fatq::QK; ++j)
+    for (int q = 0; q < 4; ++q)
+      for (int k = 0; k < 4; ++k)
+        for (int i = 0; i < 8; ++i)
+          if (s[fatq::QK * j + 8 * (q + 4 * k) + i] < 0) sw.w[j][q] |= 1u << (8 * k + i);
+  return sw;
+}
+
+fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool allow8,
+                            fatq::KTable* tab) {
+  if (!cb) return fail(FA_TQ_EINVAL, "%s: codebook pointer is NULL", what);
+  if (cb->dim != fatq::QK)
+    return fail(FA_TQ_EINVAL, "%s: codebook dim %d, tables are per 128-element block", what,
+                cb->dim);
+  const int bits = cb->bits;
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8))
+    return fail(FA_TQ_EINVAL, "%s: bits %d not in {2, 3, 4, 8}", what, bits);
+  if (cb->levels != (1 << bits))
+    return fail(FA_TQ_EINVAL, "%s: levels %d != 1 << bits (%d)", what, cb->levels, 1 << bits);
+  if (bits == 8 && !allow8)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: the 8-bit grid is supported by encode/decode only",
+                what);
+  std::memset(tab, 0, sizeof(*tab));
+  tab->bits = bits;
+  if (bits == 8) {
+    tab->nb = 255;
+    return ok();
+  }
+  const int L = cb->levels;
+  tab->nb = L - 1;
+  for (int j = 0; j < L - 1; ++j) {
+    if (!std::isfinite(cb->boundaries[j]))
+      return fail(FA_TQ_EINVAL, "%s: boundary %d is not finite", what, j);
+    if (j > 0 && !(cb->boundaries[j] > cb->boundaries[j - 1]))
+      return fail(FA_TQ_EINVAL, "%s: boundaries are not strictly ascending at %d", what, j);
+    tab->b[j] = cb->boundaries[j];
+  }
+  for (int j = 0; j < L; ++j) {
+    if (!std::isfinite(cb->centroids[j]))
+      return fail(FA_TQ_EINVAL, "%s: centroid %d is not finite", what, j);
+    tab->c[j] = cb->centroids[j];
+  }
+  return ok();
+}
+
+fa_tq_status check_head_dim(int32_t head_dim) {
+  if (head_dim <= 0 || head_dim % fatq::QK != 0 || head_dim > FA_TQ_MAX_HEAD_DIM)
+    return fail(FA_TQ_EINVAL,
+                "head_dim %d must be a positive multiple of 128 and at most %d", head_dim,
+                FA_TQ_MAX_HEAD_DIM);
+  return ok();
+}
+
+fa_tq_status launched(hipError_t e, const char* what) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(FA_TQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_tq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fa_tq_code_bytes(int32_t bits) {
+  switch (bits) {
+    case 2: return 32;
+    case 3: return 48;
+    case 4: return 64;
+    case 8: return 128;
+    default: return -1;
+  }
+}
+
+fa_tq_status fa_tq_signs(uint64_t seed, int32_t head_dim, int8_t* out) {
+  if (!out) return fail(FA_TQ_EINVAL, "fa_tq_signs: out is NULL");
+  if (head_dim <= 0 || head_dim > (1 << 20))
+    return fail(FA_TQ_EINVAL, "fa_tq_signs: head_dim %d out of range", head_dim);
+  make_signs(seed, head_dim, out);
+  return ok();
+}
+
+fa_tq_status fa_tq_codebook_init(int32_t dim, int32_t bits, fa_tq_codebook* out) {
+  if (!out) return fail(FA_TQ_EINVAL, "fa_tq_codebook_init: out is NULL");
+  if (dim < 4 || dim > 512)
+    return fail(FA_TQ_EINVAL, "fa_tq_codebook_init: dim %d not in [4, 512]", dim);
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8))
+    return fail(FA_TQ_EINVAL, "fa_tq_codebook_init: bits %d not in {2, 3, 4, 8}", bits);
+  std::memset(out, 0, sizeof(*out));
+  out->dim = dim;
+  out->bits = bits;
+  out->levels = 1 << bits;
+  if (bits == 8) return ok();
+  if (!lloyd_max(dim, bits, out->boundaries, out->centroids))
+    return fail(FA_TQ_EINVAL, "fa_tq_codebook_init: iteration did not stay finite");
+  return ok();
+}
+
+size_t fa_tq_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t t_max, int32_t head_dim) {
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0 || head_dim != fatq::QK ||
+      n_q_heads % n_kv_heads != 0)
+    return 0;
+  int32_t n_split = 1, chunk = 0;
+  fatq::attn_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
+  return fatq::attn_workspace_bytes(batch, n_q_heads, n_split);
+}
+
+fa_tq_status fa_tq_encode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
+                          const void* x, fa_tq_dtype x_dtype, fa_tq_layout x_layout,
+                          int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                          const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
+                          void* stream) {
+  fatq::KTable tab;
+  fa_tq_status st = check_codebook(cb, "fa_tq_encode", true, &tab);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "fa_tq_encode: negative size");
+  if (x_dtype != FA_TQ_F32 && x_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_encode: input dtype %d", (int)x_dtype);
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if (!x || !codes || !norms)
+    return fail(FA_TQ_EINVAL, "fa_tq_encode: NULL device pointer");
+  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return fail(FA_TQ_EINVAL, "fa_tq_encode: x and codes must be 16-byte aligned, norms 2-byte");
+  if (x_layout.stride_b % 8 || x_layout.stride_h % 8 || x_layout.stride_t % 8 ||
+      x_layout.stride_b < 0 || x_layout.stride_h < 0 || x_layout.stride_t < 0)
+    return fail(FA_TQ_EINVAL, "fa_tq_encode: strides must be non-negative multiples of 8");
+  if (n_tokens > t_max && !t0)
+    return fail(FA_TQ_EINVAL, "fa_tq_encode: n_tokens %d > t_max %d", n_tokens, t_max);
+  fatq::EncodeLaunch a;
+  a.x = x;
+  a.sb = x_layout.stride_b;
+  a.sh = x_layout.stride_h;
+  a.st = x_layout.stride_t;
+  a.batch = batch;
+  a.heads = n_kv_heads;
+  a.tokens = n_tokens;
+  a.nblk = head_dim / fatq::QK;
+  a.t_max = t_max;
+  a.t0 = t0;
+  a.codes = codes;
+  a.norms = norms;
+  a.x_is_bf16 = x_dtype == FA_TQ_BF16;
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  return launched(fatq::launch_encode(a, tab, sw, static_cast<hipStream_t>(stream)),
+                  "fa_tq_encode");
+}
+
+fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
+                          const uint8_t* codes, const uint16_t* norms, int64_t n_vec,
+                          float* out, void* stream) {
+  fatq::KTable tab;
+  fa_tq_status st = check_codebook(cb, "fa_tq_decode", true, &tab);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (n_vec < 0) return fail(FA_TQ_EINVAL, "fa_tq_decode: negative n_vec");
+  if (n_vec == 0) return ok();
+  if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "fa_tq_decode: NULL device pointer");
+  if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return fail(FA_TQ_EINVAL, "fa_tq_decode: codes and out must be 16-byte aligned");
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  return launched(fatq::launch_decode(codes, norms, n_vec, head_dim / fatq::QK, out, tab, sw,
+                                      static_cast<hipStream_t>(stream)),
+                  "fa_tq_decode");
+}
+
+fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                               uint64_t seed, int32_t head_dim, const void* q,
+                               fa_tq_dtype q_dtype, const uint8_t* k_codes,
+                               const uint16_t* k_norms, const uint8_t* v_codes,
+                               const uint16_t* v_norms, const int32_t* seq_lens,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t t_max, float scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  fatq::KTable tk, tv;
+  fa_tq_status st = check_codebook(cb_k, "fa_tq_attn_decode (keys)", false, &tk);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_codebook(cb_v, "fa_tq_attn_decode (values)", false, &tv)) != FA_TQ_OK)
+    return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (head_dim != fatq::QK)
+    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: head_dim %d (this build: 128)",
+                head_dim);
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: bad sizes");
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: n_q_heads %d not a multiple of n_kv_heads %d",
+                n_q_heads, n_kv_heads);
+  if (n_q_heads / n_kv_heads > 16)
+    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: group size %d > 16",
+                n_q_heads / n_kv_heads);
+  if (q_dtype != FA_TQ_F32 && q_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: query dtype %d", (int)q_dtype);
+  if (!std::isfinite(scale)) return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: scale not finite");
+  if (batch == 0) return ok();
+  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace)
+    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: NULL device pointer");
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out) || !aligned16(workspace) ||
+      !aligned16(q) || (reinterpret_cast<uintptr_t>(k_norms) & 1u) ||
+      (reinterpret_cast<uintptr_t>(v_norms) & 1u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: misaligned pointer");
+  const size_t need =
+      fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim);
+  if (workspace_bytes < need)
+    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: workspace %zu bytes < %zu", workspace_bytes,
+                need);
+  fatq::AttnLaunch a;
+  a.q = q;
+  a.q_is_bf16 = q_dtype == FA_TQ_BF16;
+  a.k_codes = k_codes;
+  a.k_norms = k_norms;
+  a.v_codes = v_codes;
+  a.v_norms = v_norms;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.hq = n_q_heads;
+  a.hkv = n_kv_heads;
+  a.t_max = t_max;
+  a.scale = scale;
+  a.out = out;
+  a.workspace = workspace;
+  fatq::attn_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  return launched(fatq::launch_attn(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
+                  "fa_tq_attn_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal declarations shared by the host front-end and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "fa_tq.h"
+
+namespace fatq {
+
+constexpr int QK = FA_TQ_QK;
+constexpr int MAX_BLK = FA_TQ_MAX_HEAD_DIM / FA_TQ_QK;
+
+// Sign diagonal as bit masks in the quad layout used by the block kernels: four
+// lanes own one 128-block, lane q holding chunks q, q+4, q+8, q+12 of 8 elements,
+// so element e = 8 (q + 4 k) + i.  Bit (8 k + i) of w[j][q] is set when the sign
+// of element 128 j + e is -1.
+struct SignWords {
+  uint32_t w[MAX_BLK][4];
+};
+
+// Codebook as the kernels read it (uniform kernel arguments).
+struct KTable {
+  float b[15];   // boundaries (nb used)
+  float c[16];   // centroids
+  int32_t nb;    // levels - 1
+  int32_t bits;
+};
+
+// fp32 nearest to 1/sqrt(128) (the scale of [Spec] Step 1), and the 8-bit grid
+// constant fp32(kInvSqrtQK * 127.5).
+constexpr float kInvSqrtQK = static_cast<float>(0.08838834764831845);
+constexpr float kGrid8 = kInvSqrtQK * 127.5f;
+
+struct EncodeLaunch {
+  const void* x;
+  int64_t sb, sh, st;   // element strides
+  int32_t batch, heads, tokens, nblk, t_max;
+  const int32_t* t0;
+  uint8_t* codes;
+  uint16_t* norms;
+  int32_t x_is_bf16;
+};
+
+hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
+                         hipStream_t stream);
+hipError_t launch_decode(const uint8_t* codes, const uint16_t* norms, int64_t n_vec,
+                         int32_t nblk, float* out, const KTable& tab, const SignWords& sw,
+                         hipStream_t stream);
+
+struct AttnLaunch {
+  const void* q;
+  int32_t q_is_bf16;
+  const uint8_t* k_codes;
+  const uint16_t* k_norms;
+  const uint8_t* v_codes;
+  const uint16_t* v_norms;
+  const int32_t* seq_lens;
+  int32_t batch, hq, hkv, t_max;
+  float scale;
+  float* out;
+  void* workspace;
+  int32_t n_split, chunk;
+};
+
+// Split-KV partitioning used by both the workspace query and the launch.
+void attn_partition(int32_t batch, int32_t hkv, int32_t t_max, int32_t* n_split,
+                    int32_t* chunk);
+size_t attn_workspace_bytes(int32_t batch, int32_t hq, int32_t n_split);
+
+hipError_t launch_attn(const AttnLaunch& a, const KTable& tk, const KTable& tv,
+                       const SignWords& sw, hipStream_t stream);
+
+}  // namespace fatq

@@ -1,0 +1,162 @@
+"""GPU parity of fa_tq_attn_decode against the fp64 CPU oracle (MI355X).
+
+The packed cache the kernel reads is always produced without the HIP path: by the
+oracle's own encoder, or (for the largest workloads) drawn directly as seeded
+random codes and fp16 norms.  The oracle evaluates the same packed cache.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as o_att
+from oracle import codebook as o_cb
+from oracle import codec
+from oracle import signs as o_signs
+from tests.gpu_helpers import ATTN_MAX_ABS, bf16_to_f32, say
+
+pytestmark = pytest.mark.gpu
+SEED = workloads.ROTATION_SEED
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _oracle_cache(x32: np.ndarray, bits: int, seed: int = SEED):
+    """x32 [B, H, T, 128] -> (packed [B, H, T, 1, cb] uint8, norms f16 [B, H, T, 1])."""
+    b, _ = o_cb.codebook(bits)
+    c, n, _ = codec.encode_mse(x32, o_signs.signs(seed, 128), b)
+    return codec.pack(c, bits), n
+
+
+def _random_cache(B, H, T, bits, seed):
+    """Seeded random packed codes and fp16 norms (norms ~ 11.3 * lognormal(0, 0.3))."""
+    rng = np.random.default_rng(seed)
+    cbytes = {2: 32, 3: 48, 4: 64}[bits]
+    packed = rng.integers(0, 256, size=(B, H, T, 1, cbytes), dtype=np.uint8)
+    norms = (11.3 * np.exp(0.3 * rng.standard_normal((B, H, T, 1)))).astype(np.float16)
+    return packed, norms
+
+
+def _run(fa, q, kp, kn, vp, vn, lens, kb, vb, scale, heads=None, where=""):
+    torch = _torch()
+    dev = "cuda"
+    ck, cv = fa.codebook_init(128, kb), fa.codebook_init(128, vb)
+    qt = torch.from_numpy(q).to(dev) if isinstance(q, np.ndarray) else q
+    out = fa.attn_decode(ck, cv, SEED, qt, torch.from_numpy(kp).to(dev),
+                         torch.from_numpy(kn.view(np.int16)).to(dev),
+                         torch.from_numpy(vp).to(dev), torch.from_numpy(vn.view(np.int16)).to(dev),
+                         torch.tensor(lens, dtype=torch.int32, device=dev), scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    q32 = bf16_to_f32(qt) if qt.dtype == torch.bfloat16 else qt.cpu().numpy()
+    ref = o_att.attend_fused(q32, kp, kn, vp, vn, lens, kb, vb, o_cb.codebook(kb)[1],
+                             o_cb.codebook(vb)[1], o_signs.signs(SEED, 128), scale, heads=heads)
+    if heads is not None:
+        sel = tuple(np.array(heads).T)
+        got, ref = got[sel], ref[sel]
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    say(f"{where}: max abs err {err:.3e}")
+    assert err <= ATTN_MAX_ABS, f"{where}: {err}"
+    return err
+
+
+def test_attn_tiny_workload(gpu_lib):
+    k, v, q = workloads.tiny_inputs()
+    kp, kn = _oracle_cache(k.reshape(1, 1, 1024, 128), 4)
+    vp, vn = _oracle_cache(v.reshape(1, 1, 1024, 128), 2)
+    _run(gpu_lib, q.reshape(1, 1, 128), kp, kn, vp, vn, [1024], 4, 2, 1 / np.sqrt(128),
+         where="tiny")
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4), (2, 3), (3, 4)])
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [
+    (3, 8, 2, 333, [333, 0, 1]),
+    (2, 4, 4, 1000, [1000, 517]),
+    (1, 32, 2, 700, [700]),
+    (2, 6, 3, 2100, [64, 2099]),
+])
+def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
+    torch = _torch()
+    say(f"attn ragged K{kb}V{vb} B={B} Hq={Hq} Hkv={Hkv} T={T} lens={lens}")
+    rng = np.random.default_rng(kb * 10 + vb + T)
+    k = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32) * rng.uniform(0.2, 3.0, (1, Hkv, 1, 128)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32)).to(torch.bfloat16)
+    kp, kn = _oracle_cache(k, kb)
+    vp, vn = _oracle_cache(v, vb)
+    _run(gpu_lib, q.cuda(), kp, kn, vp, vn, lens, kb, vb, 1 / np.sqrt(128), where="ragged")
+
+
+def test_attn_fp32_query_and_scales(gpu_lib):
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, T = 2, 8, 8, 257
+    k = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, 128)).astype(np.float32)
+    kp, kn = _oracle_cache(k, 4)
+    vp, vn = _oracle_cache(v, 2)
+    for scale in (1 / np.sqrt(128), 0.5, 1e-3):
+        _run(gpu_lib, q, kp, kn, vp, vn, [T, 100], 4, 2, scale, where=f"scale {scale}")
+
+
+def test_attn_seq_len_clamped_to_t_max(gpu_lib):
+    rng = np.random.default_rng(4)
+    T = 130
+    k = rng.standard_normal((1, 1, T, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 1, T, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 2, 128)).astype(np.float32)
+    kp, kn = _oracle_cache(k, 4)
+    vp, vn = _oracle_cache(v, 4)
+    torch = _torch()
+    ck = gpu_lib.codebook_init(128, 4)
+    args = [torch.from_numpy(a).cuda() for a in (kp, kn.view(np.int16), vp, vn.view(np.int16))]
+    big = gpu_lib.attn_decode(ck, ck, SEED, torch.from_numpy(q).cuda(), *args,
+                              torch.tensor([10 ** 6], dtype=torch.int32, device="cuda"), 0.1)
+    ref = gpu_lib.attn_decode(ck, ck, SEED, torch.from_numpy(q).cuda(), *args,
+                              torch.tensor([T], dtype=torch.int32, device="cuda"), 0.1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(big.cpu().numpy(), ref.cpu().numpy())
+
+
+def test_attn_llama_layer_full(gpu_lib):
+    """Llama-3-8B-shaped layer at full size (32768 tokens, 32/8 heads, K4/V2): the
+    oracle encodes the whole bf16 cache; all 32 heads compared."""
+    torch = _torch()
+    w = workloads.WORKLOADS["llama_layer"]
+    say("attn llama_layer full")
+    k, v = workloads.make_kv(w, "cuda")
+    q = workloads.make_q(w, "cuda")
+    kp, kn = _oracle_cache(bf16_to_f32(k), w.k_bits)
+    vp, vn = _oracle_cache(bf16_to_f32(v), w.v_bits)
+    del k, v
+    _run(gpu_lib, q, kp, kn, vp, vn, [w.tokens], w.k_bits, w.v_bits, 1 / np.sqrt(128),
+         where="llama_layer")
+
+
+def test_attn_batched_full_sampled(gpu_lib):
+    """Batched workload at full size (16 x 8192, K3/V3, lengths in [4096, 8192])."""
+    w = workloads.WORKLOADS["batched"]
+    say("attn batched full")
+    kp, kn = _random_cache(w.batch, w.n_kv_heads, w.tokens, w.k_bits, 31)
+    vp, vn = _random_cache(w.batch, w.n_kv_heads, w.tokens, w.v_bits, 32)
+    lens = workloads.make_seq_lens(w)
+    q = workloads.make_q(w, "cuda")
+    heads = [(b, h) for b in (0, 7, 15) for h in (0, 5, 31)]
+    _run(gpu_lib, q, kp, kn, vp, vn, lens, w.k_bits, w.v_bits, 1 / np.sqrt(128), heads=heads,
+         where="batched")
+
+
+def test_attn_long_context_full_sampled(gpu_lib):
+    """Long-context workload at full size (4 x 131072, K4/V4)."""
+    w = workloads.WORKLOADS["long_context"]
+    say("attn long_context full")
+    kp, kn = _random_cache(w.batch, w.n_kv_heads, w.tokens, w.k_bits, 41)
+    vp, vn = _random_cache(w.batch, w.n_kv_heads, w.tokens, w.v_bits, 42)
+    lens = workloads.make_seq_lens(w)
+    q = workloads.make_q(w, "cuda")
+    heads = [(0, 0), (1, 9), (3, 31)]
+    _run(gpu_lib, q, kp, kn, vp, vn, lens, w.k_bits, w.v_bits, 1 / np.sqrt(128), heads=heads,
+         where="long_context")

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (CPU only: no device compute is called here).
+
+The library must load, export every function ``include/fa_tq.h`` declares, build
+the same codebooks and signs as the oracle (two independent implementations), and
+reject bad arguments before touching the device.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_fa_amd as fa
+from oracle import codebook as o_cb
+from oracle import signs as o_signs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fa_tq.h")).read()
+    return sorted(set(re.findall(r"\b(fa_tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(fa.exported_symbols()) == declared
+
+
+@pytest.mark.parametrize("dim", [64, 96, 128, 160, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_matches_oracle_exactly(lib, dim, bits):
+    """C++ (incomplete-beta quadrature) and oracle (Gauss-Legendre) tables agree
+    bit for bit in fp32."""
+    cb = fa.codebook_init(dim, bits)
+    b, c = cb.arrays()
+    ob, oc = o_cb.codebook(bits, dim)
+    assert cb.dim == dim and cb.bits == bits and cb.levels == 1 << bits
+    np.testing.assert_array_equal(b, ob)
+    np.testing.assert_array_equal(c, oc)
+
+
+def test_codebook_8bit_is_grid(lib):
+    cb = fa.codebook_init(128, 8)
+    assert cb.levels == 256 and all(x == 0 for x in cb.boundaries) and all(x == 0 for x in cb.centroids)
+
+
+@pytest.mark.parametrize("seed", [0, 42, 2 ** 63 + 5])
+def test_signs_match_oracle(lib, seed):
+    np.testing.assert_array_equal(fa.signs(seed, 256), o_signs.signs(seed, 256))
+
+
+def test_code_bytes_and_workspace(lib):
+    assert [fa.code_bytes(b) for b in (2, 3, 4, 8)] == [32, 48, 64, 128]
+    assert fa.code_bytes(5) == -1
+    ws = fa.attn_workspace_bytes(1, 32, 8, 32768)
+    assert ws > 0 and ws % 4 == 0
+    assert fa.attn_workspace_bytes(1, 30, 8, 100) == 0      # 30 % 8 != 0
+    assert fa.attn_workspace_bytes(1, 32, 8, 100, 256) == 0  # head_dim 256 unsupported
+
+
+def _err(fn, *args):
+    with pytest.raises(fa.FaTqError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def test_codebook_init_rejects_bad_arguments(lib):
+    assert _err(fa.codebook_init, 128, 5) == fa.FA_TQ_EINVAL
+    assert _err(fa.codebook_init, 2, 4) == fa.FA_TQ_EINVAL
+    assert _err(fa.codebook_init, 1024, 4) == fa.FA_TQ_EINVAL
+    assert lib.fa_tq_codebook_init(128, 4, None) == fa.FA_TQ_EINVAL
+
+
+def _encode_raw(lib, cb, head_dim, x_ptr, dtype, layout, B, H, T, t_max, codes, norms):
+    return lib.fa_tq_encode(ctypes.byref(cb), 42, head_dim, ctypes.c_void_p(x_ptr), dtype,
+                            layout, B, H, T, None, t_max, ctypes.c_void_p(codes),
+                            ctypes.c_void_p(norms), None)
+
+
+def test_encode_validation_before_launch(lib):
+    """Every rejected call returns before any HIP call (no device is needed)."""
+    cb = fa.codebook_init(128, 4)
+    lay = fa.Layout(8 * 128, 8 * 128, 128)
+    A = 1 << 20  # any 16-byte aligned non-null value; never dereferenced on rejection
+    assert _encode_raw(lib, cb, 100, A, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    assert _encode_raw(lib, cb, 128, A + 4, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    assert _encode_raw(lib, cb, 128, 0, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    bad = fa.Layout(8 * 128, 8 * 128, 100)
+    assert _encode_raw(lib, cb, 128, A, 1, bad, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    assert _encode_raw(lib, cb, 128, A, 1, lay, 1, 1, 5, 4, A, A) == fa.FA_TQ_EINVAL
+    assert _encode_raw(lib, cb, 128, A, 7, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EUNSUPPORTED
+    assert _encode_raw(lib, cb, 128, A, 1, lay, -1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    # zero-sized work is an OK no-op (no launch)
+    assert _encode_raw(lib, cb, 128, 0, 1, lay, 0, 1, 1, 1, 0, 0) == fa.FA_TQ_OK
+    # a tampered codebook is rejected
+    bad_cb = fa.codebook_init(128, 4)
+    bad_cb.boundaries[3] = bad_cb.boundaries[2]
+    assert _encode_raw(lib, bad_cb, 128, A, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    bad_cb = fa.codebook_init(128, 4)
+    bad_cb.dim = 256
+    assert _encode_raw(lib, bad_cb, 128, A, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    bad_cb = fa.codebook_init(128, 4)
+    bad_cb.levels = 8
+    assert _encode_raw(lib, bad_cb, 128, A, 1, lay, 1, 1, 1, 1, A, A) == fa.FA_TQ_EINVAL
+    assert "levels" in lib.fa_tq_last_error().decode()
+
+
+def _attn_raw(lib, ck, cv, hd, B, Hq, Hkv, T, ws_bytes, ptr=1 << 20):
+    P = ctypes.c_void_p(ptr)
+    return lib.fa_tq_attn_decode(ctypes.byref(ck), ctypes.byref(cv), 42, hd, P, 1, P, P, P, P,
+                                 P, B, Hq, Hkv, T, 0.0884, P, P, ws_bytes, None)
+
+
+def test_attn_validation_before_launch(lib):
+    ck, cv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    big = 1 << 40
+    assert _attn_raw(lib, ck, cv, 128, 1, 30, 8, 64, big) == fa.FA_TQ_EINVAL
+    assert _attn_raw(lib, ck, cv, 256, 1, 32, 8, 64, big) == fa.FA_TQ_EUNSUPPORTED
+    assert _attn_raw(lib, ck, cv, 128, 1, 64, 2, 64, big) == fa.FA_TQ_EUNSUPPORTED
+    assert _attn_raw(lib, ck, cv, 128, 1, 32, 8, 64, 16) == fa.FA_TQ_EINVAL   # workspace
+    assert _attn_raw(lib, ck, cv, 128, 1, 32, 8, 64, big, ptr=(1 << 20) + 8) == fa.FA_TQ_EINVAL
+    c8 = fa.codebook_init(128, 8)
+    assert _attn_raw(lib, c8, cv, 128, 1, 32, 8, 64, big) == fa.FA_TQ_EUNSUPPORTED
+    assert _attn_raw(lib, ck, cv, 128, 0, 32, 8, 64, big) == fa.FA_TQ_OK

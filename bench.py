@@ -145,7 +145,7 @@ def main():
     caches = [fa.cache_buffers(B, Hkv, T, d, w.k_bits) + fa.cache_buffers(B, Hkv, T, d, w.v_bits)
               for _ in range(R)]
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(fa.attn_workspace_bytes(B, Hq, Hkv, T, d), dtype=torch.uint8, device="cuda")
+    ws = fa.attn_workspace(B, Hq, Hkv, T, d)
     scale = 1 / np.sqrt(d)
 
     def enc_k(i):

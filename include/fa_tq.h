@@ -149,8 +149,10 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
  *   k_codes/k_norms/v_codes/v_norms: device, SoA layout above.
  *   seq_lens: device int32[batch], each in [0, t_max] (larger values are clamped).
  *   out: device float [batch][n_q_heads][head_dim].
- *   workspace: device, >= fa_tq_attn_workspace_bytes(...), 16-byte aligned; holds
- *   per-split partial results between the kernels of one call.
+ *   workspace: device, >= fa_tq_attn_workspace_bytes(...), 16-byte aligned.  It
+ *   holds per-split partial results (m, l and the unnormalized rotated output per
+ *   split of the sequence); its contents on entry do not matter.  Calls that run
+ *   concurrently must not share a workspace; calls in order on one stream may.
  * This build supports head_dim == 128, key/value bits in {2, 3, 4} and
  * n_q_heads / n_kv_heads <= 16.
  */

@@ -192,6 +192,13 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
     return out
 
 
+def attn_workspace(batch, n_q_heads, n_kv_heads, t_max, head_dim=QK, device="cuda"):
+    """A workspace for ``attn_decode`` (reusable by later calls in order on one stream)."""
+    import torch
+    need = attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,
                 v_norms, seq_lens, scale: float, out=None, workspace=None, stream=None):
     """Single-query decode attention.  q [B, Hq, d]; caches [B, Hkv, T_max, nblk, cb]."""
@@ -203,7 +210,7 @@ def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, 
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     need = attn_workspace_bytes(B, Hq, Hkv, t_max, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = attn_workspace(B, Hq, Hkv, t_max, d, q.device)
     _check(lib.fa_tq_attn_decode(ctypes.byref(cb_k), ctypes.byref(cb_v), seed, d, _ptr(q),
                                  _dtype_code(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
                                  _ptr(v_norms), _ptr(seq_lens), B, Hq, Hkv, t_max,

@@ -30,6 +30,7 @@ SOURCES = [
     ("fa_tq_host.cpp", ["-x", "hip"]),
     ("codec.hip", ["-ffp-contract=off"]),
     ("attn.hip", []),
+    ("attn_mfma.hip", []),
 ]
 
 

@@ -250,6 +250,10 @@ size_t fa_tq_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv
       n_q_heads % n_kv_heads != 0)
     return 0;
   int32_t n_split = 1, chunk = 0;
+  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
+    return fatq::attn_mfma_workspace_bytes(batch, n_q_heads, n_kv_heads, n_split);
+  }
   fatq::attn_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
   return fatq::attn_workspace_bytes(batch, n_q_heads, n_split);
 }
@@ -369,8 +373,13 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook*
   a.scale = scale;
   a.out = out;
   a.workspace = workspace;
-  fatq::attn_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+    return launched(fatq::launch_attn_mfma(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
+                    "fa_tq_attn_decode");
+  }
+  fatq::attn_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
   return launched(fatq::launch_attn(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
                   "fa_tq_attn_decode");
 }

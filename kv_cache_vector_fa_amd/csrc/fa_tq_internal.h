@@ -71,4 +71,12 @@ size_t attn_workspace_bytes(int32_t batch, int32_t hq, int32_t n_split);
 hipError_t launch_attn(const AttnLaunch& a, const KTable& tk, const KTable& tv,
                        const SignWords& sw, hipStream_t stream);
 
+// MFMA path (query groups of up to 8 heads per KV head).
+bool attn_mfma_supported(int32_t hq, int32_t hkv);
+void attn_mfma_partition(int32_t batch, int32_t hkv, int32_t t_max, int32_t* n_split,
+                         int32_t* chunk);
+size_t attn_mfma_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t n_split);
+hipError_t launch_attn_mfma(const AttnLaunch& a, const KTable& tk, const KTable& tv,
+                            const SignWords& sw, hipStream_t stream);
+
 }  // namespace fatq

@@ -77,6 +77,8 @@ def test_attn_tiny_workload(gpu_lib):
     (2, 4, 4, 1000, [1000, 517]),
     (1, 32, 2, 700, [700]),
     (2, 6, 3, 2100, [64, 2099]),
+    (1, 40, 5, 300, [300]),
+    (2, 5, 1, 129, [129, 77]),
 ])
 def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
     torch = _torch()

@@ -20,6 +20,10 @@ namespace fatq {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef FATQ_ENCODE_THREADS
+#define FATQ_ENCODE_THREADS 256
+#endif
+constexpr int kEncThreads = FATQ_ENCODE_THREADS;
 
 __device__ __forceinline__ float flip_sign(float x, uint32_t bit) {
   return __uint_as_float(__float_as_uint(x) ^ (bit << 31));
@@ -75,60 +79,6 @@ __device__ __forceinline__ void fwht_quad(float (&v)[4][8], int q) {
   for (int i = 0; i < 8; ++i) {
     bfly(v[0][i], v[2][i]);
     bfly(v[1][i], v[3][i]);
-  }
-}
-
-// Canonical fp32 norm: squares summed pairwise over index bits 0, 1, ..., 6.
-__device__ __forceinline__ float norm_quad(const float (&x)[4][8]) {
-  float p[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float s[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = x[k][i] * x[k][i];
-    const float a0 = s[0] + s[1], a1 = s[2] + s[3], a2 = s[4] + s[5], a3 = s[6] + s[7];
-    const float b0 = a0 + a1, b1 = a2 + a3;
-    p[k] = b0 + b1;
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) p[k] = p[k] + __shfl_xor(p[k], 1, 64);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) p[k] = p[k] + __shfl_xor(p[k], 2, 64);
-  const float c0 = p[0] + p[1], c1 = p[2] + p[3];
-  return __builtin_sqrtf(c0 + c1);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void load_block(const void* base, int64_t off, int q,
-                                           float (&x)[4][8]) {
-  if constexpr (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    uint4 w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = p[q + 4 * k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t d[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        x[k][2 * m] = __uint_as_float(d[m] << 16);
-        x[k][2 * m + 1] = __uint_as_float(d[m] & 0xffff0000u);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    float4 w[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w[2 * k] = p[2 * (q + 4 * k)];
-      w[2 * k + 1] = p[2 * (q + 4 * k) + 1];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k][0] = w[2 * k].x; x[k][1] = w[2 * k].y; x[k][2] = w[2 * k].z; x[k][3] = w[2 * k].w;
-      x[k][4] = w[2 * k + 1].x; x[k][5] = w[2 * k + 1].y;
-      x[k][6] = w[2 * k + 1].z; x[k][7] = w[2 * k + 1].w;
-    }
   }
 }
 
@@ -194,83 +144,342 @@ constexpr int code_bytes_of() {
   return BITS == 2 ? 32 : BITS == 3 ? 48 : BITS == 4 ? 64 : 128;
 }
 
-// Encode: one quad per 128-block, grid-stride over blocks.  The number of quads in
-// the grid is a multiple of nblk, so each quad keeps one sign slice j.
-template <int BITS, bool BF16>
-__global__ void __launch_bounds__(kThreads) encode_kernel(EncodeLaunch a, KTable tab,
-                                                          SignWords sw) {
-  constexpr int CB = code_bytes_of<BITS>();
-  const int q = threadIdx.x & 3;
-  const int64_t quad0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 2;
-  const int64_t nquad = (static_cast<int64_t>(gridDim.x) * kThreads) >> 2;
-  const int64_t total = static_cast<int64_t>(a.batch) * a.heads * a.tokens * a.nblk;
-  const int j = static_cast<int>(quad0 % a.nblk);
-  const uint32_t sbits = sw.w[j][q];
+// ---------------------------------------------------------------------------
+// Bucketize by cell table.  A cell is the set of fp32 values sharing the top 11
+// bits (sign, exponent, two leading mantissa bits), so cell index = bits >> 21 and
+// cells are contiguous intervals.  Adjacent Lloyd-Max boundaries of the 2-4 bit
+// tables are more than 1.25x apart (the host checks that no two boundaries share a
+// cell), so a cell contains at most one boundary and
+//     code(u) = base[cell] + (u > thr[cell]),
+// with base = #{j : b_j < smallest value of the cell} and thr = b[base] (+inf when
+// base = L - 1).  One 8-byte LDS read and one compare per coordinate reproduce
+// code = #{j : b_j < u} exactly, ties included ([Spec] "Step 2": the boundaries
+// are the decision thresholds).
+constexpr int kCellShift = 21;
+constexpr uint32_t kCells = 1u << (32 - kCellShift);   // 2048 cells, 16 KB of LDS
+constexpr uint32_t kNegCell = kCells / 2;
 
-  for (int64_t blk = quad0; blk < total; blk += nquad) {
-    int64_t v = blk / a.nblk;
-    const int t = static_cast<int>(v % a.tokens);
-    v /= a.tokens;
-    const int h = static_cast<int>(v % a.heads);
-    const int b = static_cast<int>(v / a.heads);
-    const int tt = (a.t0 ? a.t0[b] : 0) + t;
-    if (tt < 0 || tt >= a.t_max) continue;
-    const int64_t xoff = b * a.sb + h * a.sh + t * a.st + static_cast<int64_t>(QK) * j;
+// bext: 16 floats of LDS for the boundaries followed by +inf.
+__device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTable& t) {
+  const int nb = t.nb;
+  if (threadIdx.x < 16) bext[threadIdx.x] = static_cast<int>(threadIdx.x) < nb ? t.b[threadIdx.x] : INFINITY;
+  // Exponent range of the nonzero boundaries, and how many boundaries are < 0 / <= 0
+  // (uniform values).
+  uint32_t emin = 0xFFu, emax = 0u, nneg = 0u, nle0 = 0u;
+#pragma unroll
+  for (int m = 0; m < 15; ++m) {
+    if (m < nb) {
+      const float bm = t.b[m];
+      const uint32_t e = (__float_as_uint(bm) >> 23) & 0xFFu;
+      if (bm != 0.0f) {
+        emin = e < emin ? e : emin;
+        emax = e > emax ? e : emax;
+      }
+      nneg += bm < 0.0f ? 1u : 0u;
+      nle0 += bm <= 0.0f ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  for (uint32_t c = threadIdx.x; c < kCells; c += blockDim.x) {
+    const uint32_t e = (c >> 2) & 0xFFu;
+    const bool neg = c >= kNegCell;
+    uint32_t base;
+    if (e < emin && c != 0) {          // 0 < |u| < every nonzero |boundary|
+      base = neg ? nneg : nle0;
+    } else if (e > emax) {             // |u| above every |boundary|
+      base = neg ? 0u : static_cast<uint32_t>(nb);
+    } else {                           // count directly from the smallest member
+      const uint32_t lo = c << kCellShift;
+      const float umin = __uint_as_float(neg ? (lo | ((1u << kCellShift) - 1u)) : lo);
+      base = 0;
+#pragma unroll
+      for (int m = 0; m < 15; ++m)
+        if (m < nb) base += t.b[m] < umin ? 1u : 0u;
+    }
+    cells[c] = make_uint2(__float_as_uint(bext[base]), base);
+  }
+}
 
-    float x[4][8];
-    load_block<BF16>(a.x, xoff, q, x);
-    const float n32 = norm_quad(x);
+// Codes of 8 coordinates y[0..7] (u_i = y_i * g) as LSB-first fields of width W
+// (Horner from the last coordinate, so y[0] lands in the lowest field).
+template <int W>
+__device__ __forceinline__ uint32_t bucketize8(const float (&y)[8], float g,
+                                               const uint2* cells) {
+  uint32_t acc = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[k][i] = flip_sign(x[k][i], (sbits >> (8 * k + i)) & 1u);
-    fwht_quad(x, q);
+  for (int i = 7; i >= 0; --i) {
+    const float u = y[i] * g;
+    const uint32_t off = (__float_as_uint(u) >> (kCellShift - 3)) & ((kCells - 1u) << 3);
+    const uint2 cell = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cells) + off);
+    acc = (acc << W) + cell.y + (u > __uint_as_float(cell.x) ? 1u : 0u);
+  }
+  return acc;
+}
 
-    const int64_t row = ((static_cast<int64_t>(b) * a.heads + h) * a.t_max + tt) * a.nblk + j;
-    uint8_t* crow = a.codes + row * CB;
-    uint16_t nbits;
-    if constexpr (BITS == 8) {
-      // turboq8 grid: per-block absmax scale, codes round((y / s) * 127.5 + 127.5)
-      float amax = 0.0f;
+// Cross-lane butterfly stage on one 8-element chunk: v <- v + mu * v(partner), the
+// partner chosen by the DPP quad permutation.  With mu = +1 in the lower lane of the
+// pair and -1 in the upper one this is (a + b, -(a - b)): the upper lane keeps the
+// negated difference, and the sign is tracked by the caller.  fma(x, +-1, y) rounds
+// exactly like y +- x.  The s_nop pairs cover the 2-wait-state hazard of a DPP read
+// of a VGPR written by the preceding VALU instruction (before the block) and of a
+// DPP instruction after it reading these results.
+template <int CTRL>
+__device__ __forceinline__ void xstage(float (&v)[8], float mu) {
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E, "quad permutation");
+  if constexpr (CTRL == 0xB1) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+          "+v"(v[6]), "+v"(v[7])
+        : "v"(mu));
+  } else {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+          "+v"(v[6]), "+v"(v[7])
+        : "v"(mu));
+  }
+}
+
+// Add the value of lane q ^ 1 (CTRL 0xB1) or q ^ 2 (0x4E) within the quad.
+template <int CTRL>
+__device__ __forceinline__ float quad_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_max(float x) {
+  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false)));
+}
+
+// One block's input in the quad layout: raw words (bf16: 4 x 16 B per lane; fp32:
+// 8 x 16 B per lane).
+template <bool BF16>
+struct RawBlock {
+  uint4 w[BF16 ? 4 : 8];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_raw(const void* base, int64_t off, int q,
+                                         RawBlock<BF16>& r) {
+  if constexpr (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) r.w[k] = p[q + 4 * k];
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[k][i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      const __half s16 = __float2half_rn(fp32_value(amax * kInvSqrtQK));
-      const float s32 = __half2float(s16);
-      const float G = s32 > 0.0f ? kGrid8 / s32 : 0.0f;
-      nbits = __half_as_ushort(s16);
+    for (int k = 0; k < 4; ++k) {
+      r.w[2 * k] = p[2 * (q + 4 * k)];
+      r.w[2 * k + 1] = p[2 * (q + 4 * k) + 1];
+    }
+  }
+}
+
+// Sign-flip (s * x) and widen to fp32; also return the canonical sum of squares of
+// this lane's 4 chunks (levels 0-2 of the pairwise tree, index bits 0-2).  For bf16
+// inputs x^2 is exact in fp32, so fma(x1, x1, x0 * x0) is the rounded pair sum.
+// smask[k][m]: bit 15 / bit 31 flip the low / high bf16 of word m of chunk k.
+template <bool BF16>
+__device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&smask)[16],
+                                      uint32_t sbits, float (&x)[4][8], float (&p)[4]) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t code[8];
+  for (int k = 0; k < 4; ++k) {
+    float s[4];
+    if constexpr (BF16) {
+      const uint32_t d[4] = {r.w[k].x, r.w[k].y, r.w[k].z, r.w[k].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float t8 = x[k][i] * G;
-          const float w = t8 + 127.5f;
-          code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
-        }
-        store_chunk<8>(crow, q + 4 * k, code);
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t f = d[m] ^ smask[4 * k + m];
+        const float lo = __uint_as_float(f << 16), hi = __uint_as_float(f & 0xffff0000u);
+        x[k][2 * m] = lo;
+        x[k][2 * m + 1] = hi;
+        s[m] = __builtin_fmaf(hi, hi, lo * lo);
       }
     } else {
-      const float g = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
-      nbits = __half_as_ushort(__float2half_rn(n32));
+      const uint4 a = r.w[2 * k], b = r.w[2 * k + 1];
+      const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t code[8];
+      for (int i = 0; i < 8; ++i)
+        x[k][i] = __uint_as_float(d[i] ^ (((sbits >> (8 * k + i)) & 1u) << 31));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float u = x[k][i] * g;
-          uint32_t cnt = 0;
-#pragma unroll
-          for (int m = 0; m < (1 << BITS) - 1; ++m) cnt += tab.b[m] < u ? 1u : 0u;
-          code[i] = cnt;
-        }
-        store_chunk<BITS>(crow, q + 4 * k, code);
+      for (int m = 0; m < 4; ++m) {
+        const float a0 = x[k][2 * m] * x[k][2 * m], a1 = x[k][2 * m + 1] * x[k][2 * m + 1];
+        s[m] = a0 + a1;
       }
     }
-    if (q == 0) a.norms[row] = nbits;
+    p[k] = (s[0] + s[1]) + (s[2] + s[3]);
+  }
+}
+
+// Encode: one quad per 128-block.  Grid (gx, gy): blockIdx.y strides over the
+// (batch, head) rows, and quad f of the x-grid over the rows' (token, block)
+// pairs; the x-stride is a multiple of nblk, so a quad keeps one block index j
+// (one sign slice) for the whole kernel.  The next block's input is loaded while
+// the current one is processed.
+template <int BITS, bool BF16>
+__global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
+                                                          SignWords sw) {
+  constexpr int CB = code_bytes_of<BITS>();
+  __shared__ uint2 cells[BITS == 8 ? 1 : kCells];
+  __shared__ float bext[16];
+  if constexpr (BITS != 8) {
+    fill_cells(cells, bext, tab);
+    __syncthreads();
+  }
+  const int q = threadIdx.x & 3;
+  const uint32_t f0 = blockIdx.x * (kEncThreads / 4) + (threadIdx.x >> 2);
+  const uint32_t nblk = static_cast<uint32_t>(a.nblk);
+  const int j = static_cast<int>(f0 % nblk);
+  const int t_first = static_cast<int>(f0 / nblk);
+  const int t_step = static_cast<int>(gridDim.x * (kEncThreads / 4) / nblk);
+  const uint32_t sbits = sw.w[j][q];
+  uint32_t smask[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    smask[i] = (((sbits >> (2 * i)) & 1u) << 15) | (((sbits >> (2 * i + 1)) & 1u) << 31);
+  // mu of the two cross-lane stages, and the sign the lane's results carry after them
+  const float mu1 = (q & 1) ? -1.0f : 1.0f;
+  const float mu2 = (q & 2) ? -1.0f : 1.0f;
+  const uint32_t carried = ((q ^ (q >> 1)) & 1u) << 31;
+
+  const int rows = a.batch * a.heads;
+  for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+    const int b = row / a.heads;
+    const int h = row - b * a.heads;
+    const int tbase = a.t0 ? a.t0[b] : 0;
+    const int64_t xrow = b * a.sb + h * a.sh + static_cast<int64_t>(QK) * j;
+    const int64_t crow = static_cast<int64_t>(row) * a.t_max;
+    auto process = [&](const RawBlock<BF16>& cur, int t) {
+      float x[4][8], p[4];
+      widen<BF16>(cur, smask, sbits, x, p);
+      // canonical norm: levels 3-4 across the quad, 5-6 across chunks
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p[k] = quad_add<0xB1>(p[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p[k] = quad_add<0x4E>(p[k]);
+      const float n32 = __builtin_sqrtf((p[0] + p[1]) + (p[2] + p[3]));
+      // Walsh-Hadamard butterflies, stages 1, 2, 4 (in-chunk), 8, 16 (across the
+      // quad), 32, 64 (across chunks)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bfly(x[k][0], x[k][1]); bfly(x[k][2], x[k][3]);
+        bfly(x[k][4], x[k][5]); bfly(x[k][6], x[k][7]);
+        bfly(x[k][0], x[k][2]); bfly(x[k][1], x[k][3]);
+        bfly(x[k][4], x[k][6]); bfly(x[k][5], x[k][7]);
+        bfly(x[k][0], x[k][4]); bfly(x[k][1], x[k][5]);
+        bfly(x[k][2], x[k][6]); bfly(x[k][3], x[k][7]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage<0xB1>(x[k], mu1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage<0x4E>(x[k], mu2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bfly(x[0][i], x[1][i]);
+        bfly(x[2][i], x[3][i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bfly(x[0][i], x[2][i]);
+        bfly(x[1][i], x[3][i]);
+      }
+
+      const int tt = tbase + t;
+      const bool store = tt >= 0 && tt < a.t_max;
+      const int64_t rowi = (crow + tt) * a.nblk + j;
+      uint8_t* cp = a.codes + rowi * CB;
+      uint16_t nbits;
+      if constexpr (BITS == 8) {
+        // turboq8 grid: per-block absmax scale, codes round((y / s) * 127.5 + 127.5)
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[k][i]));
+        amax = quad_max<0xB1>(amax);
+        amax = quad_max<0x4E>(amax);
+        const __half s16 = __float2half_rn(fp32_value(amax * kInvSqrtQK));
+        const float s32 = __half2float(s16);
+        const float G = __uint_as_float(__float_as_uint(s32 > 0.0f ? kGrid8 / s32 : 0.0f) ^ carried);
+        nbits = __half_as_ushort(s16);
+        if (store) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t code[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float t8 = x[k][i] * G;
+              const float w = t8 + 127.5f;
+              code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
+            }
+            store_chunk<8>(cp, q + 4 * k, code);
+          }
+        }
+      } else {
+        const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
+        const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
+        nbits = __half_as_ushort(__float2half_rn(n32));
+        if (store) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int c = q + 4 * k;
+            if constexpr (BITS == 4) {
+              reinterpret_cast<uint32_t*>(cp)[c] = bucketize8<4>(x[k], g, cells);
+            } else if constexpr (BITS == 2) {
+              reinterpret_cast<uint16_t*>(cp)[c] =
+                  static_cast<uint16_t>(bucketize8<2>(x[k], g, cells));
+            } else {
+              // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
+              const uint32_t w = bucketize8<4>(x[k], g, cells);
+              uint32_t lo = w & 0x33333333u;
+              lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
+              lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+              lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+              uint32_t hi = (w >> 2) & 0x11111111u;
+              hi = (hi | (hi >> 3)) & 0x03030303u;
+              hi = (hi | (hi >> 6)) & 0x000F000Fu;
+              hi = (hi | (hi >> 12)) & 0xFFu;
+              reinterpret_cast<uint16_t*>(cp)[c] = static_cast<uint16_t>(lo);
+              cp[32 + c] = static_cast<uint8_t>(hi);
+            }
+          }
+        }
+      }
+      if (store && q == 0) a.norms[rowi] = nbits;
+    };
+    // ping-pong buffers: block t + t_step loads while block t is processed
+    int t = t_first;
+    RawBlock<BF16> ba, bb;
+    if (t < a.tokens) load_raw<BF16>(a.x, xrow + t * a.st, q, ba);
+    while (t < a.tokens) {
+      if (t + t_step < a.tokens) load_raw<BF16>(a.x, xrow + (t + t_step) * a.st, q, bb);
+      process(ba, t);
+      t += t_step;
+      if (t >= a.tokens) break;
+      if (t + t_step < a.tokens) load_raw<BF16>(a.x, xrow + (t + t_step) * a.st, q, ba);
+      process(bb, t);
+      t += t_step;
+    }
   }
 }
 
@@ -328,12 +537,38 @@ int grid_for(int64_t blocks) {
   return static_cast<int>(g);
 }
 
+// Encode grid: y over (batch, head) rows, x over the quads of a row; about
+// kEncodeWGs workgroups in total, x a multiple of what keeps 64 * x divisible by
+// nblk (so each quad keeps one block index j).
+#ifndef FATQ_ENCODE_WGS
+#define FATQ_ENCODE_WGS 1024
+#endif
+constexpr int64_t kEncodeWGs = FATQ_ENCODE_WGS;
+
+dim3 encode_grid(const EncodeLaunch& a) {
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.heads;
+  const int64_t per_row = static_cast<int64_t>(a.tokens) * a.nblk;
+  const int64_t wg_row = (per_row + kEncThreads / 4 - 1) / (kEncThreads / 4);
+  const int64_t gy = rows < 65535 ? rows : 65535;
+  int64_t gx = kEncodeWGs / gy;
+  if (gx > wg_row) gx = wg_row;
+  if (gx < 1) gx = 1;
+  int64_t g = kEncThreads / 4, n = a.nblk;   // r = nblk / gcd(quads per WG, nblk)
+  while (n != 0) {
+    const int64_t t = g % n;
+    g = n;
+    n = t;
+  }
+  const int64_t r = a.nblk / g;
+  gx = (gx + r - 1) / r * r;
+  return dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy));
+}
+
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
                          hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(a.batch) * a.heads * a.tokens * a.nblk;
-  const dim3 grid(grid_for(total)), block(kThreads);
+  const dim3 grid = encode_grid(a), block(kEncThreads);
 #define FATQ_ENC(B, F) \
   hipLaunchKernelGGL((encode_kernel<B, F>), grid, block, 0, stream, a, tab, sw)
   if (a.x_is_bf16) {

@@ -182,6 +182,17 @@ fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool all
       return fail(FA_TQ_EINVAL, "%s: boundaries are not strictly ascending at %d", what, j);
     tab->b[j] = cb->boundaries[j];
   }
+  // The encoder bucketizes through a table of fp32 cells (values sharing their top
+  // 11 bits) that holds at most one boundary per cell.
+  for (int j = 0; j + 1 < L - 1; ++j) {
+    uint32_t u0, u1;
+    std::memcpy(&u0, &cb->boundaries[j], 4);
+    std::memcpy(&u1, &cb->boundaries[j + 1], 4);
+    if ((u0 >> 21) == (u1 >> 21))
+      return fail(FA_TQ_EUNSUPPORTED,
+                  "%s: boundaries %d and %d are closer than the encoder's cell resolution "
+                  "(ratio <= 1.25)", what, j, j + 1);
+  }
   for (int j = 0; j < L; ++j) {
     if (!std::isfinite(cb->centroids[j]))
       return fail(FA_TQ_EINVAL, "%s: centroid %d is not finite", what, j);

@@ -159,7 +159,18 @@ constexpr int kCellShift = 21;
 constexpr uint32_t kCells = 1u << (32 - kCellShift);   // 2048 cells, 16 KB of LDS
 constexpr uint32_t kNegCell = kCells / 2;
 
-// bext: 16 floats of LDS for the boundaries followed by +inf.
+// Workgroup barrier ordering LDS only: unlike __syncthreads() it does not wait for
+// outstanding global loads, so a prefetch issued before it stays in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// bext: 16 floats of LDS for the boundaries followed by +inf.  Cells whose exponent
+// lies outside the boundaries' exponent range hold no boundary and their base
+// follows from the sign alone; only the few cells inside the range (and the +0
+// cell) count boundaries.
 __device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTable& t) {
   const int nb = t.nb;
   if (threadIdx.x < 16) bext[threadIdx.x] = static_cast<int>(threadIdx.x) < nb ? t.b[threadIdx.x] : INFINITY;
@@ -179,23 +190,31 @@ __device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTab
       nle0 += bm <= 0.0f ? 1u : 0u;
     }
   }
-  __syncthreads();
+  if (emin > emax) emin = emax = 0;   // no nonzero boundary: only the +0 cell counts
+  lds_barrier();
+  // cells outside the range
   for (uint32_t c = threadIdx.x; c < kCells; c += blockDim.x) {
     const uint32_t e = (c >> 2) & 0xFFu;
+    if ((e >= emin && e <= emax) || c == 0) continue;
     const bool neg = c >= kNegCell;
-    uint32_t base;
-    if (e < emin && c != 0) {          // 0 < |u| < every nonzero |boundary|
-      base = neg ? nneg : nle0;
-    } else if (e > emax) {             // |u| above every |boundary|
-      base = neg ? 0u : static_cast<uint32_t>(nb);
-    } else {                           // count directly from the smallest member
-      const uint32_t lo = c << kCellShift;
-      const float umin = __uint_as_float(neg ? (lo | ((1u << kCellShift) - 1u)) : lo);
-      base = 0;
+    const uint32_t base = e < emin ? (neg ? nneg : nle0) : (neg ? 0u : static_cast<uint32_t>(nb));
+    cells[c] = make_uint2(__float_as_uint(bext[base]), base);
+  }
+  // cells inside the range (4 per exponent and sign) and the +0 cell: count the
+  // boundaries below the smallest member
+  const uint32_t per_sign = 4 * (emax - emin + 1);
+  for (uint32_t i = threadIdx.x; i < 2 * per_sign + 1; i += blockDim.x) {
+    uint32_t c;
+    if (i == 2 * per_sign) c = 0;
+    else c = (i < per_sign ? 0u : kNegCell) + 4 * emin + (i % per_sign);
+    if (c == 0 && i != 2 * per_sign) continue;   // +0 cell handled once
+    const bool neg = c >= kNegCell;
+    const uint32_t lo = c << kCellShift;
+    const float umin = __uint_as_float(neg ? (lo | ((1u << kCellShift) - 1u)) : lo);
+    uint32_t base = 0;
 #pragma unroll
-      for (int m = 0; m < 15; ++m)
-        if (m < nb) base += t.b[m] < umin ? 1u : 0u;
-    }
+    for (int m = 0; m < 15; ++m)
+      if (m < nb) base += t.b[m] < umin ? 1u : 0u;
     cells[c] = make_uint2(__float_as_uint(bext[base]), base);
   }
 }
@@ -278,26 +297,63 @@ struct RawBlock {
   uint4 w[BF16 ? 4 : 8];
 };
 
+// Raw buffer resources (per-row base, byte range).  An access whose offset is at or
+// beyond the range is dropped by the hardware (stores) or returns zeros (loads), so
+// lanes without work use offset kOOB instead of a branch: with no divergent control
+// flow around memory operations the compiler can wait for exactly the loads it needs.
+constexpr int32_t kRsrcWord3 = 0x00020000;   // raw dword-format buffer on gfx9
+constexpr uint32_t kOOB = 0x80000000u;        // every range is below 2^31 (host check)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+
+// One block's input in the quad layout from byte offset `off` of resource r.
 template <bool BF16>
-__device__ __forceinline__ void load_raw(const void* base, int64_t off, int q,
-                                         RawBlock<BF16>& r) {
+__device__ __forceinline__ void load_raw(Rsrc r, uint32_t off, int q, RawBlock<BF16>& b) {
   if constexpr (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r.w[k] = p[q + 4 * k];
+    for (int k = 0; k < 4; ++k)
+      b.w[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             r, off + 16 * (q + 4 * k), 0, 0));
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      r.w[2 * k] = p[2 * (q + 4 * k)];
-      r.w[2 * k + 1] = p[2 * (q + 4 * k) + 1];
+      b.w[2 * k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, off + 32 * (q + 4 * k), 0, 0));
+      b.w[2 * k + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     r, off + 32 * (q + 4 * k) + 16, 0, 0));
     }
   }
 }
 
+// Stores of one encoded block (same count and kinds as the encoder's), all to
+// offset kOOB, so they are dropped.
+template <int BITS>
+__device__ __forceinline__ void dummy_stores(Rsrc rc, Rsrc rn) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t o = kOOB + 64 * k;   // distinct offsets: no store is merged away
+    if constexpr (BITS == 8) {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, rc, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, rc, o + 4, 0, 0);
+    } else if constexpr (BITS == 4) {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, rc, o, 0, 0);
+    } else if constexpr (BITS == 2) {
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), rc, o, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), rc, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(0), rc, o + 32, 0, 0);
+    }
+  }
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), rn, kOOB, 0, 0);
+}
+
 // Sign-flip (s * x) and widen to fp32; also return the canonical sum of squares of
-// this lane's 4 chunks (levels 0-2 of the pairwise tree, index bits 0-2).  For bf16
-// inputs x^2 is exact in fp32, so fma(x1, x1, x0 * x0) is the rounded pair sum.
+// this lane's 4 chunks (levels 0-2 of the pairwise tree, index bits 0-2): each square
+// rounded to fp32, then added.
 // smask[k][m]: bit 15 / bit 31 flip the low / high bf16 of word m of chunk k.
 template <bool BF16>
 __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&smask)[16],
@@ -313,7 +369,7 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
         const float lo = __uint_as_float(f << 16), hi = __uint_as_float(f & 0xffff0000u);
         x[k][2 * m] = lo;
         x[k][2 * m + 1] = hi;
-        s[m] = __builtin_fmaf(hi, hi, lo * lo);
+        s[m] = lo * lo + hi * hi;
       }
     } else {
       const uint4 a = r.w[2 * k], b = r.w[2 * k + 1];
@@ -344,7 +400,7 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   __shared__ float bext[16];
   if constexpr (BITS != 8) {
     fill_cells(cells, bext, tab);
-    __syncthreads();
+    lds_barrier();
   }
   const int q = threadIdx.x & 3;
   const uint32_t f0 = blockIdx.x * (kEncThreads / 4) + (threadIdx.x >> 2);
@@ -363,12 +419,22 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   const uint32_t carried = ((q ^ (q >> 1)) & 1u) << 31;
 
   const int rows = a.batch * a.heads;
+  constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
+  const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + QK * a.nblk) * ES);
+  const uint32_t cbytes = static_cast<uint32_t>(a.t_max) * a.nblk * CB;
+  const uint32_t nbytes = static_cast<uint32_t>(a.t_max) * a.nblk * 2;
   for (int row = blockIdx.y; row < rows; row += gridDim.y) {
     const int b = row / a.heads;
     const int h = row - b * a.heads;
     const int tbase = a.t0 ? a.t0[b] : 0;
-    const int64_t xrow = b * a.sb + h * a.sh + static_cast<int64_t>(QK) * j;
-    const int64_t crow = static_cast<int64_t>(row) * a.t_max;
+    const Rsrc rx = make_rsrc(static_cast<const char*>(a.x) + (b * a.sb + h * a.sh) * ES, xbytes);
+    const int64_t crow = static_cast<int64_t>(row) * a.t_max * a.nblk;
+    const Rsrc rc = make_rsrc(a.codes + crow * CB, cbytes);
+    const Rsrc rn = make_rsrc(a.norms + crow, nbytes);
+    // byte offset of block (t, j) in the input row; kOOB past the last token
+    auto xoff = [&](int t) {
+      return t < a.tokens ? static_cast<uint32_t>((t * a.st + QK * j) * ES) : kOOB;
+    };
     auto process = [&](const RawBlock<BF16>& cur, int t) {
       float x[4][8], p[4];
       widen<BF16>(cur, smask, sbits, x, p);
@@ -405,9 +471,9 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
       }
 
       const int tt = tbase + t;
-      const bool store = tt >= 0 && tt < a.t_max;
-      const int64_t rowi = (crow + tt) * a.nblk + j;
-      uint8_t* cp = a.codes + rowi * CB;
+      const bool valid = t < a.tokens && tt >= 0 && tt < a.t_max;
+      const uint32_t cblk = static_cast<uint32_t>(tt * a.nblk + j);
+      const uint32_t co = valid ? cblk * CB : kOOB;
       uint16_t nbits;
       if constexpr (BITS == 8) {
         // turboq8 grid: per-block absmax scale, codes round((y / s) * 127.5 + 127.5)
@@ -422,61 +488,71 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
         const float s32 = __half2float(s16);
         const float G = __uint_as_float(__float_as_uint(s32 > 0.0f ? kGrid8 / s32 : 0.0f) ^ carried);
         nbits = __half_as_ushort(s16);
-        if (store) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            uint32_t code[8];
+        for (int k = 0; k < 4; ++k) {
+          uint32_t code[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float t8 = x[k][i] * G;
-              const float w = t8 + 127.5f;
-              code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
-            }
-            store_chunk<8>(cp, q + 4 * k, code);
+          for (int i = 0; i < 8; ++i) {
+            const float t8 = x[k][i] * G;
+            const float w = t8 + 127.5f;
+            code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
           }
+          const uint32_t lo = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
+          const uint32_t hi = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
+          const uint32_t o = co + 8 * (q + 4 * k);
+          __builtin_amdgcn_raw_buffer_store_b32(lo, rc, o, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(hi, rc, o + 4, 0, 0);
         }
       } else {
         const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
         const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
         nbits = __half_as_ushort(__float2half_rn(n32));
-        if (store) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int c = q + 4 * k;
-            if constexpr (BITS == 4) {
-              reinterpret_cast<uint32_t*>(cp)[c] = bucketize8<4>(x[k], g, cells);
-            } else if constexpr (BITS == 2) {
-              reinterpret_cast<uint16_t*>(cp)[c] =
-                  static_cast<uint16_t>(bucketize8<2>(x[k], g, cells));
-            } else {
-              // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
-              const uint32_t w = bucketize8<4>(x[k], g, cells);
-              uint32_t lo = w & 0x33333333u;
-              lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
-              lo = (lo | (lo >> 4)) & 0x00FF00FFu;
-              lo = (lo | (lo >> 8)) & 0x0000FFFFu;
-              uint32_t hi = (w >> 2) & 0x11111111u;
-              hi = (hi | (hi >> 3)) & 0x03030303u;
-              hi = (hi | (hi >> 6)) & 0x000F000Fu;
-              hi = (hi | (hi >> 12)) & 0xFFu;
-              reinterpret_cast<uint16_t*>(cp)[c] = static_cast<uint16_t>(lo);
-              cp[32 + c] = static_cast<uint8_t>(hi);
-            }
+        for (int k = 0; k < 4; ++k) {
+          const int c = q + 4 * k;
+          if constexpr (BITS == 4) {
+            __builtin_amdgcn_raw_buffer_store_b32(bucketize8<4>(x[k], g, cells), rc, co + 4 * c, 0, 0);
+          } else if constexpr (BITS == 2) {
+            __builtin_amdgcn_raw_buffer_store_b16(
+                static_cast<uint16_t>(bucketize8<2>(x[k], g, cells)), rc, co + 2 * c, 0, 0);
+          } else {
+            // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
+            const uint32_t w = bucketize8<4>(x[k], g, cells);
+            uint32_t lo = w & 0x33333333u;
+            lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
+            lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+            lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+            uint32_t hi = (w >> 2) & 0x11111111u;
+            hi = (hi | (hi >> 3)) & 0x03030303u;
+            hi = (hi | (hi >> 6)) & 0x000F000Fu;
+            hi = (hi | (hi >> 12)) & 0xFFu;
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(lo), rc, co + 2 * c, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(hi), rc, co + 32 + c, 0, 0);
           }
         }
       }
-      if (store && q == 0) a.norms[rowi] = nbits;
+      __builtin_amdgcn_raw_buffer_store_b16(nbits, rn, valid && q == 0 ? 2 * cblk : kOOB, 0, 0);
     };
-    // ping-pong buffers: block t + t_step loads while block t is processed
+    // Ping-pong buffers: block t + t_step loads while block t is processed.  The trip
+    // count is uniform over the wavefront (lane 0 holds its smallest t); lanes past the
+    // last token load zeros and store nothing.
+    // The stores of one block go to offsets past every range here (dropped by the
+    // hardware) after the first load: the loop is then entered with the same
+    // outstanding-memory pattern as every later iteration (loads, then that block's
+    // stores), so the compiler's wait before each block covers only its own loads.
+    // The scheduling barriers keep each prefetch ahead of the block it overlaps.
     int t = t_first;
     RawBlock<BF16> ba, bb;
-    if (t < a.tokens) load_raw<BF16>(a.x, xrow + t * a.st, q, ba);
-    while (t < a.tokens) {
-      if (t + t_step < a.tokens) load_raw<BF16>(a.x, xrow + (t + t_step) * a.st, q, bb);
+    load_raw<BF16>(rx, xoff(t), q, ba);
+    dummy_stores<BITS>(rc, rn);
+    while (__builtin_amdgcn_readfirstlane(t) < a.tokens) {
+      load_raw<BF16>(rx, xoff(t + t_step), q, bb);
+      __builtin_amdgcn_sched_barrier(0);
       process(ba, t);
       t += t_step;
-      if (t >= a.tokens) break;
-      if (t + t_step < a.tokens) load_raw<BF16>(a.x, xrow + (t + t_step) * a.st, q, ba);
+      if (__builtin_amdgcn_readfirstlane(t) >= a.tokens) break;
+      load_raw<BF16>(rx, xoff(t + t_step), q, ba);
+      __builtin_amdgcn_sched_barrier(0);
       process(bb, t);
       t += t_step;
     }

@@ -9,15 +9,30 @@ Prints one JSON line.  ``value`` = algorithmic bytes of a step / step time (GB/s
 Algorithmic bytes: encode = input bytes + packed code bytes + 2-byte norm per
 128-block; attention = per (sequence, token, KV head) the K and V code bytes and
 the two norms, plus the query and output.  Buffers rotate over several copies so
-that consecutive steps do not hit the 256 MB last-level cache with the previous
-step's data.
+that consecutive steps do not find the previous step's data in the 256 MB
+last-level cache.
+
+Per-kernel durations come from HIP events recorded between the launches of every
+timed step (on the stream the library launches on).  The ``roofline.traffic``
+figure is read from the committed rocprofv3 counter summary in ``profiles/`` when
+the kernel's source file still has the hash recorded there, else it is null.
+
+Other modes:
+  --calibrate-copy        before the steps, copy a 256 MiB buffer 5 times (the
+                          plain copy whose counters calibrate FETCH_SIZE/WRITE_SIZE);
+  --summarize-rocprof DIR print per-kernel means of a rocprofv3 CSV directory
+                          (kernel_stats or counter_collection) and exit.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +43,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn packed-KV GB/s + encode vectors/s, % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "kv_cache_vector_fa_amd", "csrc")
+# kernel name prefix (as rocprofv3 reports it) -> source file that defines it
+KERNEL_SOURCE = {"encode_kernel": "codec.hip", "attn_mfma_kernel": "attn_mfma.hip",
+                 "attn_merge_splits_kernel": "attn_mfma.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama_layer_pmc_traffic.txt")
+CALIB_BYTES = 256 << 20
 
 
 def parse():
@@ -38,7 +59,8 @@ def parse():
     p.add_argument("--workload", default="llama_layer")
     p.add_argument("--copies", type=int, default=4, help="input/cache copies rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--summarize-rocprof", metavar="DIR")
     return p.parse_args()
 
 
@@ -54,18 +76,53 @@ def attn_bytes(lens, hkv, hq, kb, vb) -> int:
     return int(np.sum(lens)) * per_tok + len(lens) * hq * 128 * (2 + 4)
 
 
-def time_events(fn, reps: int) -> float:
-    """Average ms per call of ``fn`` over ``reps`` back-to-back calls (HIP events on
-    the current stream, which is the stream the library launches on)."""
-    import torch
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+def source_hash(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def short_kernel(name: str) -> str:
+    n = name.split("(anonymous namespace)::")[-1]
+    n = re.sub(r"^void ", "", n)
+    return n.split("(")[0].strip()
+
+
+def summarize_rocprof(d: str) -> None:
+    """Per-kernel means of the rocprofv3 CSV files in ``d``."""
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# {os.path.basename(f)}: kernel | calls | average_ns | min_ns | max_ns")
+        for r in csv.DictReader(open(f)):
+            print(f"{short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                  f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg, disp = {}, {}
+        for r in csv.DictReader(open(f)):
+            k = short_kernel(r["Kernel_Name"])
+            agg.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+            agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp.setdefault(k, set()).add(r["Dispatch_Id"])
+        print(f"# {os.path.basename(f)}: kernel | dispatches | counter=mean per dispatch")
+        for k, cs in agg.items():
+            n = len(disp[k])
+            print(f"{k} | {n} | " + " ".join(f"{c}={v / n:.6g}" for c, v in sorted(cs.items())))
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, or None
+    when it is absent or the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals, hashes = {}, {}
+    for line in open(TRAFFIC_FILE):
+        f = [x.strip() for x in line.split("|")]
+        if f[0] == "source_sha256" and len(f) == 3:
+            hashes[f[1]] = f[2]
+        elif f[0] == "traffic" and len(f) >= 3:
+            vals[f[1]] = float(f[2])
+    src = next((v for p, v in KERNEL_SOURCE.items() if kernel.startswith(p)), None)
+    if kernel not in vals or src is None or hashes.get(src) != source_hash(src):
+        return None
+    return vals[kernel]
 
 
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
@@ -73,7 +130,6 @@ def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float =
     (default: all of them): encode their K and V blocks in canonical fp32 and run fp64
     attention for their query heads; repeated until ``min_seconds`` have passed."""
     n_slices = n_slices or w.n_kv_heads
-    import torch
     from threadpoolctl import threadpool_limits
 
     import workloads
@@ -85,6 +141,7 @@ def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float =
     T = w.tokens
     k, v = workloads.make_kv(w, "cpu", batch=1)
     q = workloads.make_q(w, "cpu", batch=1)
+    import torch
     k32 = k[:, :n_slices].to(torch.float32).numpy()
     v32 = v[:, :n_slices].to(torch.float32).numpy()
     grp = w.n_q_heads // w.n_kv_heads
@@ -121,6 +178,9 @@ def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float =
 
 def main():
     args = parse()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
@@ -131,6 +191,13 @@ def main():
 
     fa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.WORKLOADS[args.workload]
     seed = workloads.ROTATION_SEED
     B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim
@@ -147,59 +214,59 @@ def main():
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     ws = fa.attn_workspace(B, Hq, Hkv, T, d)
     scale = 1 / np.sqrt(d)
-
-    def enc_k(i):
-        kc, kn, _, _ = caches[i % R]
-        fa.encode(cbk, seed, ks[i % R], codes=kc, norms=kn)
-
-    def enc_v(i):
-        _, _, vc, vn = caches[i % R]
-        fa.encode(cbv, seed, vs[i % R], codes=vc, norms=vn)
-
-    def attn(i):
-        kc, kn, vc, vn = caches[i % R]
-        fa.attn_decode(cbk, cbv, seed, q, kc, kn, vc, vn, lens, scale, out=out, workspace=ws)
-
-    def step(i):
-        enc_k(i)
-        enc_v(i)
-        attn(i)
+    # arguments marshalled once per buffer copy: a launch costs one ctypes call
+    enc_k = [fa.encode_call(cbk, seed, ks[i], caches[i][0], caches[i][1]) for i in range(R)]
+    enc_v = [fa.encode_call(cbv, seed, vs[i], caches[i][2], caches[i][3]) for i in range(R)]
+    attn = [fa.attn_decode_call(cbk, cbv, seed, q, *caches[i], lens, scale, out, ws)
+            for i in range(R)]
+    names = ("encode_k", "encode_v", "attn_decode")
+    calls = (enc_k, enc_v, attn)
 
     for i in range(args.warmup):
-        step(i)
+        for c in calls:
+            c[i % R]()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(step, args.steps)
+    for i in range(K):
+        for j, c in enumerate(calls):
+            ev[3 * i + j].record()
+            c[i % R]()
+    ev[3 * K].record()
+    t_host = time.perf_counter() - t0
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[3 * K]) / K
+    kms = [sum(ev[3 * i + j].elapsed_time(ev[3 * i + j + 1]) for i in range(K)) / K
+           for j in range(3)]
 
     nblk = B * Hkv * T * (d // 128)
-    b_ek = enc_bytes(nblk, 256, w.k_bits)
-    b_ev = enc_bytes(nblk, 256, w.v_bits)
-    b_at = attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits)
-    step_bytes = b_ek + b_ev + b_at
-
-    reps = args.kernel_reps
+    nbytes = (enc_bytes(nblk, 256, w.k_bits), enc_bytes(nblk, 256, w.v_bits),
+              attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits))
+    step_bytes = sum(nbytes)
     kern = {}
-    for name, fn, nbytes, vecs in (("encode_k", enc_k, b_ek, nblk), ("encode_v", enc_v, b_ev, nblk),
-                                   ("attn_decode", attn, b_at, None)):
-        fn(0)
-        kms = time_events(fn, reps)
-        rec = {"us": round(kms * 1e3, 3), "algorithmic_bytes": nbytes,
-               "gbps": round(nbytes / (kms * 1e-3) / 1e9, 1),
-               "frac_hbm_peak": round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        if vecs:
-            rec["vectors_per_s"] = round(vecs / (d // 128) / (kms * 1e-3), 1)
+    for name, km, nb in zip(names, kms, nbytes):
+        gbs = nb / (km * 1e-3) / 1e9
+        rec = {"us": round(km * 1e3, 3), "algorithmic_bytes": nb, "gbps": round(gbs, 1),
+               "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        if name.startswith("encode"):
+            rec["vectors_per_s"] = round(nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["gbps"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": None}
+    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true>",
+             "encode_v": f"encode_kernel<{w.v_bits}, true>"}.get(dom, dom)
+    traffic = traffic_for(kname)
+    roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
+            "traffic": None if traffic is None else round(traffic)}
 
     rec = {
         "metric": METRIC,
         "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -211,7 +278,8 @@ def main():
                    "tokens": T, "head_dim": d, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "step": "encode K + encode V + decode attention", "copies": R},
         "step_algorithmic_bytes": step_bytes,
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(wall, 4),
+        "host_us_per_step": round(t_host / K * 1e6, 1),
         "kernels": kern,
         "roofline": roof,
     }

@@ -217,3 +217,50 @@ def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, 
                                  float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------ prepared device calls
+
+def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = None, t0=None,
+                stream=None):
+    """``encode`` with its arguments marshalled once: returns a callable that launches
+    fa_tq_encode on the same tensors (for tight loops where per-call Python work
+    would dominate the kernel)."""
+    lib = load()
+    B, H, T, d = x.shape
+    if x.stride(3) != 1:
+        raise ValueError("channel stride must be 1")
+    t_max = T if t_max is None else t_max
+    args = (ctypes.byref(cb), ctypes.c_uint64(seed), ctypes.c_int32(d), _ptr(x),
+            ctypes.c_int(_dtype_code(x)), Layout(x.stride(0), x.stride(1), x.stride(2)),
+            ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(T), _ptr(t0),
+            ctypes.c_int32(t_max), _ptr(codes), _ptr(norms), _stream(stream))
+    fn = lib.fa_tq_encode
+    keep = (cb, x, codes, norms, t0)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call
+
+
+def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,
+                     v_norms, seq_lens, scale: float, out, workspace, stream=None):
+    """``attn_decode`` with its arguments marshalled once (see ``encode_call``)."""
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    args = (ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_int32(d),
+            _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_codes), _ptr(k_norms),
+            _ptr(v_codes), _ptr(v_norms), _ptr(seq_lens), ctypes.c_int32(B),
+            ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max),
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
+    fn = lib.fa_tq_attn_decode
+    keep = (cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, seq_lens, out, workspace)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call
+

@@ -20,13 +20,19 @@ sequence of length 0 gives an all-zero output; the scale is a caller argument
 
 ``attend_bruteforce`` is the plain definition softmax(scale q K_hat^T) V_hat on the
 decoded cache (``codec.decode_mse``), used to pin ``attend_fused``.
+
+``append_attend`` is [Spec] "Attention with TurboQuant cache": quantize the new K
+and V vectors into the cache at their positions, then attend with the
+full-precision query over the cached positions.  Positions map to cache slots
+modulo the cache length ([Spec] "Integration Points": circular addressing
+cache_pos = pos % max_seq), so a full ring holds the last max_seq tokens.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .codec import decode_mse, unpack
+from .codec import decode_mse, encode_mse, pack, unpack
 from .rotation import QK, forward64, inverse64
 
 
@@ -98,3 +104,35 @@ def attend_bruteforce(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v
             p = _softmax64(scale * (kh @ q[b, h]))
             out[b, h] = p @ vh
     return out
+
+
+def append_attend(q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, k_bits, v_bits,
+                  k_boundaries, k_centroids, v_boundaries, v_centroids, s, scale):
+    """Append then attend (fp64 attention; canonical fp32 encode).
+
+    q: [B, Hq, d]; k_new/v_new: [B, Hkv, n_new, d] float32; pos: [B] position of the
+    first new token of each sequence; caches as in ``attend_fused`` with T slots.
+    Token i of sequence b is encoded into slot (pos[b] + i) mod T; the attention then
+    covers the min(pos[b] + n_new, T) filled slots (softmax and the weighted sum do
+    not depend on slot order).  The caches are updated in place.
+    Returns (out [B, Hq, d] float64, seq_lens [B]).
+    """
+    k_new = np.asarray(k_new, np.float32)
+    v_new = np.asarray(v_new, np.float32)
+    B, Hkv, n_new, d = k_new.shape
+    T = k_codes.shape[2]
+    kc, kn, _ = encode_mse(k_new, s, k_boundaries)
+    vc, vn, _ = encode_mse(v_new, s, v_boundaries)
+    kp, vp = pack(kc, k_bits), pack(vc, v_bits)
+    for b in range(B):
+        for i in range(n_new):
+            slot = (int(pos[b]) + i) % T
+            k_codes[b, :, slot] = kp[b, :, i]
+            v_codes[b, :, slot] = vp[b, :, i]
+            k_norms[b, :, slot] = kn[b, :, i]
+            v_norms[b, :, slot] = vn[b, :, i]
+    lens = np.array([min(int(pos[b]) + n_new, T) for b in range(B)], np.int64)
+    out = attend_fused(q, k_codes, k_norms, v_codes, v_norms, lens, k_bits, v_bits,
+                       k_centroids, v_centroids, s, scale)
+    return out, lens
+

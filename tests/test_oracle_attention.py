@@ -119,3 +119,92 @@ def test_quality_matches_spec_table_correlated():
     qs = np.random.default_rng(101).standard_normal((20, 128))
     c = _cosine_study(k, v, qs, 4, 2)
     assert 0.96 <= c <= 0.99, (c, GOLDEN["attention_cosine"]["k4v2_correlated"])
+
+
+def _empty_cache(B, Hkv, T, d, kb, vb):
+    nblk = d // 128
+    return (np.zeros((B, Hkv, T, nblk, codec.code_bytes(kb)), np.uint8),
+            np.zeros((B, Hkv, T, nblk), np.float16),
+            np.zeros((B, Hkv, T, nblk, codec.code_bytes(vb)), np.uint8),
+            np.zeros((B, Hkv, T, nblk), np.float16))
+
+
+def test_append_first_token_gives_its_value():
+    """pos 0 into an empty cache: one cached token, so every head returns its V_hat."""
+    rng = np.random.default_rng(3)
+    d, s = 128, sg.signs(42, 128)
+    bk, ck = cbm.codebook(4)
+    bv, cv = cbm.codebook(2)
+    kc, kn, vc, vn = _empty_cache(1, 2, 16, d, 4, 2)
+    kx = rng.standard_normal((1, 2, 1, d)).astype(np.float32)
+    vx = rng.standard_normal((1, 2, 1, d)).astype(np.float32)
+    q = rng.standard_normal((1, 4, d)).astype(np.float32)
+    out, lens = att.append_attend(q, kx, vx, [0], kc, kn, vc, vn, 4, 2, bk, ck, bv, cv, s, 0.1)
+    assert list(lens) == [1]
+    for h in range(4):
+        g = h // 2
+        vhat = codec.decode_mse(codec.unpack(vc[0, g, :1], 2), vn[0, g, :1], s, cv)[0]
+        np.testing.assert_allclose(out[0, h], vhat, atol=1e-12)
+    # slot 0 holds exactly the packed encoding of the new vectors
+    ref_k, ref_kn, _ = codec.encode_mse(kx, s, bk)
+    np.testing.assert_array_equal(kc[0, :, 0], codec.pack(ref_k, 4)[0, :, 0])
+    np.testing.assert_array_equal(kn[0, :, 0], ref_kn[0, :, 0])
+
+
+@pytest.mark.parametrize("n_new", [1, 3])
+def test_append_ring_equals_attention_over_last_tokens(n_new):
+    """Appending a stream of tokens into a ring of T slots, then attending, equals
+    brute-force attention over the last T tokens encoded into a plain cache (the
+    circular addressing keeps exactly those, in some slot order)."""
+    rng = np.random.default_rng(4)
+    d, T, Hkv, Hq, total = 128, 7, 2, 4, 23
+    s = sg.signs(42, d)
+    bk, ck = cbm.codebook(4)
+    bv, cv = cbm.codebook(3)
+    kx = rng.standard_normal((1, Hkv, total, d)).astype(np.float32)
+    vx = rng.standard_normal((1, Hkv, total, d)).astype(np.float32)
+    q = rng.standard_normal((1, Hq, d)).astype(np.float32)
+    ring = _empty_cache(1, Hkv, T, d, 4, 3)
+    pos = 0
+    while pos < total:
+        n = min(n_new, total - pos)
+        out, lens = att.append_attend(q, kx[:, :, pos:pos + n], vx[:, :, pos:pos + n], [pos],
+                                      *ring, 4, 3, bk, ck, bv, cv, s, 0.09)
+        pos += n
+        assert list(lens) == [min(pos, T)]
+    kc, kn, vc, vn = _cache(kx[:, :, total - T:], vx[:, :, total - T:], s, 4, 3)
+    ref = att.attend_bruteforce(q, kc, kn, vc, vn, [T], 4, 3, ck, cv, s, 0.09)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_append_per_sequence_positions():
+    """Each sequence appends at its own position; a sequence that has not wrapped
+    attends over pos + n_new tokens, one that has wrapped over all T slots."""
+    rng = np.random.default_rng(5)
+    d, T, Hkv, Hq = 128, 9, 1, 2
+    s = sg.signs(42, d)
+    bk, ck = cbm.codebook(4)
+    bv, cv = cbm.codebook(2)
+    kc, kn, vc, vn = _empty_cache(2, Hkv, T, d, 4, 2)
+    hist_k = rng.standard_normal((2, Hkv, T, d)).astype(np.float32)
+    hist_v = rng.standard_normal((2, Hkv, T, d)).astype(np.float32)
+    pk, pkn, pv, pvn = _cache(hist_k, hist_v, s, 4, 2)
+    kc[:], kn[:], vc[:], vn[:] = pk, pkn, pv, pvn
+    kx = rng.standard_normal((2, Hkv, 2, d)).astype(np.float32)
+    vx = rng.standard_normal((2, Hkv, 2, d)).astype(np.float32)
+    q = rng.standard_normal((2, Hq, d)).astype(np.float32)
+    out, lens = att.append_attend(q, kx, vx, [3, 17], kc, kn, vc, vn, 4, 2, bk, ck, bv, cv, s,
+                                  0.09)
+    assert list(lens) == [5, 9]
+    # sequence 0: history slots 0-2, new tokens in slots 3-4
+    k0 = np.concatenate([hist_k[0:1, :, :3], kx[0:1]], axis=2)
+    v0 = np.concatenate([hist_v[0:1, :, :3], vx[0:1]], axis=2)
+    # sequence 1: positions 17, 18 -> slots 8, 0; the other slots keep the history
+    k1 = hist_k[1:2].copy()
+    v1 = hist_v[1:2].copy()
+    k1[:, :, 8], k1[:, :, 0] = kx[1, :, 0], kx[1, :, 1]
+    v1[:, :, 8], v1[:, :, 0] = vx[1, :, 0], vx[1, :, 1]
+    for b, (kk, vv, L) in enumerate(((k0, v0, 5), (k1, v1, 9))):
+        c = _cache(kk, vv, s, 4, 2)
+        ref = att.attend_bruteforce(q[b:b + 1], *c, [L], 4, 2, ck, cv, s, 0.09)
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)

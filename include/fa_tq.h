@@ -166,6 +166,36 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook 
                                float scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Append, then attend ([Spec] "Attention with TurboQuant cache": the cached-attention
+ * call quantizes the current K and V into the cache, then attends with the full-
+ * precision query; [Spec] "Integration Points": circular addressing, cache position
+ * = pos % max_seq).  In one call, on `stream`:
+ *   1. encode k_new[b][h][i][:] and v_new[b][h][i][:] (i < n_new) as fa_tq_encode
+ *      does, into cache slot (pos[b] + i) % t_max of sequence b;
+ *   2. decode attention as fa_tq_attn_decode with seq_lens[b] = min(pos[b] + n_new,
+ *      t_max): every filled slot (a full ring holds the last t_max tokens; the
+ *      result does not depend on slot order).
+ *   q, out, workspace: as for fa_tq_attn_decode; k_new, v_new: device, kv_dtype, with
+ *      the element strides of k_layout / v_layout (channel stride 1), 16-byte aligned.
+ *   pos: device int32[batch], positions >= 0 (a negative position stores nothing and
+ *      clamps the attended length at 0).
+ *   codebooks: bits 2, 3 or 4 for keys and values; head_dim 128 (this build).
+ *   1 <= n_new <= t_max (two new tokens never share a slot); every argument is
+ *   checked before anything is written to the cache.
+ */
+fa_tq_status fa_tq_attn_append(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                               uint64_t seed, int32_t head_dim,
+                               const void *q, fa_tq_dtype q_dtype,
+                               const void *k_new, const void *v_new, fa_tq_dtype kv_dtype,
+                               fa_tq_layout k_layout, fa_tq_layout v_layout,
+                               int32_t n_new, const int32_t *pos,
+                               uint8_t *k_codes, uint16_t *k_norms,
+                               uint8_t *v_codes, uint16_t *v_norms,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t t_max, float scale, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

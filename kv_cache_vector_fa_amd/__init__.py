@@ -65,6 +65,12 @@ _SIGS = {
                                          _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
                                          _P, ctypes.c_size_t, _P]),
+    "fa_tq_attn_append": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook),
+                                         ctypes.c_uint64, ctypes.c_int32, _P, ctypes.c_int,
+                                         _P, _P, ctypes.c_int, Layout, Layout, ctypes.c_int32,
+                                         _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
+                                         _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -215,6 +221,55 @@ def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, 
                                  _dtype_code(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
                                  _ptr(v_norms), _ptr(seq_lens), B, Hq, Hkv, t_max,
                                  float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return out
+
+
+def _expect(t, shape, dtype, name):
+    """Shape/dtype/contiguity check of a device buffer the kernels index densely."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} (contiguous={t.is_contiguous()})")
+
+
+def _expect_cache(codes, norms, B, H, t_max, d, bits, name):
+    import torch
+    nblk = d // QK
+    _expect(codes, (B, H, t_max, nblk, code_bytes(bits)), torch.uint8, f"{name} codes")
+    _expect(norms, (B, H, t_max, nblk), torch.int16, f"{name} norms")
+
+
+def attn_append(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos, k_codes,
+                k_norms, v_codes, v_norms, scale: float, out=None, workspace=None, stream=None):
+    """Append k_new/v_new [B, Hkv, n_new, d] at positions pos [B] (slot = position mod
+    T_max) into the packed caches, then decode attention for q [B, Hq, d]."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    _, Hkv, n_new, _ = k_new.shape
+    t_max = k_codes.shape[2]
+    if k_new.dtype != v_new.dtype or k_new.stride(3) != 1 or v_new.stride(3) != 1:
+        raise ValueError("k_new and v_new need one dtype and channel stride 1")
+    if tuple(v_new.shape) != tuple(k_new.shape) or k_new.shape[0] != B or k_new.shape[3] != d:
+        raise ValueError(f"k_new {tuple(k_new.shape)}, v_new {tuple(v_new.shape)} for q "
+                         f"{tuple(q.shape)}")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
+    _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _expect(out, (B, Hq, d), torch.float32, "out")
+    if workspace is None:
+        workspace = attn_workspace(B, Hq, Hkv, t_max, d, q.device)
+    kl = Layout(k_new.stride(0), k_new.stride(1), k_new.stride(2))
+    vl = Layout(v_new.stride(0), v_new.stride(1), v_new.stride(2))
+    _check(lib.fa_tq_attn_append(ctypes.byref(cb_k), ctypes.byref(cb_v), seed, d, _ptr(q),
+                                 _dtype_code(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                 kl, vl, n_new, _ptr(pos), _ptr(k_codes), _ptr(k_norms),
+                                 _ptr(v_codes), _ptr(v_norms), B, Hq, Hkv, t_max, float(scale),
+                                 _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
     return out
 

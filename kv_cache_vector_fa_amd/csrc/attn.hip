@@ -136,8 +136,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_split_kernel(AttnLaunch a, K
 
   const int split = blockIdx.x * kWaves + wave;
   if (split >= a.n_split) return;
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.t_max ? a.t_max : len);
+  const int64_t len64 = a.pos ? static_cast<int64_t>(a.pos[b]) + a.n_new : a.seq_lens[b];
+  const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
   const int t_begin = split * a.chunk;
   const int t_end = min(len, t_begin + a.chunk);
   const float sc2 = a.scale * kLog2e;

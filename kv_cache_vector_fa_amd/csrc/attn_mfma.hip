@@ -262,8 +262,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   const int G = GT > 0 ? GT : a.hq / a.hkv;
 
   // ---- the sequence range, then the first super tile's loads (in flight during setup)
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.t_max ? a.t_max : len);
+  const int64_t len64 = a.pos ? static_cast<int64_t>(a.pos[b]) + a.n_new : a.seq_lens[b];
+  const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
   const int c0 = split * a.chunk;
   const int c1 = min(len, c0 + a.chunk);
   const int last = c1 - 1;

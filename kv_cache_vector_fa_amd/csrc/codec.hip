@@ -470,7 +470,10 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
         bfly(x[1][i], x[3][i]);
       }
 
-      const int tt = tbase + t;
+      // position tbase + t, or its ring slot; 0 <= tbase + t < 2^32 when tbase >= 0
+      int64_t tt = static_cast<int64_t>(tbase) + t;
+      if (a.ring && tt >= 0)
+        tt = static_cast<uint32_t>(tt) % static_cast<uint32_t>(a.t_max);
       const bool valid = t < a.tokens && tt >= 0 && tt < a.t_max;
       const uint32_t cblk = static_cast<uint32_t>(tt * a.nblk + j);
       const uint32_t co = valid ? cblk * CB : kOOB;

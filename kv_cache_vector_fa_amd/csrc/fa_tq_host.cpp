@@ -215,6 +215,129 @@ fa_tq_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t seed,
+                         int32_t head_dim,
+                          const void* x, fa_tq_dtype x_dtype, fa_tq_layout x_layout,
+                          int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                          const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
+                          void* stream, bool ring, bool check_only = false) {
+  fatq::KTable tab;
+  fa_tq_status st = check_codebook(cb, who, true, &tab);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative size", who);
+  if (x_dtype != FA_TQ_F32 && x_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: input dtype %d", who, (int)x_dtype);
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if (!x || !codes || !norms)
+    return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return fail(FA_TQ_EINVAL, "%s: x and codes must be 16-byte aligned, norms 2-byte", who);
+  if (x_layout.stride_b % 8 || x_layout.stride_h % 8 || x_layout.stride_t % 8 ||
+      x_layout.stride_b < 0 || x_layout.stride_h < 0 || x_layout.stride_t < 0)
+    return fail(FA_TQ_EINVAL, "%s: strides must be non-negative multiples of 8", who);
+  if (n_tokens > t_max && !t0)
+    return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  // The kernel addresses one (batch, head) row of input, codes and norms with 32-bit
+  // byte offsets below 2^31.
+  const int64_t esize = x_dtype == FA_TQ_BF16 ? 2 : 4;
+  const int64_t xrow = ((static_cast<int64_t>(n_tokens) - 1) * x_layout.stride_t + head_dim) * esize;
+  const int64_t crow = static_cast<int64_t>(t_max) * (head_dim / fatq::QK) * fa_tq_code_bytes(cb->bits);
+  if (xrow >= (int64_t{1} << 31) || crow >= (int64_t{1} << 31))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: one (batch, head) row spans 2 GiB or more", who);
+  if (check_only) return ok();
+  fatq::EncodeLaunch a;
+  a.x = x;
+  a.sb = x_layout.stride_b;
+  a.sh = x_layout.stride_h;
+  a.st = x_layout.stride_t;
+  a.batch = batch;
+  a.heads = n_kv_heads;
+  a.tokens = n_tokens;
+  a.nblk = head_dim / fatq::QK;
+  a.t_max = t_max;
+  a.t0 = t0;
+  a.ring = ring ? 1 : 0;
+  a.codes = codes;
+  a.norms = norms;
+  a.x_is_bf16 = x_dtype == FA_TQ_BF16;
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  return launched(fatq::launch_encode(a, tab, sw, static_cast<hipStream_t>(stream)),
+                  who);
+}
+
+fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
+                       const fa_tq_codebook* cb_v, uint64_t seed, int32_t head_dim,
+                       const void* q, fa_tq_dtype q_dtype, const uint8_t* k_codes,
+                       const uint16_t* k_norms, const uint8_t* v_codes,
+                       const uint16_t* v_norms, const int32_t* seq_lens, const int32_t* pos,
+                       int32_t n_new, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t t_max, float scale, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream, bool check_only = false) {
+  fatq::KTable tk, tv;
+  fa_tq_status st = check_codebook(cb_k, who, false, &tk);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_codebook(cb_v, who, false, &tv)) != FA_TQ_OK)
+    return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (head_dim != fatq::QK)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (this build: 128)", who,
+                head_dim);
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: bad sizes", who);
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(FA_TQ_EINVAL, "%s: n_q_heads %d not a multiple of n_kv_heads %d", who,
+                n_q_heads, n_kv_heads);
+  if (n_q_heads / n_kv_heads > 16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: group size %d > 16", who,
+                n_q_heads / n_kv_heads);
+  if (q_dtype != FA_TQ_F32 && q_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: query dtype %d", who, (int)q_dtype);
+  if (!std::isfinite(scale)) return fail(FA_TQ_EINVAL, "%s: scale not finite", who);
+  if (batch == 0) return ok();
+  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !(seq_lens || pos) || !out ||
+      !workspace)
+    return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out) || !aligned16(workspace) ||
+      !aligned16(q) || (reinterpret_cast<uintptr_t>(k_norms) & 1u) ||
+      (reinterpret_cast<uintptr_t>(v_norms) & 1u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return fail(FA_TQ_EINVAL, "%s: misaligned pointer", who);
+  const size_t need =
+      fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim);
+  if (workspace_bytes < need)
+    return fail(FA_TQ_EINVAL, "%s: workspace %zu bytes < %zu", who, workspace_bytes,
+                need);
+  if (check_only) return ok();
+  fatq::AttnLaunch a;
+  a.q = q;
+  a.q_is_bf16 = q_dtype == FA_TQ_BF16;
+  a.k_codes = k_codes;
+  a.k_norms = k_norms;
+  a.v_codes = v_codes;
+  a.v_norms = v_norms;
+  a.seq_lens = seq_lens;
+  a.pos = pos;
+  a.n_new = n_new;
+  a.batch = batch;
+  a.hq = n_q_heads;
+  a.hkv = n_kv_heads;
+  a.t_max = t_max;
+  a.scale = scale;
+  a.out = out;
+  a.workspace = workspace;
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+    return launched(fatq::launch_attn_mfma(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
+                    who);
+  }
+  fatq::attn_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+  return launched(fatq::launch_attn(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
+                  who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,41 +397,8 @@ fa_tq_status fa_tq_encode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
                           int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
                           const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
                           void* stream) {
-  fatq::KTable tab;
-  fa_tq_status st = check_codebook(cb, "fa_tq_encode", true, &tab);
-  if (st != FA_TQ_OK) return st;
-  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
-  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
-    return fail(FA_TQ_EINVAL, "fa_tq_encode: negative size");
-  if (x_dtype != FA_TQ_F32 && x_dtype != FA_TQ_BF16)
-    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_encode: input dtype %d", (int)x_dtype);
-  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
-  if (!x || !codes || !norms)
-    return fail(FA_TQ_EINVAL, "fa_tq_encode: NULL device pointer");
-  if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(norms) & 1u))
-    return fail(FA_TQ_EINVAL, "fa_tq_encode: x and codes must be 16-byte aligned, norms 2-byte");
-  if (x_layout.stride_b % 8 || x_layout.stride_h % 8 || x_layout.stride_t % 8 ||
-      x_layout.stride_b < 0 || x_layout.stride_h < 0 || x_layout.stride_t < 0)
-    return fail(FA_TQ_EINVAL, "fa_tq_encode: strides must be non-negative multiples of 8");
-  if (n_tokens > t_max && !t0)
-    return fail(FA_TQ_EINVAL, "fa_tq_encode: n_tokens %d > t_max %d", n_tokens, t_max);
-  fatq::EncodeLaunch a;
-  a.x = x;
-  a.sb = x_layout.stride_b;
-  a.sh = x_layout.stride_h;
-  a.st = x_layout.stride_t;
-  a.batch = batch;
-  a.heads = n_kv_heads;
-  a.tokens = n_tokens;
-  a.nblk = head_dim / fatq::QK;
-  a.t_max = t_max;
-  a.t0 = t0;
-  a.codes = codes;
-  a.norms = norms;
-  a.x_is_bf16 = x_dtype == FA_TQ_BF16;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  return launched(fatq::launch_encode(a, tab, sw, static_cast<hipStream_t>(stream)),
-                  "fa_tq_encode");
+  return encode_impl("fa_tq_encode", cb, seed, head_dim, x, x_dtype, x_layout, batch,
+                     n_kv_heads, n_tokens, t0, t_max, codes, norms, stream, false);
 }
 
 fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
@@ -337,62 +427,47 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook*
                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t t_max, float scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  fatq::KTable tk, tv;
-  fa_tq_status st = check_codebook(cb_k, "fa_tq_attn_decode (keys)", false, &tk);
-  if (st != FA_TQ_OK) return st;
-  if ((st = check_codebook(cb_v, "fa_tq_attn_decode (values)", false, &tv)) != FA_TQ_OK)
-    return st;
-  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
-  if (head_dim != fatq::QK)
-    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: head_dim %d (this build: 128)",
-                head_dim);
-  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0)
-    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: bad sizes");
-  if (n_q_heads % n_kv_heads != 0)
-    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: n_q_heads %d not a multiple of n_kv_heads %d",
-                n_q_heads, n_kv_heads);
-  if (n_q_heads / n_kv_heads > 16)
-    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: group size %d > 16",
-                n_q_heads / n_kv_heads);
-  if (q_dtype != FA_TQ_F32 && q_dtype != FA_TQ_BF16)
-    return fail(FA_TQ_EUNSUPPORTED, "fa_tq_attn_decode: query dtype %d", (int)q_dtype);
-  if (!std::isfinite(scale)) return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: scale not finite");
+  if (batch > 0 && !seq_lens) return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: seq_lens is NULL");
+  return attn_impl("fa_tq_attn_decode", cb_k, cb_v, seed, head_dim, q, q_dtype, k_codes,
+                   k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
+                   n_kv_heads, t_max, scale, out, workspace, workspace_bytes, stream);
+}
+
+fa_tq_status fa_tq_attn_append(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                               uint64_t seed, int32_t head_dim, const void* q,
+                               fa_tq_dtype q_dtype, const void* k_new, const void* v_new,
+                               fa_tq_dtype kv_dtype, fa_tq_layout k_layout,
+                               fa_tq_layout v_layout, int32_t n_new, const int32_t* pos,
+                               uint8_t* k_codes, uint16_t* k_norms, uint8_t* v_codes,
+                               uint16_t* v_norms, int32_t batch, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t t_max, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* who = "fa_tq_attn_append";
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max <= 0)
+    return fail(FA_TQ_EINVAL, "%s: bad sizes", who);
+  if (n_new < 1 || n_new > t_max)
+    return fail(FA_TQ_EINVAL, "%s: n_new %d not in [1, t_max %d]", who, n_new, t_max);
   if (batch == 0) return ok();
-  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace)
-    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: NULL device pointer");
-  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(out) || !aligned16(workspace) ||
-      !aligned16(q) || (reinterpret_cast<uintptr_t>(k_norms) & 1u) ||
-      (reinterpret_cast<uintptr_t>(v_norms) & 1u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
-    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: misaligned pointer");
-  const size_t need =
-      fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim);
-  if (workspace_bytes < need)
-    return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: workspace %zu bytes < %zu", workspace_bytes,
-                need);
-  fatq::AttnLaunch a;
-  a.q = q;
-  a.q_is_bf16 = q_dtype == FA_TQ_BF16;
-  a.k_codes = k_codes;
-  a.k_norms = k_norms;
-  a.v_codes = v_codes;
-  a.v_norms = v_norms;
-  a.seq_lens = seq_lens;
-  a.batch = batch;
-  a.hq = n_q_heads;
-  a.hkv = n_kv_heads;
-  a.t_max = t_max;
-  a.scale = scale;
-  a.out = out;
-  a.workspace = workspace;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
-    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
-    return launched(fatq::launch_attn_mfma(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
-                    "fa_tq_attn_decode");
+  if (!pos) return fail(FA_TQ_EINVAL, "%s: pos is NULL", who);
+  // Every argument of the three steps is checked before the first launch, so a
+  // rejected call leaves the cache untouched.
+  fa_tq_status st;
+  for (bool check_only : {true, false}) {
+    if ((st = encode_impl(who, cb_k, seed, head_dim, k_new, kv_dtype, k_layout, batch,
+                          n_kv_heads, n_new, pos, t_max, k_codes, k_norms, stream, true,
+                          check_only)) != FA_TQ_OK)
+      return st;
+    if ((st = encode_impl(who, cb_v, seed, head_dim, v_new, kv_dtype, v_layout, batch,
+                          n_kv_heads, n_new, pos, t_max, v_codes, v_norms, stream, true,
+                          check_only)) != FA_TQ_OK)
+      return st;
+    if ((st = attn_impl(who, cb_k, cb_v, seed, head_dim, q, q_dtype, k_codes, k_norms,
+                        v_codes, v_norms, nullptr, pos, n_new, batch, n_q_heads, n_kv_heads,
+                        t_max, scale, out, workspace, workspace_bytes, stream, check_only)) !=
+        FA_TQ_OK)
+      return st;
   }
-  fatq::attn_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
-  return launched(fatq::launch_attn(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
-                  "fa_tq_attn_decode");
+  return ok();
 }
 
 }  // extern "C"

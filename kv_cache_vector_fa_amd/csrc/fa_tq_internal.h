@@ -36,7 +36,8 @@ struct EncodeLaunch {
   const void* x;
   int64_t sb, sh, st;   // element strides
   int32_t batch, heads, tokens, nblk, t_max;
-  const int32_t* t0;
+  const int32_t* t0;     // first cache position per sequence, or null (0)
+  int32_t ring;          // positions map to slots modulo t_max (append into a ring)
   uint8_t* codes;
   uint16_t* norms;
   int32_t x_is_bf16;
@@ -55,7 +56,9 @@ struct AttnLaunch {
   const uint16_t* k_norms;
   const uint8_t* v_codes;
   const uint16_t* v_norms;
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;   // tokens per sequence, or (when pos is set)
+  const int32_t* pos;        //   min(pos[b] + n_new, t_max)
+  int32_t n_new;
   int32_t batch, hq, hkv, t_max;
   float scale;
   float* out;

@@ -22,6 +22,12 @@ Other modes:
                           plain copy whose counters calibrate FETCH_SIZE/WRITE_SIZE);
   --summarize-rocprof DIR print per-kernel means of a rocprofv3 CSV directory
                           (kernel_stats or counter_collection) and exit.
+
+After the timed steps (outside them), ``append_decode`` reports the decode-loop call
+fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
+slot), then attention over all T_max slots.  Eight such calls with distinct
+positions are captured in one HIP graph and replayed, so the figure is GPU time per
+call without host launch gaps.
 """
 
 from __future__ import annotations
@@ -59,6 +65,7 @@ def parse():
     p.add_argument("--workload", default="llama_layer")
     p.add_argument("--copies", type=int, default=4, help="input/cache copies rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-append", action="store_true", help="skip the append_decode figure")
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--summarize-rocprof", metavar="DIR")
     return p.parse_args()
@@ -123,6 +130,50 @@ def traffic_for(kernel: str):
     if kernel not in vals or src is None or hashes.get(src) != source_hash(src):
         return None
     return vals[kernel]
+
+
+def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -> dict:
+    """GPU time per fa_tq_attn_append call (one token per sequence, full cache),
+    from replays of a HIP graph holding eight calls at distinct positions."""
+    import torch
+    B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim
+    P = 8
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    new = [(torch.randn((B, Hkv, 1, d), generator=g).to(torch.bfloat16).cuda(),
+            torch.randn((B, Hkv, 1, d), generator=g).to(torch.bfloat16).cuda()) for _ in range(P)]
+    pos = [torch.full((B,), T - 1 + i, dtype=torch.int32, device="cuda") for i in range(P)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls = [fa.attn_append_call(cbk, cbv, seed, q, new[i][0], new[i][1], pos[i], *cache,
+                                     scale, out, ws) for i in range(P)]
+        for c in calls:     # eager warm-up on the capture stream
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls = [fa.attn_append_call(cbk, cbv, seed, q, new[i][0], new[i][1], pos[i], *cache,
+                                     scale, out, ws) for i in range(P)]
+        for c in calls:
+            c()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (replays * P)
+    kb, vb = fa.code_bytes(w.k_bits), fa.code_bytes(w.v_bits)
+    nbytes = (B * Hkv * 256 * 2 + B * Hkv * (kb + vb + 4)
+              + attn_bytes(np.full(B, T), Hkv, Hq, w.k_bits, w.v_bits))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 3), "new_tokens_per_sequence": 1, "attended_slots": T,
+            "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph of 8 calls"}
 
 
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
@@ -283,6 +334,8 @@ def main():
         "kernels": kern,
         "roofline": roof,
     }
+    if not args.no_append:
+        rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

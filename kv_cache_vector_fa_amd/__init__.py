@@ -244,33 +244,14 @@ def attn_append(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos,
     """Append k_new/v_new [B, Hkv, n_new, d] at positions pos [B] (slot = position mod
     T_max) into the packed caches, then decode attention for q [B, Hq, d]."""
     import torch
-    lib = load()
     B, Hq, d = q.shape
-    _, Hkv, n_new, _ = k_new.shape
-    t_max = k_codes.shape[2]
-    if k_new.dtype != v_new.dtype or k_new.stride(3) != 1 or v_new.stride(3) != 1:
-        raise ValueError("k_new and v_new need one dtype and channel stride 1")
-    if tuple(v_new.shape) != tuple(k_new.shape) or k_new.shape[0] != B or k_new.shape[3] != d:
-        raise ValueError(f"k_new {tuple(k_new.shape)}, v_new {tuple(v_new.shape)} for q "
-                         f"{tuple(q.shape)}")
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
-    _expect(pos, (B,), torch.int32, "pos")
-    _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
-    _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
+    Hkv, t_max = k_new.shape[1], k_codes.shape[2]
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    _expect(out, (B, Hq, d), torch.float32, "out")
     if workspace is None:
         workspace = attn_workspace(B, Hq, Hkv, t_max, d, q.device)
-    kl = Layout(k_new.stride(0), k_new.stride(1), k_new.stride(2))
-    vl = Layout(v_new.stride(0), v_new.stride(1), v_new.stride(2))
-    _check(lib.fa_tq_attn_append(ctypes.byref(cb_k), ctypes.byref(cb_v), seed, d, _ptr(q),
-                                 _dtype_code(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
-                                 kl, vl, n_new, _ptr(pos), _ptr(k_codes), _ptr(k_norms),
-                                 _ptr(v_codes), _ptr(v_norms), B, Hq, Hkv, t_max, float(scale),
-                                 _ptr(out), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)))
+    attn_append_call(cb_k, cb_v, seed, q, k_new, v_new, pos, k_codes, k_norms, v_codes,
+                     v_norms, scale, out, workspace, stream)()
     return out
 
 
@@ -319,3 +300,40 @@ def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_no
         return keep
     return call
 
+
+
+def attn_append_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos, k_codes,
+                     k_norms, v_codes, v_norms, scale: float, out, workspace, stream=None):
+    """``attn_append`` with its arguments marshalled once (see ``encode_call``)."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    _, Hkv, n_new, _ = k_new.shape
+    t_max = k_codes.shape[2]
+    if k_new.dtype != v_new.dtype or k_new.stride(3) != 1 or v_new.stride(3) != 1:
+        raise ValueError("k_new and v_new need one dtype and channel stride 1")
+    if tuple(v_new.shape) != tuple(k_new.shape) or k_new.shape[0] != B or k_new.shape[3] != d:
+        raise ValueError(f"k_new {tuple(k_new.shape)}, v_new {tuple(v_new.shape)} for q "
+                         f"{tuple(q.shape)}")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
+    _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
+    _expect(out, (B, Hq, d), torch.float32, "out")
+    args = (ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_int32(d),
+            _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_new), _ptr(v_new),
+            ctypes.c_int(_dtype_code(k_new)),
+            Layout(k_new.stride(0), k_new.stride(1), k_new.stride(2)),
+            Layout(v_new.stride(0), v_new.stride(1), v_new.stride(2)), ctypes.c_int32(n_new),
+            _ptr(pos), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+            ctypes.c_int32(B), ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max),
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
+    fn = lib.fa_tq_attn_append
+    keep = (cb_k, cb_v, q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, out, workspace)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call

@@ -194,3 +194,48 @@ def test_append_llama_layer_full(gpu_lib):
         assert np.array_equal(dev[3][:, :, slot].cpu().numpy().view(np.float16), vn[:, :, slot])
         say(f"append llama pos {pos} (slot {slot}): max abs err {err:.3e}")
         assert err <= ATTN_MAX_ABS
+
+
+def test_append_graph_replay_matches_eager(gpu_lib):
+    """A captured append call, replayed with new positions, tokens and queries written
+    into its input buffers between replays, matches the same calls made eagerly on a
+    twin cache (every replay compared: output, codes and norms)."""
+    torch = _torch()
+    fa = gpu_lib
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, T = 2, 8, 2, 64
+    kp, kn = _history(B, Hkv, T, 4, rng)
+    vp, vn = _history(B, Hkv, T, 2, rng)
+    graph_cache, eager_cache = _device(fa, kp, kn, vp, vn), _device(fa, kp, kn, vp, vn)
+    ck, cv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    q = torch.zeros((B, Hq, 128), device="cuda")
+    kx = torch.zeros((B, Hkv, 1, 128), device="cuda")
+    vx = torch.zeros((B, Hkv, 1, 128), device="cuda")
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = torch.zeros((B, Hq, 128), device="cuda")
+    ws = fa.attn_workspace(B, Hq, Hkv, T)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.attn_append_call(ck, cv, SEED, q, kx, vx, pos, *eager_cache, 0.09, out, ws)()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager_cache[0].copy_(graph_cache[0]), eager_cache[1].copy_(graph_cache[1])
+    eager_cache[2].copy_(graph_cache[2]), eager_cache[3].copy_(graph_cache[3])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.attn_append_call(ck, cv, SEED, q, kx, vx, pos, *graph_cache, 0.09, out, ws)()
+    for step, p in enumerate([[3, 70], [4, 71], [63, 127], [64, 200]]):
+        qn = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32)).cuda()
+        kn_ = torch.from_numpy(rng.standard_normal((B, Hkv, 1, 128)).astype(np.float32)).cuda()
+        vn_ = torch.from_numpy(rng.standard_normal((B, Hkv, 1, 128)).astype(np.float32)).cuda()
+        pn = torch.tensor(p, dtype=torch.int32, device="cuda")
+        ref = fa.attn_append(ck, cv, SEED, qn, kn_, vn_, pn, *eager_cache, 0.09)
+        torch.cuda.synchronize()
+        q.copy_(qn), kx.copy_(kn_), vx.copy_(vn_), pos.copy_(pn)
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"graph replay {step} pos {p}")
+        assert torch.equal(out, ref), f"replay {step}: output differs from the eager call"
+        for g, e in zip(graph_cache, eager_cache):
+            assert torch.equal(g, e), f"replay {step}: cache differs from the eager call"

@@ -154,7 +154,7 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
  *   split of the sequence); its contents on entry do not matter.  Calls that run
  *   concurrently must not share a workspace; calls in order on one stream may.
  * This build supports head_dim == 128, key/value bits in {2, 3, 4} and
- * n_q_heads / n_kv_heads <= 16.
+ * n_q_heads / n_kv_heads <= 16, and t_max < 33554432 (one cache row below 2 GiB).
  */
 fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
                                uint64_t seed, int32_t head_dim,

@@ -199,7 +199,8 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
 
 
 def attn_workspace(batch, n_q_heads, n_kv_heads, t_max, head_dim=QK, device="cuda"):
-    """A workspace for ``attn_decode`` (reusable by later calls in order on one stream)."""
+    """A workspace for ``attn_decode`` / ``attn_append`` (reusable by later calls in
+    order on one stream)."""
     import torch
     need = attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim)
     return torch.empty(max(need, 16), dtype=torch.uint8, device=device)

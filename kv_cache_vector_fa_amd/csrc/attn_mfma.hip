@@ -21,13 +21,18 @@
 //    G..2G-1 = lo(p'); the two output rows of a head are added at the end.
 // Every fp16 product is exact in the fp32 accumulator.
 //
-// Dequantization is a table look-up in LDS returning a ready MFMA operand (8 bytes):
-//  * keys: byte of two 4-bit codes -> entry (3- and 2-bit keys are first widened
-//    to 4-bit fields in registers);
-//  * values: the codes of one element in two tokens -> entry (2-bit: 16 entries;
-//    3/4-bit: 256 entries).
-// Tables with 256 entries are replicated 16 times and lane L reads copy L % 16, so
-// the 16 lanes an LDS cycle serves hit 16 different bank pairs.
+// Dequantization is a table look-up in LDS returning a ready MFMA operand.  One
+// 64 KB table has a 256-byte row per index byte r:
+//  * bytes [0, 128): key entry r (two 4-bit key codes: low nibble first element),
+//    8 bytes replicated 16 times;
+//  * bytes [128, 256): value entry r.  2-bit values: r holds the codes of one
+//    element in the four tokens of a lane's operand, and the 16-byte entry is that
+//    whole operand, replicated 8 times; 3/4-bit values: r holds the codes of one
+//    element in two tokens (8 bytes, 16 replicas).  When keys and values share a codebook the value
+//    look-ups use the key half.
+// A look-up address is one v_perm: (index byte << 8) | replica offset of the lane.
+// Lane L reads replica L % 16 (8-byte entries) or L % 8 (16-byte entries), so the
+// lanes an LDS cycle serves hit distinct banks.
 //
 // Token order inside a 16-token tile is the identity: score row r = 4 qq + j is
 // token r, which is the token pair (4qq + j, j = 0..3) lane group qq needs for its
@@ -37,8 +42,9 @@
 // tokens [split*chunk, min(len, (split+1)*chunk)) and wave w takes 32-token super
 // tiles w, w+4, ... with the next super tile's codes loaded while the current one
 // is processed.  Waves merge in LDS and each workgroup writes one partial
-// (m, l, o') per head to the workspace; a second kernel merges the splits,
-// divides by l and applies R^T = D H / sqrt(128).  Scores are kept in base 2.
+// (m, l, o') per head to the workspace; a second kernel merges the splits by
+// log-sum-exp, divides by l and applies R^T = D H / sqrt(128).  Scores are in
+// base 2.
 //
 // MFMA 16x16x32 f16 operand layout (wave64): A[i][k]: lane i%16 + 16*(k/8), slot
 // k%8; B[k][j]: lane j + 16*(k/8), slot k%8; D[i][j]: lane j + 16*(i/4), slot i%4.
@@ -51,19 +57,25 @@ namespace fatq {
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kST = 32;          // tokens per super tile (2 MFMA tiles)
 constexpr int kMaxG = 8;         // query heads per KV head on this path
-constexpr int kRep = 16;         // replicas of the 256-entry tables
+constexpr int kRow = 256;        // table bytes per index byte
+constexpr int kMaxSplit = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kCScale = 4.0f;  // centroid pre-scale (exact)
+// Raw buffer resources: an access at or beyond the range returns zeros, so loads
+// past the sequence need no clamp and lanes without work use offset kOOB.
+constexpr int32_t kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOOB = 0x80000000u;   // every range is below 2^31 (host check)
 
 #ifndef FATQ_ATTN_WANT_WG
-#define FATQ_ATTN_WANT_WG 768
+#define FATQ_ATTN_WANT_WG 512
 #endif
 #ifndef FATQ_ATTN_MIN_CHUNK
 #define FATQ_ATTN_MIN_CHUNK 512
@@ -72,8 +84,13 @@ constexpr float kCScale = 4.0f;  // centroid pre-scale (exact)
 template <int B>
 constexpr int cbytes() { return B == 2 ? 32 : B == 3 ? 48 : 64; }
 
-__device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 x, _Float16 y) {
@@ -81,11 +98,21 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 x, _Float16 y) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ h4 h4_of(uint2 u) { return __builtin_bit_cast(h4, u); }
-
 __device__ __forceinline__ void split_h(float x, _Float16& hi, _Float16& lo) {
   hi = static_cast<_Float16>(x);
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ h8 h8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
+}
+
+// Barrier that orders LDS only: the workgroup's outstanding global loads stay in
+// flight (__syncthreads would also wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Spread 8 two-bit fields (bits 2i..2i+1) to nibbles (bits 4i..4i+1).
@@ -104,101 +131,120 @@ __device__ __forceinline__ uint32_t spread1(uint32_t x) {
   return x;
 }
 
-// Key codes of elements 32 qq .. 32 qq + 31 of a token as 16 bytes of two 4-bit
-// fields (byte i: element 32 qq + 2i in the low nibble, 32 qq + 2i + 1 high).
-template <int KB>
-__device__ __forceinline__ uint4 load_k32(const uint8_t* row, int qq) {
-  if constexpr (KB == 4) {
-    return *reinterpret_cast<const uint4*>(row + 16 * qq);
-  } else if constexpr (KB == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(row + 8 * qq);
-    return make_uint4(spread2(w.x & 0xFFFFu), spread2(w.x >> 16), spread2(w.y & 0xFFFFu),
-                      spread2(w.y >> 16));
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(row + 8 * qq);
-    const uint32_t h = *reinterpret_cast<const uint32_t*>(row + 32 + 4 * qq);
-    return make_uint4(spread2(w.x & 0xFFFFu) | (spread1(h & 0xFFu) << 2),
-                      spread2(w.x >> 16) | (spread1((h >> 8) & 0xFFu) << 2),
-                      spread2(w.y & 0xFFFFu) | (spread1((h >> 16) & 0xFFu) << 2),
-                      spread2(w.y >> 16) | (spread1(h >> 24) << 2));
-  }
-}
+// Raw code words of one super tile as loaded (widened to 4-bit fields at use).
+//  k[t4]: the key codes of elements 32 qq .. 32 qq + 31 of token 16 t4 + n;
+//  v[t4][j]: the value codes of elements 8 n .. 8 n + 7 of token 16 t4 + 4 qq + j;
+//  nrm: lanes < 32 the key norm, lanes >= 32 the value norm of token lane % 32.
+template <int KB, int VB>
+struct Codes {
+  uint32_t k[2][KB == 4 ? 4 : 3];
+  uint32_t v[2][4][VB == 3 ? 2 : 1];
+  uint32_t nrm;
+};
 
-// Value codes of elements 8n .. 8n+7 of a token: 16 bits of 2-bit fields (VB = 2)
-// or a word of 4-bit fields (VB = 3, 4).
-template <int VB>
-__device__ __forceinline__ uint32_t load_v8(const uint8_t* row, int n) {
-  if constexpr (VB == 4) {
-    return *reinterpret_cast<const uint32_t*>(row + 4 * n);
-  } else if constexpr (VB == 2) {
-    return *reinterpret_cast<const uint16_t*>(row + 2 * n);
-  } else {
-    const uint32_t lo = *reinterpret_cast<const uint16_t*>(row + 2 * n);
-    const uint32_t hi = row[32 + n];
-    return spread2(lo) | (spread1(hi) << 2);
-  }
-}
+struct Rows {
+  Rsrc kc, vc, kn, vn;
+};
 
-// Fill a 256-entry operand table for a byte index of two 4-bit codes (low nibble:
-// first element/token, high nibble: second), replicated kRep times, by the 192
-// threads t in [0, 192) of waves 1..3.
-__device__ __forceinline__ void fill_table256(uint2* tab, const KTable& t, int t3) {
-  for (int i = t3; i < 256; i += 192) {
-    const int r = i & (kRep - 1);
-    const int lo4 = i >> 4;
-    _Float16 h0, l0;
-    split_h(kCScale * t.c[lo4], h0, l0);
+template <int KB, int VB>
+__device__ __forceinline__ void issue_loads(const Rows& r, Codes<KB, VB>& c, int s0, bool live,
+                                            int lane) {
+  constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
+  const int n = lane & 15, qq = lane >> 4;
+  const uint32_t tk = static_cast<uint32_t>(s0 + n);
+  const uint32_t tv = static_cast<uint32_t>(s0 + 4 * qq);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      _Float16 h1, l1;
-      split_h(kCScale * t.c[k], h1, l1);
-      const int byte = lo4 | (k << 4);
-      tab[byte * kRep + r] = make_uint2(pack_h2(h0, h1), pack_h2(l0, l1));
+  for (int t4 = 0; t4 < 2; ++t4) {
+    if constexpr (KB == 4) {
+      const uint32_t o = live ? tk * KCB + 16 * qq : kOOB;
+      const uint4 w = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kc, o + 16 * KCB * t4, 0, 0));
+      c.k[t4][0] = w.x; c.k[t4][1] = w.y; c.k[t4][2] = w.z; c.k[t4][3] = w.w;
+    } else {
+      const uint32_t o = live ? tk * KCB + 8 * qq : kOOB;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(r.kc, o + 16 * KCB * t4, 0, 0);
+      c.k[t4][0] = w[0];
+      c.k[t4][1] = w[1];
+      if constexpr (KB == 3) {
+        const uint32_t oh = live ? tk * KCB + 32 + 4 * qq : kOOB;
+        c.k[t4][2] = __builtin_amdgcn_raw_buffer_load_b32(r.kc, oh + 16 * KCB * t4, 0, 0);
+      } else {
+        c.k[t4][2] = 0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d = (16 * t4 + j) * VCB;
+      if constexpr (VB == 4) {
+        const uint32_t o = live ? tv * VCB + 4 * n : kOOB;
+        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o + d, 0, 0);
+      } else {
+        const uint32_t o = live ? tv * VCB + 2 * n : kOOB;
+        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b16(r.vc, o + d, 0, 0);
+        if constexpr (VB == 3) {
+          const uint32_t oh = live ? tv * VCB + 32 + n : kOOB;
+          c.v[t4][j][1] = __builtin_amdgcn_raw_buffer_load_b8(r.vc, oh + d, 0, 0);
+        }
+      }
     }
   }
+  const uint32_t on = static_cast<uint32_t>(s0 + (lane & 31)) * 2;
+  const uint32_t ok = live && lane < 32 ? on : kOOB;
+  const uint32_t ov = live && lane >= 32 ? on : kOOB;
+  c.nrm = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r.kn, ok, 0, 0)) |
+          static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r.vn, ov, 0, 0));
 }
 
-// In-register Walsh-Hadamard transform (unnormalized) of a 128-block held by a quad
-// of lanes: lane q holds elements 8 (q + 4k) + i in v[k][i].  Strides 1, 2, 4 are
-// inside a chunk, 8 and 16 across the quad's lanes, 32 and 64 across chunks.
-__device__ __forceinline__ void fwht_quad(float (&v)[4][8], int q) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int L = 1; L < 8; L <<= 1)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((i & L) == 0) {
-          const float x = v[k][i], y = v[k][i + L];
-          v[k][i] = x + y;
-          v[k][i + L] = x - y;
-        }
-#pragma unroll
-  for (int msk = 1; msk <= 2; msk <<= 1) {
-    const bool upper = (q & msk) != 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = __shfl_xor(v[k][i], msk, 64);
-        v[k][i] = upper ? p - v[k][i] : v[k][i] + p;
-      }
+// The key words of one tile as four words of 4-bit fields (byte i of the 16: elements
+// 32 qq + 2i (low nibble) and 32 qq + 2i + 1).
+template <int KB>
+__device__ __forceinline__ void key_fields(const uint32_t (&w)[KB == 4 ? 4 : 3], uint32_t (&f)[4]) {
+  if constexpr (KB == 4) {
+    f[0] = w[0]; f[1] = w[1]; f[2] = w[2]; f[3] = w[3];
+  } else if constexpr (KB == 2) {
+    f[0] = spread2(w[0] & 0xFFFFu); f[1] = spread2(w[0] >> 16);
+    f[2] = spread2(w[1] & 0xFFFFu); f[3] = spread2(w[1] >> 16);
+  } else {
+    const uint32_t h = w[2];
+    f[0] = spread2(w[0] & 0xFFFFu) | (spread1(h & 0xFFu) << 2);
+    f[1] = spread2(w[0] >> 16) | (spread1((h >> 8) & 0xFFu) << 2);
+    f[2] = spread2(w[1] & 0xFFFFu) | (spread1((h >> 16) & 0xFFu) << 2);
+    f[3] = spread2(w[1] >> 16) | (spread1(h >> 24) << 2);
   }
-#pragma unroll
-  for (int L = 1; L < 4; L <<= 1)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if ((k & L) == 0)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x = v[k][i], y = v[k + L][i];
-          v[k][i] = x + y;
-          v[k + L][i] = x - y;
-        }
 }
 
-// Shift a value down (lane i reads lane i + d) or up (lane i reads lane i - d)
-// inside rows of 16 lanes; a compile-time distance becomes one DPP move.
+// Value word of elements 8 n .. 8 n + 7 as 4-bit fields (3/4-bit values).
+template <int VB>
+__device__ __forceinline__ uint32_t value_fields(const uint32_t (&w)[VB == 3 ? 2 : 1]) {
+  if constexpr (VB == 4) return w[0];
+  else return spread2(w[0] & 0xFFFFu) | (spread1(w[1] & 0xFFu) << 2);
+}
+
+// Four 16-bit words of 2-bit value codes (tokens a, b, c, d; field i = element
+// 8n + i) -> index bytes: byte k of e = element 2k, of o = element 2k + 1, each
+// (code of a) | (b) << 2 | (c) << 4 | (d) << 6.
+__device__ __forceinline__ void quad_index2(uint32_t wa, uint32_t wb, uint32_t wc, uint32_t wd,
+                                            uint32_t& e, uint32_t& o) {
+  auto pair = [](uint32_t x, uint32_t y) {
+    // bytes [x.b0, y.b0, x.b1, y.b1], then nibble k = (x nibble k) | (y nibble k) << 4,
+    // then fields reordered within each byte to (x_2k, y_2k, x_2k+1, y_2k+1)
+    uint32_t z = __builtin_amdgcn_perm(y, x, 0x05010400u);
+    uint32_t t = ((z >> 4) ^ z) & 0x00F000F0u;
+    z ^= t ^ (t << 4);
+    t = ((z >> 2) ^ z) & 0x0C0C0C0Cu;
+    return z ^ t ^ (t << 2);
+  };
+  const uint32_t ab = pair(wa, wb), cd = pair(wc, wd);
+  e = (ab & 0x0F0F0F0Fu) | ((cd << 4) & 0xF0F0F0F0u);
+  o = ((ab >> 4) & 0x0F0F0F0Fu) | (cd & 0xF0F0F0F0u);
+}
+
+// Table address of index byte k of word z: (byte << 8) | byte `rsel` of lane word R.
+template <int K, int RSEL>
+__device__ __forceinline__ uint32_t taddr(uint32_t z, uint32_t R) {
+  return __builtin_amdgcn_perm(z, R, 0x0C0C0000u | ((4u + K) << 8) | RSEL);
+}
+
 template <int D>
 __device__ __forceinline__ float row_down(float x, int d) {
   if constexpr (D > 0)
@@ -216,202 +262,196 @@ __device__ __forceinline__ uint32_t row_up(uint32_t x, int d) {
     return __shfl_up(x, d, 16);
 }
 
-// 8 two-bit fields of each of two 16-bit words wa, wb interleaved to nibbles:
-// nibble m = (wa field m) | (wb field m) << 2.
-__device__ __forceinline__ uint32_t interleave2(uint32_t wa, uint32_t wb) {
-  uint32_t x = __builtin_amdgcn_perm(wb, wa, 0x05010400u);   // [wa.b0, wb.b0, wa.b1, wb.b1]
-  uint32_t t = ((x >> 4) ^ x) & 0x00F000F0u;
-  x ^= t ^ (t << 4);
-  t = ((x >> 2) ^ x) & 0x0C0C0C0Cu;
-  x ^= t ^ (t << 2);
-  return x;
+// Sign of element e of the first 128-block (SignWords quad layout).
+__device__ __forceinline__ bool sign_bit(const SignWords& sw, int e) {
+  const int c = e >> 3;
+  return (sw.w[0][c & 3] >> (8 * (c >> 2) + (e & 7))) & 1u;
 }
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// Inverse rotation of one head's merged output held as elements 2 lane, 2 lane + 1
+// (fp32, unnormalized Walsh-Hadamard, then signs and 1/sqrt(128)), stored to dst.
+__device__ __forceinline__ void rotate_out(float2 o, const SignWords& sw, int lane, float* dst) {
+  float u = o.x + o.y, v = o.x - o.y;
+#pragma unroll
+  for (int L = 1; L < 64; L <<= 1) {
+    const float pu = __shfl_xor(u, L, 64), pv = __shfl_xor(v, L, 64);
+    const bool up = (lane & L) != 0;
+    u = up ? pu - u : u + pu;
+    v = up ? pv - v : v + pv;
+  }
+  const float r0 = u * kInvSqrtQK, r1 = v * kInvSqrtQK;
+  reinterpret_cast<float2*>(dst)[lane] =
+      make_float2(sign_bit(sw, 2 * lane) ? -r0 : r0, sign_bit(sw, 2 * lane + 1) ? -r1 : r1);
 }
 
-__device__ __forceinline__ h8 h8_of(uint2 lo, uint2 hi) {
-  uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  return __builtin_bit_cast(h8, u);
-}
-
-// VSH: key and value codebooks are identical, so one operand table serves both.
+// VSH: key and value codebooks are identical, so the key entries serve both.
 // GT: the group size G as a compile-time constant (1, 2, 4, 8), or 0 (runtime).
 template <int KB, int VB, bool VSH, int GT>
 __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KTable tk,
                                                                 KTable tv, SignWords sw) {
   constexpr bool V2 = VB == 2;
-  constexpr int KCB = cbytes<KB>(), VCB = cbytes<VB>();
-  constexpr int VENT = VSH ? 1 : (V2 ? 16 : 256 * kRep);
-  __shared__ uint2 ktab[256 * kRep];            // 32 KB; reused for the wave merge
-  __shared__ uint2 vtab_own[VENT];
-  __shared__ __attribute__((aligned(16))) float qr[kMaxG][QK];
-  __shared__ float qsc;
+  __shared__ __attribute__((aligned(16))) uint8_t tab[256 * kRow];   // 64 KB
+  __shared__ __attribute__((aligned(16))) uint16_t qhl[17][QK];      // hi, lo, zero rows
   __shared__ __attribute__((aligned(16))) float nrm[kWaves][3][kST];
+  __shared__ uint32_t sp[2][16];
+  __shared__ float qmx[kMaxG];
   __shared__ float comb_ml[kWaves][kMaxG][2];
-  static_assert(sizeof(ktab) >= sizeof(float) * kWaves * 2 * kMaxG * QK, "merge buffer");
-  static_assert(!(VSH && V2), "2-bit values use their own 16-entry table");
-  uint2* vtab = VSH ? ktab : vtab_own;
+  static_assert(sizeof(tab) >= sizeof(float) * kWaves * 2 * kMaxG * QK, "merge buffer");
+  static_assert(!(VSH && V2), "2-bit values have their own entries");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qq = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = GT > 0 ? GT : a.hq / a.hkv;
+  constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
 
   // ---- the sequence range, then the first super tile's loads (in flight during setup)
   const int64_t len64 = a.pos ? static_cast<int64_t>(a.pos[b]) + a.n_new : a.seq_lens[b];
   const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
   const int c0 = split * a.chunk;
   const int c1 = min(len, c0 + a.chunk);
-  const int last = c1 - 1;
   const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g) * a.t_max;
-  const uint8_t* kc = a.k_codes + kvb * KCB;
-  const uint8_t* vc = a.v_codes + kvb * VCB;
-  const uint16_t* kn = a.k_norms + kvb;
-  const uint16_t* vn = a.v_norms + kvb;
+  const uint32_t ulen = static_cast<uint32_t>(len);
+  Rows rows;
+  rows.kc = make_rsrc(a.k_codes + kvb * KCB, ulen * KCB);
+  rows.vc = make_rsrc(a.v_codes + kvb * VCB, ulen * VCB);
+  rows.kn = make_rsrc(a.k_norms + kvb, ulen * 2);
+  rows.vn = make_rsrc(a.v_norms + kvb, ulen * 2);
   int st = c0 + wave * kST;
-  uint4 kw[2];
-  uint32_t vw[2][4];
-  uint32_t nh = 0;
-  auto issue_loads = [&](int s0) {
-#pragma unroll
-    for (int t4 = 0; t4 < 2; ++t4) {
-      const uint32_t ta = static_cast<uint32_t>(min(s0 + 16 * t4 + n, last));
-      kw[t4] = load_k32<KB>(kc + ta * KCB, qq);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t tv_ = static_cast<uint32_t>(min(s0 + 16 * t4 + 4 * qq + j, last));
-        vw[t4][j] = load_v8<VB>(vc + tv_ * VCB, n);
-      }
-    }
-    const int tcl = min(s0 + (lane & 31), last);
-    nh = lane < 32 ? kn[tcl] : vn[tcl];
-  };
-  if (st < c1) issue_loads(st);
+  Codes<KB, VB> buf0, buf1;
+  issue_loads<KB, VB>(rows, buf0, st, st < c1, lane);
 
-  // ---- wave 0: q' = H (s * q) / sqrt(128) for the G heads in registers (quad h =
-  // lanes 4h..4h+3 holds head h, lane q of the quad elements 8 (q + 4k) + i), scaled
-  // by a power of two so that |q'| < 1, into LDS.  The other waves fill the tables.
-  if (wave == 0) {
-    float qx[4][8];
-    const int hq_ = lane >> 2, qd = lane & 3;
-    const bool act = hq_ < G;
-    const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + (act ? hq_ : 0)) * QK;
+  // ---- query loads: wave w rotates heads w and w + 4; lane holds elements lane and
+  // lane + 64 of each
+  float qx[2][2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e0 = 8 * (qd + 4 * k);
-      if (a.q_is_bf16) {
-        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + e0);
-        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          qx[k][2 * m] = __uint_as_float(d[m] << 16);
-          qx[k][2 * m + 1] = __uint_as_float(d[m] & 0xffff0000u);
-        }
-      } else {
-        const float* qf = static_cast<const float*>(a.q) + qo + e0;
-        const float4 w0 = *reinterpret_cast<const float4*>(qf);
-        const float4 w1 = *reinterpret_cast<const float4*>(qf + 4);
-        qx[k][0] = w0.x; qx[k][1] = w0.y; qx[k][2] = w0.z; qx[k][3] = w0.w;
-        qx[k][4] = w1.x; qx[k][5] = w1.y; qx[k][6] = w1.z; qx[k][7] = w1.w;
-      }
-      const uint32_t sb = sw.w[0][qd];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = ((sb >> (8 * k + i)) & 1u) ? -qx[k][i] : qx[k][i];
-        qx[k][i] = act ? v : 0.0f;
-      }
-    }
-    fwht_quad(qx, qd);
-    float qmax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qmax = fmaxf(qmax, fabsf(qx[k][i]));
-#pragma unroll
-    for (int s2 = 32; s2 >= 1; s2 >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, s2, 64));
-    int qex = 0;
-    frexpf(qmax * kInvSqrtQK, &qex);
-    const float qs = qmax > 0.0f ? ldexpf(1.0f, qex) : 1.0f;
-    const float inv = kInvSqrtQK / qs;
-    if (act) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float* dst = &qr[hq_][8 * (qd + 4 * k)];
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(qx[k][0] * inv, qx[k][1] * inv, qx[k][2] * inv, qx[k][3] * inv);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(qx[k][4] * inv, qx[k][5] * inv, qx[k][6] * inv, qx[k][7] * inv);
-      }
-    }
-    if (lane == 0) qsc = qs;
-  } else {
-    // ---- operand tables (shared by the four waves), filled by waves 1..3
-    const int t3 = tid - 64;
-    fill_table256(ktab, tk, t3);
-    if constexpr (!VSH) {
-      if constexpr (V2) {
-        if (t3 < 16) {
-          _Float16 h0, l0, h1, l1;
-          split_h(kCScale * tv.c[t3 & 3], h0, l0);
-          split_h(kCScale * tv.c[t3 >> 2], h1, l1);
-          vtab[t3] = make_uint2(pack_h2(h0, h1), pack_h2(l0, l1));
-        }
-      } else {
-        fill_table256(vtab, tv, t3);
-      }
+  for (int hs = 0; hs < 2; ++hs) {
+    const int h = wave + kWaves * hs;
+    const int hc = h < G ? h : 0;
+    const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + hc) * QK;
+    if (a.q_is_bf16) {
+      const uint16_t* qb = static_cast<const uint16_t*>(a.q) + qo;
+      qx[hs][0] = __uint_as_float(static_cast<uint32_t>(qb[lane]) << 16);
+      qx[hs][1] = __uint_as_float(static_cast<uint32_t>(qb[lane + 64]) << 16);
+    } else {
+      const float* qf = static_cast<const float*>(a.q) + qo;
+      qx[hs][0] = qf[lane];
+      qx[hs][1] = qf[lane + 64];
     }
   }
-  __syncthreads();   // q' and the operand tables are complete
-  const float qscale = qsc;
 
-  // ---- B operands of the score product: k-step m covers elements 32qq + 4m .. +3
+  // ---- centroid splits, then the operand table (thread r fills row r)
+  if (tid < 32) {
+    const int i = tid & 15;
+    _Float16 hi, lo;
+    split_h(kCScale * (tid < 16 ? tk.c[i] : tv.c[i]), hi, lo);
+    sp[tid >> 4][i] = pack_h2(hi, lo);
+  }
+  lds_barrier();
+  {
+    const int r = tid;
+    uint8_t* row = tab + r * kRow;
+    const uint32_t a0 = sp[0][r & 15], a1 = sp[0][r >> 4];
+    const uint32_t kh = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // hi(c_lo4), hi(c_hi4)
+    const uint32_t kl = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // lo(c_lo4), lo(c_hi4)
+    const uint4 ke = make_uint4(kh, kl, kh, kl);
+    // all 8 slots of a row hold the same value; rotating the slot a step writes by
+    // the row index spreads the lanes of one store over all banks
+#pragma unroll
+    for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row)[(k + r) & 7] = ke;
+    if constexpr (V2) {
+      const uint32_t va = sp[1][r & 3], vb = sp[1][(r >> 2) & 3];
+      const uint32_t vc = sp[1][(r >> 4) & 3], vd = sp[1][r >> 6];
+      const uint4 ve = make_uint4(__builtin_amdgcn_perm(vb, va, 0x05040100u),
+                                  __builtin_amdgcn_perm(vb, va, 0x07060302u),
+                                  __builtin_amdgcn_perm(vd, vc, 0x05040100u),
+                                  __builtin_amdgcn_perm(vd, vc, 0x07060302u));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row + 128)[(k + r) & 7] = ve;
+    } else if constexpr (!VSH) {
+      const uint32_t v0 = sp[1][r & 15], v1 = sp[1][r >> 4];
+      const uint32_t vh = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
+      const uint32_t vl = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+      const uint4 ve = make_uint4(vh, vl, vh, vl);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row + 128)[(k + r) & 7] = ve;
+    }
+  }
+
+  // ---- q' = H (s * q): stride 64 in-lane, strides 32 .. 1 across lanes; the largest
+  // |q'| of each head to LDS
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    float x0 = sign_bit(sw, lane) ? -qx[hs][0] : qx[hs][0];
+    float x1 = sign_bit(sw, lane + 64) ? -qx[hs][1] : qx[hs][1];
+    float u = x0 + x1, v = x0 - x1;
+#pragma unroll
+    for (int L = 32; L >= 1; L >>= 1) {
+      const float pu = __shfl_xor(u, L, 64), pv = __shfl_xor(v, L, 64);
+      const bool up = (lane & L) != 0;
+      u = up ? pu - u : u + pu;
+      v = up ? pv - v : v + pv;
+    }
+    qx[hs][0] = u;
+    qx[hs][1] = v;
+    float mx = fmaxf(fabsf(u), fabsf(v));
+#pragma unroll
+    for (int s2 = 32; s2 >= 1; s2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s2, 64));
+    const int h = wave + kWaves * hs;
+    if (lane == 0 && h < G) qmx[h] = mx;
+  }
+  lds_barrier();   // tables and per-head maxima complete
+  float qmax = 0.0f;
+  for (int h = 0; h < G; ++h) qmax = fmaxf(qmax, qmx[h]);
+  int qex = 0;
+  frexpf(qmax * kInvSqrtQK, &qex);
+  const float qscale = qmax > 0.0f ? ldexpf(1.0f, qex) : 1.0f;
+  {
+    const float inv = kInvSqrtQK / qscale;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const int h = wave + kWaves * hs;
+      if (h < G) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          _Float16 hi, lo;
+          split_h(qx[hs][i] * inv, hi, lo);
+          qhl[h][lane + 64 * i] = __builtin_bit_cast(uint16_t, hi);
+          qhl[kMaxG + h][lane + 64 * i] = __builtin_bit_cast(uint16_t, lo);
+        }
+      }
+    }
+    if (tid < 64) reinterpret_cast<uint32_t*>(&qhl[2 * kMaxG][0])[tid] = 0u;
+  }
+  lds_barrier();   // q' halves complete
+
+  // ---- B operands of the score product: k-step m covers elements 32qq + 4m .. +3;
+  // column n < G: hi(q'_n), G <= n < 2G: lo(q'_{n-G}), else zero
   h8 bq[8];
   {
-    const bool used = n < 2 * G;
-    const int h = n < G ? n : (used ? n - G : 0);
+    const int qrow = n < G ? n : (n < 2 * G ? kMaxG + n - G : 2 * kMaxG);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float4 xv = *reinterpret_cast<const float4*>(&qr[h][32 * qq + 4 * m]);
-      const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-      _Float16 x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        _Float16 hi, lo;
-        split_h(xs[i], hi, lo);
-        x[i] = n < G ? hi : (used ? lo : _Float16(0));
-      }
-      bq[m] = h8{x[0], x[1], x[0], x[1], x[2], x[3], x[2], x[3]};
+      const uint2 d = *reinterpret_cast<const uint2*>(&qhl[qrow][32 * qq + 4 * m]);
+      bq[m] = h8_of(d.x, d.x, d.y, d.y);
     }
   }
   const float sc2 = a.scale * kLog2e * qscale / kCScale;
-  const uint32_t roff = (lane & (kRep - 1)) << 3;      // byte offset of this lane's replica
+  // byte 0: key replica offset, byte 1: value replica offset (+128) of this lane
+  const uint32_t R = ((lane & 15) << 3) |
+                     ((VSH ? ((lane & 15) << 3) : V2 ? 128 + ((lane & 7) << 4) : 128 + ((lane & 15) << 3)) << 8);
 
   float m_run = -INFINITY, l_run = 0.0f;
   f4 o[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (; st < c1; st += kWaves * kST) {
-    // take this super tile's data, start loading the next one
-    uint4 kcur[2];
-    uint32_t vcur[2][4];
-#pragma unroll
-    for (int t4 = 0; t4 < 2; ++t4) {
-      kcur[t4] = kw[t4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vcur[t4][j] = vw[t4][j];
-    }
-    const uint32_t ncur = nh;
-    if (st + kWaves * kST < c1) issue_loads(st + kWaves * kST);
+  auto process = [&](const Codes<KB, VB>& cur, int s0) {
     // per-token factors through LDS: key scale (0 when masked), key bias (-inf when
     // masked), value scale
     {
-      const int t = st + (lane & 31);
-      const float nf = __half2float(__ushort_as_half(static_cast<uint16_t>(ncur)));
+      const int t = s0 + (lane & 31);
+      const float nf = __half2float(__ushort_as_half(static_cast<uint16_t>(cur.nrm)));
       if (lane < 32) {
         nrm[wave][0][lane] = t < c1 ? nf * sc2 : 0.0f;
         nrm[wave][1][lane] = t < c1 ? 0.0f : -INFINITY;
@@ -424,24 +464,30 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     float sc[2][4];
 #pragma unroll
     for (int t4 = 0; t4 < 2; ++t4) {
+      uint32_t f[4];
+      key_fields<KB>(cur.k[t4], f);
       f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      const uint32_t w4[4] = {kcur[t4].x, kcur[t4].y, kcur[t4].z, kcur[t4].w};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const uint32_t w = w4[m >> 1] >> (16 * (m & 1));
-        const uint32_t a0 = ((m & 1) ? (w << 7) : (w << 7)) & 0x7F80u;
-        const uint32_t a1 = (w >> 1) & 0x7F80u;
-        const uint2 e0 = *reinterpret_cast<const uint2*>(
-            reinterpret_cast<const uint8_t*>(ktab) + (a0 | roff));
-        const uint2 e1 = *reinterpret_cast<const uint2*>(
-            reinterpret_cast<const uint8_t*>(ktab) + (a1 | roff));
-        acc = mfma32(h8_of(e0, e1), bq[m], acc);
+        const uint32_t w = f[m >> 1];
+        uint32_t a0, a1;
+        if (m & 1) {
+          a0 = taddr<2, 0>(w, R);
+          a1 = taddr<3, 0>(w, R);
+        } else {
+          a0 = taddr<0, 0>(w, R);
+          a1 = taddr<1, 0>(w, R);
+        }
+        const uint2 e0 = *reinterpret_cast<const uint2*>(tab + a0);
+        const uint2 e1 = *reinterpret_cast<const uint2*>(tab + a1);
+        acc = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc);
       }
-      const float4 f = *reinterpret_cast<const float4*>(&nrm[wave][0][16 * t4 + 4 * qq]);
-      const float4 z = *reinterpret_cast<const float4*>(&nrm[wave][1][16 * t4 + 4 * qq]);
-      const float fk[4] = {f.x, f.y, f.z, f.w}, zb[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[t4][j] = fmaf(acc[j] + row_down<GT>(acc[j], G), fk[j], zb[j]);
+      const float4 fk = *reinterpret_cast<const float4*>(&nrm[wave][0][16 * t4 + 4 * qq]);
+      const float4 zb = *reinterpret_cast<const float4*>(&nrm[wave][1][16 * t4 + 4 * qq]);
+      sc[t4][0] = fmaf(acc[0] + row_down<GT>(acc[0], G), fk.x, zb.x);
+      sc[t4][1] = fmaf(acc[1] + row_down<GT>(acc[1], G), fk.y, zb.y);
+      sc[t4][2] = fmaf(acc[2] + row_down<GT>(acc[2], G), fk.z, zb.z);
+      sc[t4][3] = fmaf(acc[3] + row_down<GT>(acc[3], G), fk.w, zb.w);
     }
     // ---- online softmax (lanes n < G carry head n; other columns are ignored)
     float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
@@ -476,51 +522,77 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     // 4qq..4qq+3; rows < G hi(p'), rows G..2G-1 lo(p') (moved up by G lanes)
 #pragma unroll
     for (int t4 = 0; t4 < 2; ++t4) {
-      const float4 f = *reinterpret_cast<const float4*>(&nrm[wave][2][16 * t4 + 4 * qq]);
-      const float pv[4] = {p[t4][0] * f.x, p[t4][1] * f.y, p[t4][2] * f.z, p[t4][3] * f.w};
-      _Float16 hv[4], lv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) split_h(pv[j], hv[j], lv[j]);
-      const uint32_t lab = row_up<GT>(pack_h2(lv[0], lv[1]), G);
-      const uint32_t lcd = row_up<GT>(pack_h2(lv[2], lv[3]), G);
-      const uint32_t pab = n < G ? pack_h2(hv[0], hv[1]) : (n < 2 * G ? lab : 0u);
-      const uint32_t pcd = n < G ? pack_h2(hv[2], hv[3]) : (n < 2 * G ? lcd : 0u);
-      const h8 ap = __builtin_bit_cast(h8, make_uint4(pab, pab, pcd, pcd));
+      const float4 fv = *reinterpret_cast<const float4*>(&nrm[wave][2][16 * t4 + 4 * qq]);
+      const float pa = p[t4][0] * fv.x, pb = p[t4][1] * fv.y;
+      const float pc = p[t4][2] * fv.z, pd = p[t4][3] * fv.w;
+      // hi = fp16 pair rounded toward zero, lo = the exact fp32 remainder in fp16
+      const auto hab = __builtin_amdgcn_cvt_pkrtz(pa, pb);
+      const auto hcd = __builtin_amdgcn_cvt_pkrtz(pc, pd);
+      const auto lab2 = __builtin_amdgcn_cvt_pkrtz(pa - static_cast<float>(hab[0]),
+                                                   pb - static_cast<float>(hab[1]));
+      const auto lcd2 = __builtin_amdgcn_cvt_pkrtz(pc - static_cast<float>(hcd[0]),
+                                                   pd - static_cast<float>(hcd[1]));
+      const uint32_t lab = row_up<GT>(__builtin_bit_cast(uint32_t, lab2), G);
+      const uint32_t lcd = row_up<GT>(__builtin_bit_cast(uint32_t, lcd2), G);
+      const uint32_t pab = n < G ? __builtin_bit_cast(uint32_t, hab) : (n < 2 * G ? lab : 0u);
+      const uint32_t pcd = n < G ? __builtin_bit_cast(uint32_t, hcd) : (n < 2 * G ? lcd : 0u);
+      const h8 ap = h8_of(pab, pab, pcd, pcd);
       if constexpr (V2) {
-        const uint32_t zab = interleave2(vcur[t4][0], vcur[t4][1]);
-        const uint32_t zcd = interleave2(vcur[t4][2], vcur[t4][3]);
+        uint32_t ze, zo;
+        quad_index2(cur.v[t4][0][0], cur.v[t4][1][0], cur.v[t4][2][0], cur.v[t4][3][0], ze, zo);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const uint32_t oab = (m == 0 ? (zab << 3) : (zab >> (4 * m - 3))) & 0x78u;
-          const uint32_t ocd = (m == 0 ? (zcd << 3) : (zcd >> (4 * m - 3))) & 0x78u;
-          const uint2 eab = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vtab) + oab);
-          const uint2 ecd = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vtab) + ocd);
-          o[m] = mfma32(ap, h8_of(eab, ecd), o[m]);
+          const uint32_t z = (m & 1) ? zo : ze;
+          uint32_t ad;
+          if ((m >> 1) == 0) ad = taddr<0, 1>(z, R);
+          else if ((m >> 1) == 1) ad = taddr<1, 1>(z, R);
+          else if ((m >> 1) == 2) ad = taddr<2, 1>(z, R);
+          else ad = taddr<3, 1>(z, R);
+          const uint4 ev = *reinterpret_cast<const uint4*>(tab + ad);
+          o[m] = mfma32(ap, h8_of(ev.x, ev.y, ev.z, ev.w), o[m]);
         }
       } else {
-        const uint32_t wa = vcur[t4][0], wb = vcur[t4][1], wc = vcur[t4][2], wd = vcur[t4][3];
+        const uint32_t wa = value_fields<VB>(cur.v[t4][0]), wb = value_fields<VB>(cur.v[t4][1]);
+        const uint32_t wc = value_fields<VB>(cur.v[t4][2]), wd = value_fields<VB>(cur.v[t4][3]);
+        // byte k of ze: element 2k (tokens a | b << 4); zo: element 2k + 1
         const uint32_t ze0 = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
         const uint32_t zo0 = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
         const uint32_t ze1 = (wc & 0x0F0F0F0Fu) | ((wd << 4) & 0xF0F0F0F0u);
         const uint32_t zo1 = ((wc >> 4) & 0x0F0F0F0Fu) | (wd & 0xF0F0F0F0u);
+        constexpr int RS = VSH ? 0 : 1;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const int k = m >> 1;
           const uint32_t z0 = (m & 1) ? zo0 : ze0, z1 = (m & 1) ? zo1 : ze1;
-          const uint32_t i0 = (k == 0 ? (z0 << 7) : (z0 >> (8 * k - 7))) & 0x7F80u;
-          const uint32_t i1 = (k == 0 ? (z1 << 7) : (z1 >> (8 * k - 7))) & 0x7F80u;
-          const uint2 eab = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vtab) + (i0 | roff));
-          const uint2 ecd = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vtab) + (i1 | roff));
-          o[m] = mfma32(ap, h8_of(eab, ecd), o[m]);
+          uint32_t i0, i1;
+          if ((m >> 1) == 0) { i0 = taddr<0, RS>(z0, R); i1 = taddr<0, RS>(z1, R); }
+          else if ((m >> 1) == 1) { i0 = taddr<1, RS>(z0, R); i1 = taddr<1, RS>(z1, R); }
+          else if ((m >> 1) == 2) { i0 = taddr<2, RS>(z0, R); i1 = taddr<2, RS>(z1, R); }
+          else { i0 = taddr<3, RS>(z0, R); i1 = taddr<3, RS>(z1, R); }
+          const uint2 eab = *reinterpret_cast<const uint2*>(tab + i0);
+          const uint2 ecd = *reinterpret_cast<const uint2*>(tab + i1);
+          o[m] = mfma32(ap, h8_of(eab.x, eab.y, ecd.x, ecd.y), o[m]);
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // ---- main loop: two register sets, the next super tile loading while one is used
+  constexpr int kStep = kWaves * kST;
+  while (st < c1) {
+    issue_loads<KB, VB>(rows, buf1, st + kStep, st + kStep < c1, lane);
+    process(buf0, st);
+    st += kStep;
+    if (st >= c1) break;
+    issue_loads<KB, VB>(rows, buf0, st + kStep, st + kStep < c1, lane);
+    process(buf1, st);
+    st += kStep;
   }
 
-  // ---- merge the four waves in LDS (the key table is no longer needed)
+  // ---- merge the four waves in LDS (the table is no longer needed) and write this
+  // split's partial (m, l, o') per head
   __syncthreads();
-  float* comb_o = reinterpret_cast<float*>(ktab);
+  float* comb_o = reinterpret_cast<float*>(tab);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * qq + j;
@@ -534,105 +606,94 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     comb_ml[wave][n][1] = l_run;
   }
   __syncthreads();
+  const int ns = a.n_split;
   float* ws_o = static_cast<float*>(a.workspace);
-  float* ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * a.n_split * QK;
-  const int64_t rbase = (static_cast<int64_t>(b) * a.hq + g * G) * a.n_split;
-  for (int idx = tid; idx < G * QK; idx += kThreads) {
-    const int h = idx >> 7, e = idx & 127;
+  float* ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * ns * QK;
+  const int64_t rbase = (static_cast<int64_t>(b) * a.hq + g * G) * ns;
+  for (int idx = tid; idx < G * (QK / 4); idx += kThreads) {
+    const int h = idx >> 5, e4 = idx & 31;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
-    float os = 0.0f, ls = 0.0f;
+    float4 os = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float ls = 0.0f;
     if (M > -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float m_w = comb_ml[w][h][0];
         const float f = m_w > -INFINITY ? __builtin_amdgcn_exp2f(m_w - M) : 0.0f;
-        os += f * (comb_o[(w * 2 * kMaxG + h) * QK + e] + comb_o[(w * 2 * kMaxG + G + h) * QK + e]);
+        const float4 hi4 = reinterpret_cast<const float4*>(comb_o + (w * 2 * kMaxG + h) * QK)[e4];
+        const float4 lo4 = reinterpret_cast<const float4*>(comb_o + (w * 2 * kMaxG + G + h) * QK)[e4];
+        os.x += f * (hi4.x + lo4.x);
+        os.y += f * (hi4.y + lo4.y);
+        os.z += f * (hi4.z + lo4.z);
+        os.w += f * (hi4.w + lo4.w);
         ls += f * comb_ml[w][h][1];
       }
     }
-    const int64_t r = rbase + static_cast<int64_t>(h) * a.n_split + split;
-    ws_o[r * QK + e] = os;
-    if (e == 0) {
-      ws_ml[2 * r] = M;
-      ws_ml[2 * r + 1] = ls;
-    }
+    const int64_t r = rbase + static_cast<int64_t>(h) * ns + split;
+    reinterpret_cast<float4*>(ws_o + r * QK)[e4] = os;
+    if (e4 == 0) reinterpret_cast<float2*>(ws_ml)[r] = make_float2(M, ls);
   }
 }
 
 // Merge the splits of one (b, query head): weights f_s = exp2(m_s - M), output
 // (sum_s f_s o'_s) / (sum_s f_s l_s), then R^T = D H / sqrt(128).  256 threads:
-// 32 float4 columns x 8 split groups.
+// thread (slice, c) folds float4 column c of splits slice, slice + 8, ... with a
+// running maximum, so every load of the head is issued without waiting for another;
+// the 8 slices are then combined in LDS.
 __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, SignWords sw) {
-  __shared__ float fs[1024];
-  __shared__ __attribute__((aligned(16))) float part[8][QK];
-  __shared__ float red[2];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) float po[8][QK];
+  __shared__ float pm[8], pl[8];
+  __shared__ float ov[QK];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int c4 = tid & 31, sl = tid >> 5;
   const int ns = a.n_split;
   const float* ws_o = static_cast<const float*>(a.workspace);
   const float* ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * ns * QK;
   const int64_t r0 = (static_cast<int64_t>(b) * a.hq + h) * ns;
-  if (wave == 0) {
-    float mx = -INFINITY;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ws_ml[2 * (r0 + s)]);
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 64));
-    float den = 0.0f;
-    for (int s = lane; s < ns; s += 64) {
-      const float ms = ws_ml[2 * (r0 + s)];
-      const float f = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - mx) : 0.0f;
-      fs[s] = f;
-      den += f * ws_ml[2 * (r0 + s) + 1];
+  float mx = -INFINITY, den = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+  for (int s = sl; s < ns; s += 8) {
+    const float2 ml = reinterpret_cast<const float2*>(ws_ml)[r0 + s];
+    const float4 v = reinterpret_cast<const float4*>(ws_o + (r0 + s) * QK)[c4];
+    if (ml.x > mx) {
+      const float f = mx > -INFINITY ? __builtin_amdgcn_exp2f(mx - ml.x) : 0.0f;
+      acc = make_float4(acc.x * f + v.x, acc.y * f + v.y, acc.z * f + v.z, acc.w * f + v.w);
+      den = den * f + ml.y;
+      mx = ml.x;
+    } else if (ml.x > -INFINITY) {
+      const float f = __builtin_amdgcn_exp2f(ml.x - mx);
+      acc = make_float4(acc.x + f * v.x, acc.y + f * v.y, acc.z + f * v.z, acc.w + f * v.w);
+      den += f * ml.y;
     }
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k, 64);
-    if (lane == 0) red[0] = den;
+  }
+  reinterpret_cast<float4*>(&po[sl][0])[c4] = acc;
+  if (c4 == 0) {
+    pm[sl] = mx;
+    pl[sl] = den;
   }
   __syncthreads();
-  const int e4 = tid & 31, grp = tid >> 5;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = grp; s < ns; s += 8) {
-    const float f = fs[s];
-    const float4 v = reinterpret_cast<const float4*>(ws_o + (r0 + s) * QK)[e4];
-    acc.x += f * v.x;
-    acc.y += f * v.y;
-    acc.z += f * v.z;
-    acc.w += f * v.w;
-  }
-  reinterpret_cast<float4*>(&part[grp][0])[e4] = acc;
-  __syncthreads();
-  float num = 0.0f;
   if (tid < QK) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi) num += part[gi][tid];
-  }
-  const float den = red[0];
-  __syncthreads();
-  float* o = &part[0][0];
-  if (tid < QK) o[tid] = den > 0.0f ? num / den : 0.0f;
-  __syncthreads();
-  for (int L = 1; L < QK; L <<= 1) {
-    float u = 0.0f, v = 0.0f;
-    int i = 0;
-    if (tid < QK / 2) {
-      i = (tid / L) * 2 * L + (tid % L);
-      u = o[i];
-      v = o[i + L];
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, pm[k]);
+    float num = 0.0f, dsum = 0.0f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = pm[k] > -INFINITY ? __builtin_amdgcn_exp2f(pm[k] - M) : 0.0f;
+        num += f * po[k][tid];
+        dsum += f * pl[k];
+      }
     }
-    __syncthreads();
-    if (tid < QK / 2) {
-      o[i] = u + v;
-      o[i + L] = u - v;
-    }
-    __syncthreads();
+    ov[tid] = dsum > 0.0f ? num / dsum : 0.0f;
   }
-  if (tid < QK) {
-    const int qd = (tid >> 3) & 3, k = tid >> 5, i = tid & 7;
-    const float r = o[tid] * kInvSqrtQK;
-    a.out[(static_cast<int64_t>(b) * a.hq + h) * QK + tid] =
-        ((sw.w[0][qd] >> (8 * k + i)) & 1u) ? -r : r;
+  __syncthreads();
+  if (tid < 64) {
+    const float2 v = reinterpret_cast<const float2*>(ov)[lane];
+    rotate_out(v, sw, lane, a.out + (static_cast<int64_t>(b) * a.hq + h) * QK);
   }
 }
 
@@ -648,7 +709,7 @@ void attn_mfma_partition(int32_t batch, int32_t hkv, int32_t t_max, int32_t* n_s
   const int64_t min_chunk = FATQ_ATTN_MIN_CHUNK;   // tokens per split at least
   const int64_t max_ns = t_max > 0 ? (t_max + min_chunk - 1) / min_chunk : 1;
   if (ns > max_ns) ns = max_ns;
-  if (ns > 1024) ns = 1024;
+  if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
   int64_t c = t_max > 0 ? (t_max + ns - 1) / ns : kST;
   c = (c + kST - 1) / kST * kST;

@@ -329,6 +329,10 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   a.workspace = workspace;
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
   if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+    // the MFMA kernels address one (batch, KV head) row of codes with 32-bit offsets
+    if (static_cast<int64_t>(t_max) * 64 >= (int64_t{1} << 31))
+      return fail(FA_TQ_EUNSUPPORTED, "%s: t_max %d: a cache row spans 2 GiB or more", who,
+                  t_max);
     fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
     return launched(fatq::launch_attn_mfma(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
                     who);

@@ -348,7 +348,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     sp[tid >> 4][i] = pack_h2(hi, lo);
   }
   lds_barrier();
-  {
+  if (tid < 256) {
     const int r = tid;
     uint8_t* row = tab + r * kRow;
     const uint32_t a0 = sp[0][r & 15], a1 = sp[0][r >> 4];
@@ -467,6 +467,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
       uint32_t f[4];
       key_fields<KB>(cur.k[t4], f);
       f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      f4 acc1 = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const uint32_t w = f[m >> 1];
@@ -480,8 +481,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
         }
         const uint2 e0 = *reinterpret_cast<const uint2*>(tab + a0);
         const uint2 e1 = *reinterpret_cast<const uint2*>(tab + a1);
-        acc = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc);
+        // two accumulators halve the chain of dependent products
+        if (m & 1) acc1 = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc1);
+        else acc = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc);
       }
+      acc += acc1;
       const float4 fk = *reinterpret_cast<const float4*>(&nrm[wave][0][16 * t4 + 4 * qq]);
       const float4 zb = *reinterpret_cast<const float4*>(&nrm[wave][1][16 * t4 + 4 * qq]);
       sc[t4][0] = fmaf(acc[0] + row_down<GT>(acc[0], G), fk.x, zb.x);
@@ -577,8 +581,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     __builtin_amdgcn_wave_barrier();
   };
 
-  // ---- main loop: two register sets, the next super tile loading while one is used
   constexpr int kStep = kWaves * kST;
+  // ---- main loop: two register sets, the next super tile loading while one is used
   while (st < c1) {
     issue_loads<KB, VB>(rows, buf1, st + kStep, st + kStep < c1, lane);
     process(buf0, st);
@@ -639,9 +643,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
 
 // Merge the splits of one (b, query head): weights f_s = exp2(m_s - M), output
 // (sum_s f_s o'_s) / (sum_s f_s l_s), then R^T = D H / sqrt(128).  256 threads:
-// thread (slice, c) folds float4 column c of splits slice, slice + 8, ... with a
-// running maximum, so every load of the head is issued without waiting for another;
-// the 8 slices are then combined in LDS.
+// thread (slice, c) folds float4 column c of splits slice, slice + 8, ... eight at a
+// time with a running maximum (the eight loads of a chunk are all in flight
+// together); the 8 slices are then combined in LDS.
 __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, SignWords sw) {
   __shared__ __attribute__((aligned(16))) float po[8][QK];
   __shared__ float pm[8], pl[8];
@@ -654,20 +658,37 @@ __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, Si
   const int64_t r0 = (static_cast<int64_t>(b) * a.hq + h) * ns;
   float mx = -INFINITY, den = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 8
-  for (int s = sl; s < ns; s += 8) {
-    const float2 ml = reinterpret_cast<const float2*>(ws_ml)[r0 + s];
-    const float4 v = reinterpret_cast<const float4*>(ws_o + (r0 + s) * QK)[c4];
-    if (ml.x > mx) {
-      const float f = mx > -INFINITY ? __builtin_amdgcn_exp2f(mx - ml.x) : 0.0f;
-      acc = make_float4(acc.x * f + v.x, acc.y * f + v.y, acc.z * f + v.z, acc.w * f + v.w);
-      den = den * f + ml.y;
-      mx = ml.x;
-    } else if (ml.x > -INFINITY) {
-      const float f = __builtin_amdgcn_exp2f(ml.x - mx);
-      acc = make_float4(acc.x + f * v.x, acc.y + f * v.y, acc.z + f * v.z, acc.w + f * v.w);
-      den += f * ml.y;
+  // chunks of 8 splits per thread: all 16 loads issued, then one rescale per chunk
+  for (int s0 = sl; s0 < ns; s0 += 64) {
+    float2 ml[8];
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = min(s0 + 8 * k, ns - 1);
+      ml[k] = reinterpret_cast<const float2*>(ws_ml)[r0 + s];
+      v[k] = reinterpret_cast<const float4*>(ws_o + (r0 + s) * QK)[c4];
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep the 16 loads ahead of their uses
+    float cm = mx;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + 8 * k >= ns) ml[k].x = -INFINITY;
+      cm = fmaxf(cm, ml[k].x);
+    }
+    // no branch: with every maximum still -inf all weights are 0 and acc stays 0
+    const float f0 = mx > -INFINITY ? __builtin_amdgcn_exp2f(mx - cm) : 0.0f;
+    acc = make_float4(acc.x * f0, acc.y * f0, acc.z * f0, acc.w * f0);
+    den *= f0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float f = ml[k].x > -INFINITY ? __builtin_amdgcn_exp2f(ml[k].x - cm) : 0.0f;
+      acc.x += f * v[k].x;
+      acc.y += f * v[k].y;
+      acc.z += f * v[k].z;
+      acc.w += f * v[k].w;
+      den += f * ml[k].y;
+    }
+    mx = cm;
   }
   reinterpret_cast<float4*>(&po[sl][0])[c4] = acc;
   if (c4 == 0) {

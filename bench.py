@@ -23,7 +23,8 @@ Other modes:
   --summarize-rocprof DIR print per-kernel means of a rocprofv3 CSV directory
                           (kernel_stats or counter_collection) and exit.
 
-After the timed steps (outside them), ``append_decode`` reports the decode-loop call
+After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv restoring
+the K cache to bf16 in the LMCache layout, and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
 positions are captured in one HIP graph and replayed, so the figure is GPU time per
@@ -174,6 +175,30 @@ def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -
     return {"us_per_call": round(us, 3), "new_tokens_per_sequence": 1, "attended_slots": T,
             "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph of 8 calls"}
+
+
+def restore_bf16(fa, w, cbk, seed, cache, reps=20) -> dict:
+    """GPU time of fa_tq_decode_kv restoring the whole K cache to bf16 in the LMCache
+    layout [tokens][heads * head_dim] (the serde restore path)."""
+    import torch
+    B, Hkv, T, d = w.batch, w.n_kv_heads, w.tokens, w.head_dim
+    lm = torch.empty((B, T, Hkv * d), dtype=torch.bfloat16, device="cuda")
+    view = lm.view(B, T, Hkv, d).permute(0, 2, 1, 3)
+    fa.decode_kv(cbk, seed, cache[0], cache[1], out=view)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fa.decode_kv(cbk, seed, cache[0], cache[1], out=view)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nblk = B * Hkv * T * (d // 128)
+    nbytes = nblk * (fa.code_bytes(w.k_bits) + 2 + 256)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "packed K cache -> bf16 [tokens][heads*head_dim]"}
 
 
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
@@ -336,6 +361,7 @@ def main():
     }
     if not args.no_append:
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
+        rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches[0])
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

@@ -140,6 +140,25 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
                           float *out, void *stream);
 
 /*
+ * Bulk restore of a packed cache to a plain K or V tensor (the decompression path
+ * of the LMCache page "TurboQuant Serde Backend": compressed bytes back to the
+ * original KV layout for storage reuse; no attention).  Every block of tokens
+ * t < n_tokens of every (b, h) row is decoded as fa_tq_decode does and written to
+ * out at element (b, h, t, c) = b*stride_b + h*stride_h + t*stride_t + c, as fp32 or
+ * as bf16 (round to nearest even of the fp32 result).  The LMCache tensor
+ * [2][num_layers][num_tokens][hidden] of one (K or V, layer) pair is the layout
+ * stride_h = head_dim, stride_t = hidden with batch 1.
+ *   codes, norms: device, SoA layout above (T_max = t_max, Hkv = n_kv_heads).
+ *   out: device, 16-byte aligned; strides non-negative multiples of 8 elements.
+ * batch, n_kv_heads or n_tokens == 0 is an OK no-op; n_tokens <= t_max.
+ */
+fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, int32_t head_dim,
+                             const uint8_t *codes, const uint16_t *norms, int32_t batch,
+                             int32_t n_kv_heads, int32_t n_tokens, int32_t t_max,
+                             void *out, fa_tq_dtype out_dtype, fa_tq_layout out_layout,
+                             void *stream);
+
+/*
  * Single-query decode attention over the packed cache ([Spec] "Optimization: Fused
  * dequant-dot"): per (b, query head h), with g = h / (n_q_heads / n_kv_heads):
  *   q' = R q;  s_t = scale * n_K[t] * <q', c_K[code_K[t]]>  for t < seq_lens[b];

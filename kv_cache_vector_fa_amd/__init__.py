@@ -58,6 +58,9 @@ _SIGS = {
     "fa_tq_encode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
                                     _P, ctypes.c_int, Layout, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
+    "fa_tq_decode_kv": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
+                                       _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, _P, ctypes.c_int, Layout, _P]),
     "fa_tq_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
                                     _P, _P, ctypes.c_int64, _P, _P]),
     "fa_tq_attn_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook),
@@ -195,6 +198,33 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
                           device=codes.device)
     _check(lib.fa_tq_decode(ctypes.byref(cb), seed, head_dim, _ptr(codes), _ptr(norms), n_vec,
                             _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None, out=None,
+              out_dtype=None, stream=None):
+    """Restore a packed cache [B, Hkv, T_max, nblk, cb] to a K or V tensor: tokens
+    [0, n_tokens) of every row into out [B, Hkv, n_tokens, head_dim] (any strides
+    with channel stride 1, bf16 or float32; bf16 by default)."""
+    import torch
+    lib = load()
+    B, H, t_max, nblk, cbytes = codes.shape
+    d = nblk * QK
+    n_tokens = t_max if n_tokens is None else n_tokens
+    if cbytes != code_bytes(cb.bits):
+        raise ValueError(f"code rows of {cbytes} bytes for {cb.bits}-bit codes")
+    if not codes.is_contiguous() or tuple(norms.shape) != (B, H, t_max, nblk) or \
+            not norms.is_contiguous():
+        raise ValueError("codes/norms must be the contiguous packed cache")
+    if out is None:
+        out = torch.empty((B, H, n_tokens, d), dtype=out_dtype or torch.bfloat16,
+                          device=codes.device)
+    if tuple(out.shape) != (B, H, n_tokens, d) or out.stride(3) != 1:
+        raise ValueError(f"out {tuple(out.shape)} for a cache of {tuple(codes.shape)}")
+    lay = Layout(out.stride(0), out.stride(1), out.stride(2))
+    _check(lib.fa_tq_decode_kv(ctypes.byref(cb), seed, d, _ptr(codes), _ptr(norms), B, H,
+                               n_tokens, t_max, _ptr(out), _dtype_code(out), lay,
+                               _stream(stream)))
     return out
 
 

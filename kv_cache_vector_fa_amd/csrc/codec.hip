@@ -25,6 +25,13 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kEncThreads = FATQ_ENCODE_THREADS;
 
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ float flip_sign(float x, uint32_t bit) {
   return __uint_as_float(__float_as_uint(x) ^ (bit << 31));
 }
@@ -563,11 +570,9 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
 }
 
 // Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block.
-template <int BITS>
-__global__ void __launch_bounds__(kThreads) decode_kernel(const uint8_t* codes,
-                                                          const uint16_t* norms,
-                                                          int64_t nblocks, int nblk, float* out,
-                                                          KTable tab, SignWords sw) {
+template <int BITS, bool BF16_OUT>
+__global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
+                                                          SignWords sw) {
   constexpr int CB = code_bytes_of<BITS>();
   __shared__ float cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
@@ -575,11 +580,19 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const uint8_t* codes,
   const int q = threadIdx.x & 3;
   const int64_t quad0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 2;
   const int64_t nquad = (static_cast<int64_t>(gridDim.x) * kThreads) >> 2;
-  const int j = static_cast<int>(quad0 % nblk);
-  const uint32_t sbits = sw.w[j][q];
+  const int64_t per_row = d.tokens * d.nblk;
+  const int64_t nblocks = d.rows * per_row;
   for (int64_t blk = quad0; blk < nblocks; blk += nquad) {
-    const uint8_t* crow = codes + blk * CB;
-    const float n = __half2float(__ushort_as_half(norms[blk]));
+    // block blk = (row, token t, block j) of the decoded range; its cache block sits
+    // in a row of t_max slots
+    const int64_t row = blk / per_row;
+    const int64_t rem = blk - row * per_row;
+    const int64_t t = rem / d.nblk;
+    const int j = static_cast<int>(rem - t * d.nblk);
+    const int64_t cblk = (row * d.t_max + t) * d.nblk + j;
+    const uint8_t* crow = d.codes + cblk * CB;
+    const float n = __half2float(__ushort_as_half(d.norms[cblk]));
+    const uint32_t sbits = sw.w[j][q];
     float v[4][8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -594,7 +607,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const uint8_t* codes,
       }
     }
     fwht_quad(v, q);
-    float4* o = reinterpret_cast<float4*>(out + blk * QK);
+    const int64_t b = row / d.heads, h = row - b * d.heads;
+    const int64_t eo = b * d.sb + h * d.sh + t * d.st + static_cast<int64_t>(QK) * j;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float r[8];
@@ -602,8 +616,17 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const uint8_t* codes,
       for (int i = 0; i < 8; ++i)
         r[i] = flip_sign(v[k][i] * kInvSqrtQK, (sbits >> (8 * k + i)) & 1u);
       const int c = q + 4 * k;
-      o[2 * c] = make_float4(r[0], r[1], r[2], r[3]);
-      o[2 * c + 1] = make_float4(r[4], r[5], r[6], r[7]);
+      if constexpr (BF16_OUT) {
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = bf16_rne(r[2 * m]) | (bf16_rne(r[2 * m + 1]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + eo + 8 * c) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(d.out) + eo + 8 * c);
+        o[0] = make_float4(r[0], r[1], r[2], r[3]);
+        o[1] = make_float4(r[4], r[5], r[6], r[7]);
+      }
     }
   }
 }
@@ -669,17 +692,26 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const uint8_t* codes, const uint16_t* norms, int64_t n_vec,
-                         int32_t nblk, float* out, const KTable& tab, const SignWords& sw,
+hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          hipStream_t stream) {
-  const int64_t nblocks = n_vec * nblk;
-  const dim3 grid(grid_for(nblocks)), block(kThreads);
-  switch (tab.bits) {
-    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, codes, norms, nblocks, nblk, out, tab, sw); break;
-    case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, codes, norms, nblocks, nblk, out, tab, sw); break;
-    case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, codes, norms, nblocks, nblk, out, tab, sw); break;
-    default: hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, stream, codes, norms, nblocks, nblk, out, tab, sw); break;
+  const dim3 grid(grid_for(d.rows * d.tokens * d.nblk)), block(kThreads);
+#define FATQ_DEC(B, F) hipLaunchKernelGGL((decode_kernel<B, F>), grid, block, 0, stream, d, tab, sw)
+  if (d.out_bf16) {
+    switch (tab.bits) {
+      case 2: FATQ_DEC(2, true); break;
+      case 3: FATQ_DEC(3, true); break;
+      case 4: FATQ_DEC(4, true); break;
+      default: FATQ_DEC(8, true); break;
+    }
+  } else {
+    switch (tab.bits) {
+      case 2: FATQ_DEC(2, false); break;
+      case 3: FATQ_DEC(3, false); break;
+      case 4: FATQ_DEC(4, false); break;
+      default: FATQ_DEC(8, false); break;
+    }
   }
+#undef FATQ_DEC
   return hipGetLastError();
 }
 

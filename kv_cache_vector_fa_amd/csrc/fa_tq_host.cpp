@@ -417,10 +417,61 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
   if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "fa_tq_decode: NULL device pointer");
   if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 1u))
     return fail(FA_TQ_EINVAL, "fa_tq_decode: codes and out must be 16-byte aligned");
+  fatq::DecodeLaunch d;
+  d.codes = codes;
+  d.norms = norms;
+  d.rows = 1;
+  d.tokens = n_vec;
+  d.t_max = n_vec;
+  d.heads = 1;
+  d.nblk = head_dim / fatq::QK;
+  d.out = out;
+  d.sb = 0;
+  d.sh = 0;
+  d.st = head_dim;
+  d.out_bf16 = 0;
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  return launched(fatq::launch_decode(codes, norms, n_vec, head_dim / fatq::QK, out, tab, sw,
-                                      static_cast<hipStream_t>(stream)),
+  return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)),
                   "fa_tq_decode");
+}
+
+fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
+                             const uint8_t* codes, const uint16_t* norms, int32_t batch,
+                             int32_t n_kv_heads, int32_t n_tokens, int32_t t_max, void* out,
+                             fa_tq_dtype out_dtype, fa_tq_layout out_layout, void* stream) {
+  static const char* who = "fa_tq_decode_kv";
+  fatq::KTable tab;
+  fa_tq_status st = check_codebook(cb, who, true, &tab);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative size", who);
+  if (n_tokens > t_max)
+    return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (out_dtype != FA_TQ_F32 && out_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: output dtype %d", who, (int)out_dtype);
+  if (out_layout.stride_b % 8 || out_layout.stride_h % 8 || out_layout.stride_t % 8 ||
+      out_layout.stride_b < 0 || out_layout.stride_h < 0 || out_layout.stride_t < 0)
+    return fail(FA_TQ_EINVAL, "%s: strides must be non-negative multiples of 8", who);
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return fail(FA_TQ_EINVAL, "%s: codes and out must be 16-byte aligned, norms 2-byte", who);
+  fatq::DecodeLaunch d;
+  d.codes = codes;
+  d.norms = norms;
+  d.rows = static_cast<int64_t>(batch) * n_kv_heads;
+  d.tokens = n_tokens;
+  d.t_max = t_max;
+  d.heads = n_kv_heads;
+  d.nblk = head_dim / fatq::QK;
+  d.out = out;
+  d.sb = out_layout.stride_b;
+  d.sh = out_layout.stride_h;
+  d.st = out_layout.stride_t;
+  d.out_bf16 = out_dtype == FA_TQ_BF16;
+  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)), who);
 }
 
 fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,

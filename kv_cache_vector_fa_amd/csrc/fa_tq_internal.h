@@ -45,8 +45,19 @@ struct EncodeLaunch {
 
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
                          hipStream_t stream);
-hipError_t launch_decode(const uint8_t* codes, const uint16_t* norms, int64_t n_vec,
-                         int32_t nblk, float* out, const KTable& tab, const SignWords& sw,
+// Decode of tokens [0, tokens) of `rows` cache rows of t_max slots each (row =
+// b * heads + h) into out[b][h][t][:] at element strides (sb, sh, st).
+struct DecodeLaunch {
+  const uint8_t* codes;
+  const uint16_t* norms;
+  int64_t rows, tokens, t_max;
+  int32_t heads, nblk;
+  void* out;
+  int64_t sb, sh, st;
+  int32_t out_bf16;
+};
+
+hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          hipStream_t stream);
 
 struct AttnLaunch {

@@ -59,6 +59,15 @@ K8 = np.float32(C_SCALE * np.float32(127.5))
 CODE_BYTES = {2: 32, 3: 48, 4: 64, 8: 128}
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of fp64 values, returned as fp64: 8
+    significant bits, fp32's exponent range (the bulk restore of the LMCache page
+    "TurboQuant Serde Backend" writes bf16 KV; values here are normal numbers)."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 def code_bytes(bits: int) -> int:
     """Packed bytes per 128-element block."""
     return CODE_BYTES[bits]

@@ -192,3 +192,16 @@ def test_u8_variant_error_bounds():
 def test_u8_zero_block():
     codes, sc = codec.encode_u8(np.zeros((1, 128), np.float32), S128)
     assert np.all(codes == 128) and sc[0] == 0
+
+
+def test_round_bf16_ties_and_library_agreement():
+    """Ties go to the even 8-bit significand; on fp32 inputs the result equals an
+    independent bf16 conversion (torch's round-to-nearest-even cast)."""
+    import torch
+    assert codec.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert codec.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert codec.round_bf16(np.array([-(1.0 + 2.0 ** -7 + 2.0 ** -20)]))[0] == -(1.0 + 2.0 ** -7)
+    assert codec.round_bf16(np.array([0.0]))[0] == 0.0
+    x = np.random.default_rng(5).standard_normal(100000).astype(np.float32) * 3.0
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(codec.round_bf16(x.astype(np.float64)), want)

@@ -21,6 +21,10 @@ sequence of length 0 gives an all-zero output; the scale is a caller argument
 ``attend_bruteforce`` is the plain definition softmax(scale q K_hat^T) V_hat on the
 decoded cache (``codec.decode_mse``), used to pin ``attend_fused``.
 
+Every function takes an optional second sign vector s2 ([turboq] "Encode pipeline"
+step 2: R = D2 H D1 / sqrt(128)); the rotated-domain identity holds for any
+orthogonal R, so the fused form is unchanged apart from the rotation.
+
 ``append_attend`` is [Spec] "Attention with TurboQuant cache": quantize the new K
 and V vectors into the cache at their positions, then attend with the
 full-precision query over the cached positions.  Positions map to cache slots
@@ -43,7 +47,7 @@ def _softmax64(s: np.ndarray) -> np.ndarray:
 
 
 def attend_fused(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits,
-                 k_centroids, v_centroids, s, scale, heads=None):
+                 k_centroids, v_centroids, s, scale, heads=None, s2=None):
     """fp64 fused rotated-domain attention.
 
     q: [B, Hq, d] (any float dtype), k_codes/v_codes: [B, Hkv, T, nblk, cb] uint8,
@@ -74,17 +78,17 @@ def attend_fused(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits
             vn = np.asarray(v_norms[b, g, :L], np.float16).astype(np.float64)
             cache = {(b, g): (kc, vc, kn, vn)}
         kc, vc, kn, vn = cache[(b, g)]
-        qr = forward64(q[b, h], s).reshape(nblk, QK)
+        qr = forward64(q[b, h], s, s2).reshape(nblk, QK)
         dots = np.einsum("tjc,jc->tj", kc, qr)
         scores = scale * np.sum(kn * dots, axis=-1)
         p = _softmax64(scores)
         o_rot = np.einsum("t,tj,tjc->jc", p, vn, vc)
-        out[b, h] = inverse64(o_rot.reshape(d), s)
+        out[b, h] = inverse64(o_rot.reshape(d), s, s2)
     return out
 
 
 def attend_bruteforce(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits,
-                      k_centroids, v_centroids, s, scale):
+                      k_centroids, v_centroids, s, scale, s2=None):
     """softmax(scale * q K_hat^T) V_hat on the decoded cache, fp64 (tiny inputs)."""
     q = np.asarray(q, np.float64)
     B, Hq, d = q.shape
@@ -98,16 +102,17 @@ def attend_bruteforce(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v
         for h in range(Hq):
             g = h // grp
             kh = decode_mse(unpack(k_codes[b, g, :L], k_bits), k_norms[b, g, :L], s,
-                            k_centroids)
+                            k_centroids, s2)
             vh = decode_mse(unpack(v_codes[b, g, :L], v_bits), v_norms[b, g, :L], s,
-                            v_centroids)
+                            v_centroids, s2)
             p = _softmax64(scale * (kh @ q[b, h]))
             out[b, h] = p @ vh
     return out
 
 
 def append_attend(q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, k_bits, v_bits,
-                  k_boundaries, k_centroids, v_boundaries, v_centroids, s, scale):
+                  k_boundaries, k_centroids, v_boundaries, v_centroids, s, scale, s2=None,
+                  norm_correct=False):
     """Append then attend (fp64 attention; canonical fp32 encode).
 
     q: [B, Hq, d]; k_new/v_new: [B, Hkv, n_new, d] float32; pos: [B] position of the
@@ -121,8 +126,8 @@ def append_attend(q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, k_bi
     v_new = np.asarray(v_new, np.float32)
     B, Hkv, n_new, d = k_new.shape
     T = k_codes.shape[2]
-    kc, kn, _ = encode_mse(k_new, s, k_boundaries)
-    vc, vn, _ = encode_mse(v_new, s, v_boundaries)
+    kc, kn, _ = encode_mse(k_new, s, k_boundaries, s2, k_centroids, norm_correct)
+    vc, vn, _ = encode_mse(v_new, s, v_boundaries, s2, v_centroids, norm_correct)
     kp, vp = pack(kc, k_bits), pack(vc, v_bits)
     for b in range(B):
         for i in range(n_new):
@@ -133,6 +138,6 @@ def append_attend(q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, k_bi
             v_norms[b, :, slot] = vn[b, :, i]
     lens = np.array([min(int(pos[b]) + n_new, T) for b in range(B)], np.int64)
     out = attend_fused(q, k_codes, k_norms, v_codes, v_norms, lens, k_bits, v_bits,
-                       k_centroids, v_centroids, s, scale)
+                       k_centroids, v_centroids, s, scale, s2=s2)
     return out, lens
 

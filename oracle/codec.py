@@ -96,9 +96,18 @@ def norm_f32(xb: np.ndarray) -> np.ndarray:
     return np.sqrt(q[..., 0])
 
 
-def encode_mse(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
+def encode_mse(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray,
+               s2: np.ndarray | None = None, centroids: np.ndarray | None = None,
+               norm_correct: bool = False):
     """Canonical fp32 encode.  x: float32 [..., d].  Returns (codes uint8 [..., d],
-    norms float16 [..., d/128], u float32 [..., d])."""
+    norms float16 [..., d/128], u float32 [..., d]).
+
+    s2: the second sign vector ([turboq] "Encode pipeline" step 2): h_i becomes
+    s2_i h_i (an exact sign change) before the scaling.
+    norm_correct ([turboq] "Encode pipeline" step 4): the stored norm is
+    RN16(RN32(n32 / r32)) with r32 the canonical fp32 norm of the block's centroid
+    values c[code_i] (same pairwise order as the input norm), so the decoded block
+    has the input's norm up to the fp16 rounding of the stored value."""
     x = np.asarray(x)
     assert x.dtype == np.float32
     d = x.shape[-1]
@@ -106,11 +115,19 @@ def encode_mse(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
     xs = xb * _sign_blocks(s, d)
     n32 = norm_f32(xb)
     h = fwht_stages_f32(xs)
+    if s2 is not None:
+        h = h * _sign_blocks(s2, d)
     g = np.zeros_like(n32)
     np.divide(C_SCALE, n32, out=g, where=n32 > 0)
     u = h * g[..., None]
     codes = np.searchsorted(np.asarray(boundaries, np.float32), u, side="left")
-    return (codes.astype(np.uint8).reshape(x.shape), n32.astype(np.float16),
+    stored = n32
+    if norm_correct:
+        cv = np.asarray(centroids, np.float32)[codes]
+        r32 = norm_f32(cv)
+        stored = np.zeros_like(n32)
+        np.divide(n32, r32, out=stored, where=r32 > 0)
+    return (codes.astype(np.uint8).reshape(x.shape), stored.astype(np.float16),
             u.reshape(x.shape))
 
 
@@ -126,23 +143,27 @@ def encode_mse_f64(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
 
 
 def decode_mse(codes: np.ndarray, norms16: np.ndarray, s: np.ndarray,
-               centroids: np.ndarray) -> np.ndarray:
-    """fp64 decode: x_hat = s * (H (n16 * c[code])) / sqrt(128), per block."""
+               centroids: np.ndarray, s2: np.ndarray | None = None) -> np.ndarray:
+    """fp64 decode: x_hat = s * (H (s2 * n16 * c[code])) / sqrt(128), per block (s2
+    omitted: all ones)."""
     codes = np.asarray(codes)
     d = codes.shape[-1]
     c = np.asarray(centroids, np.float32).astype(np.float64)
     n = np.asarray(norms16, np.float16).astype(np.float64)
     v = _blocks(c[codes]) * n[..., None]
-    return inverse64(v.reshape(codes.shape), s)
+    return inverse64(v.reshape(codes.shape), s, s2)
 
 
-def encode_u8(x: np.ndarray, s: np.ndarray):
-    """Canonical fp32 8-bit encode.  Returns (codes uint8 [..., d], scales fp16)."""
+def encode_u8(x: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None):
+    """Canonical fp32 8-bit encode.  Returns (codes uint8 [..., d], scales fp16);
+    s2 as for ``encode_mse``."""
     x = np.asarray(x)
     assert x.dtype == np.float32
     d = x.shape[-1]
     xs = _blocks(x) * _sign_blocks(s, d)
     h = fwht_stages_f32(xs)
+    if s2 is not None:
+        h = h * _sign_blocks(s2, d)
     a = np.max(np.abs(h), axis=-1)
     s16 = (a * C_SCALE).astype(np.float16)
     s32 = s16.astype(np.float32)
@@ -154,12 +175,13 @@ def encode_u8(x: np.ndarray, s: np.ndarray):
     return codes.reshape(x.shape), s16
 
 
-def decode_u8(codes: np.ndarray, scales16: np.ndarray, s: np.ndarray) -> np.ndarray:
+def decode_u8(codes: np.ndarray, scales16: np.ndarray, s: np.ndarray,
+              s2: np.ndarray | None = None) -> np.ndarray:
     """fp64 decode of the 8-bit variant."""
     codes = np.asarray(codes)
     sc = np.asarray(scales16, np.float16).astype(np.float64)
     y = (_blocks(codes.astype(np.float64)) - 127.5) / 127.5 * sc[..., None]
-    return inverse64(y.reshape(codes.shape), s)
+    return inverse64(y.reshape(codes.shape), s, s2)
 
 
 def pack(codes: np.ndarray, bits: int) -> np.ndarray:

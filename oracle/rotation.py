@@ -71,15 +71,22 @@ def _blocked(x: np.ndarray):
     return x.reshape(x.shape[:-1] + (d // QK, QK))
 
 
-def forward64(x: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """R x = H (s * x) / sqrt(128), blockwise per 128 elements, in fp64."""
+def forward64(x: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None) -> np.ndarray:
+    """R x = H (s * x) / sqrt(128), blockwise per 128 elements, in fp64.  With a
+    second sign vector ([turboq] "Encode pipeline" step 2): R x = s2 * H (s * x) /
+    sqrt(128)."""
     xb = _blocked(np.asarray(x, np.float64) * np.asarray(s, np.float64))
     y, _ = fwht_stages(xb, np.float64)
-    return (y / np.sqrt(QK)).reshape(np.shape(x))
+    y = (y / np.sqrt(QK)).reshape(np.shape(x))
+    return y if s2 is None else y * np.asarray(s2, np.float64)
 
 
-def inverse64(y: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """R^T y = s * (H y) / sqrt(128), blockwise per 128 elements, in fp64."""
-    yb = _blocked(np.asarray(y, np.float64))
+def inverse64(y: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None) -> np.ndarray:
+    """R^T y = s * (H y) / sqrt(128), blockwise per 128 elements, in fp64 (with a
+    second sign vector: s * H (s2 * y) / sqrt(128), the transpose of the above)."""
+    y = np.asarray(y, np.float64)
+    if s2 is not None:
+        y = y * np.asarray(s2, np.float64)
+    yb = _blocked(y)
     h, _ = fwht_stages(yb, np.float64)
     return (h / np.sqrt(QK)).reshape(np.shape(y)) * np.asarray(s, np.float64)

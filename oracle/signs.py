@@ -38,3 +38,11 @@ def signs(seed: int, head_dim: int) -> np.ndarray:
     """int8 array of +1/-1, s_i = -1 iff bit 63 of the i-th SplitMix64 draw is set."""
     draws = splitmix64(seed, head_dim)
     return np.array([-1 if (z >> 63) else 1 for z in draws], dtype=np.int8)
+
+
+def signs2(seed: int, head_dim: int) -> np.ndarray:
+    """The second fixed +/-1 vector of [turboq] "Encode pipeline" step 2 (applied
+    after the normalized butterflies).  Reading: the next head_dim draws of the same
+    SplitMix64 stream, i.e. draws head_dim .. 2 head_dim - 1, sign from the top bit."""
+    draws = splitmix64(seed, 2 * head_dim)[head_dim:]
+    return np.array([-1 if (z >> 63) else 1 for z in draws], dtype=np.int8)

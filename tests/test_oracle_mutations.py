@@ -77,3 +77,33 @@ def test_transposed_attention_operand_is_caught():
     good = att.attend_bruteforce(q, kc, kn, vc, vn, [T], 4, 4, ck, ck, s, 0.3)
     swapped = att.attend_fused(q, vc, vn, vc, vn, [T], 4, 4, ck, ck, s, 0.3)
     assert np.max(np.abs(good - swapped)) > 1e-3
+
+
+def test_second_signs_before_the_transform_are_caught(monkeypatch):
+    """Applying s2 before the butterflies (with s1) instead of after them breaks the
+    dense D2 H D1 pin."""
+    s1, s2 = sg.signs(42, 128), sg.signs2(42, 128)
+    real = rot.forward64
+
+    def early(x, s, s2_=None):
+        s_comb = np.asarray(s, np.float64) * (1.0 if s2_ is None else np.asarray(s2_, np.float64))
+        return real(x, s_comb)
+
+    monkeypatch.setattr(rot, "forward64", early)
+    R = np.diag(s2.astype(float)) @ rot.hadamard(128) @ np.diag(s1.astype(float)) / np.sqrt(128)
+    x = np.random.default_rng(0).standard_normal((3, 128))
+    assert not np.allclose(rot.forward64(x, s1, s2), x @ R.T, atol=1e-9)
+
+
+def test_corrected_norm_with_the_fp16_input_norm_is_caught():
+    """Dividing the fp16-rounded norm (instead of n32) by ||c[codes]|| and rounding
+    again misses the fp64 quotient in far more than a few blocks."""
+    x = np.random.default_rng(7).standard_normal((4000, 128)).astype(np.float32)
+    s1 = sg.signs(42, 128)
+    b, c = cbm.codebook(4)
+    codes, n16, _ = codec.encode_mse(x, s1, b)
+    r32 = codec.norm_f32(np.asarray(c, np.float32)[codes.reshape(-1, 1, 128)])
+    wrong = (n16.astype(np.float32) / r32).astype(np.float16)
+    r64 = np.linalg.norm(np.asarray(c, np.float32).astype(np.float64)[codes], axis=-1)
+    q64 = (np.linalg.norm(x.astype(np.float64), axis=-1) / r64).astype(np.float16)
+    assert np.count_nonzero(q64 != wrong[..., 0]) > 40

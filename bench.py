@@ -24,7 +24,8 @@ Other modes:
                           (kernel_stats or counter_collection) and exit.
 
 After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv restoring
-the K cache to bf16 in the LMCache layout, and ``append_decode`` reports the decode-loop call
+the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
+second sign vector and corrected norm, and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
 positions are captured in one HIP graph and replayed, so the figure is GPU time per
@@ -201,6 +202,28 @@ def restore_bf16(fa, w, cbk, seed, cache, reps=20) -> dict:
             "what": "packed K cache -> bf16 [tokens][heads*head_dim]"}
 
 
+def encode_variants(fa, w, cbk, seed, k, cache, reps=20) -> dict:
+    """GPU time of the K encode with the second sign vector and the corrected norm
+    (fa_tq_encode_ex), same input and cache as the step's K encode."""
+    import torch
+    flags = fa.TWO_SIGNS | fa.NORM_CORRECT
+    call = fa.encode_call(cbk, seed, k, cache[0], cache[1], flags=flags)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nblk = w.batch * w.n_kv_heads * w.tokens * (w.head_dim // 128)
+    nbytes = enc_bytes(nblk, 256, w.k_bits)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "flags": "two signs + corrected norm"}
+
+
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
     """The oracle as it stands, on ``n_slices`` (batch, KV head) slices of the workload
     (default: all of them): encode their K and V blocks in canonical fp32 and run fp64
@@ -362,6 +385,7 @@ def main():
     if not args.no_append:
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches[0])
+        rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks[0], caches[0])
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

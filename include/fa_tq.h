@@ -51,6 +51,23 @@ typedef enum {
 typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
 
 /*
+ * Variant flags of the _ex entry points ([turboq] "Encode pipeline"):
+ *   FA_TQ_TWO_SIGNS: the rotation is R = D2 H D1 / sqrt(128) (step 2: a second fixed
+ *     +/-1 vector after the normalized butterflies); D1 holds draws 0 .. head_dim-1
+ *     of the seed's SplitMix64 stream (as fa_tq_signs), D2 draws head_dim ..
+ *     2 head_dim - 1.  Encode, decode and attention of one cache must agree on it.
+ *     Encoding with bits 2-4 needs a mirror-symmetric codebook (as fa_tq_codebook_init
+ *     builds): the sign change of D2 is applied as the mirrored code.
+ *   FA_TQ_NORM_CORRECT (encode only, bits 2-4): store grp_norm / recon_norm (step 4),
+ *     recon_norm being the norm of the block's centroid values c[code_i] (fp32,
+ *     squares summed pairwise as for the input norm), so a decoded block keeps its
+ *     input norm up to the fp16 rounding of the stored value.
+ * Entry points without _ex use flags 0.
+ */
+#define FA_TQ_TWO_SIGNS 1u
+#define FA_TQ_NORM_CORRECT 2u
+
+/*
  * Scalar quantizer for one 128-element block ([Spec] "Step 2: Lloyd-Max Scalar
  * Quantization": bits, levels, boundaries[15], centroids[16]; plus the dimension
  * the table was built for).  Plain data, owned by the caller, passed by pointer
@@ -128,6 +145,13 @@ fa_tq_status fa_tq_encode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
                           const int32_t *t0, int32_t t_max,
                           uint8_t *codes, uint16_t *norms, void *stream);
 
+/* fa_tq_encode with variant flags (FA_TQ_TWO_SIGNS, FA_TQ_NORM_CORRECT). */
+fa_tq_status fa_tq_encode_ex(const fa_tq_codebook *cb, uint64_t seed, uint32_t flags,
+                             int32_t head_dim, const void *x, fa_tq_dtype x_dtype,
+                             fa_tq_layout x_layout, int32_t batch, int32_t n_kv_heads,
+                             int32_t n_tokens, const int32_t *t0, int32_t t_max,
+                             uint8_t *codes, uint16_t *norms, void *stream);
+
 /*
  * Decode ([Spec] "Overview": look up reconstruction values, then rotate back; the
  * exact inverse R^T = D H / sqrt(d)):  x_hat = s * (H (n16 * c[code])) / sqrt(128)
@@ -150,13 +174,14 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
  * stride_h = head_dim, stride_t = hidden with batch 1.
  *   codes, norms: device, SoA layout above (T_max = t_max, Hkv = n_kv_heads).
  *   out: device, 16-byte aligned; strides non-negative multiples of 8 elements.
+ * flags: 0 or FA_TQ_TWO_SIGNS (the rotation the cache was encoded with).
  * batch, n_kv_heads or n_tokens == 0 is an OK no-op; n_tokens <= t_max.
  */
-fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, int32_t head_dim,
-                             const uint8_t *codes, const uint16_t *norms, int32_t batch,
-                             int32_t n_kv_heads, int32_t n_tokens, int32_t t_max,
-                             void *out, fa_tq_dtype out_dtype, fa_tq_layout out_layout,
-                             void *stream);
+fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, uint32_t flags,
+                             int32_t head_dim, const uint8_t *codes, const uint16_t *norms,
+                             int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                             int32_t t_max, void *out, fa_tq_dtype out_dtype,
+                             fa_tq_layout out_layout, void *stream);
 
 /*
  * Single-query decode attention over the packed cache ([Spec] "Optimization: Fused
@@ -184,6 +209,16 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook 
                                int32_t n_q_heads, int32_t n_kv_heads, int32_t t_max,
                                float scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa_tq_attn_decode with flags 0 or FA_TQ_TWO_SIGNS (the cache's rotation). */
+fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                                  uint64_t seed, uint32_t flags, int32_t head_dim,
+                                  const void *q, fa_tq_dtype q_dtype,
+                                  const uint8_t *k_codes, const uint16_t *k_norms,
+                                  const uint8_t *v_codes, const uint16_t *v_norms,
+                                  const int32_t *seq_lens, int32_t batch, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t t_max, float scale, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Append, then attend ([Spec] "Attention with TurboQuant cache": the cached-attention
@@ -214,6 +249,20 @@ fa_tq_status fa_tq_attn_append(const fa_tq_codebook *cb_k, const fa_tq_codebook 
                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t t_max, float scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa_tq_attn_append with variant flags: FA_TQ_TWO_SIGNS (encode and attention) and
+ * FA_TQ_NORM_CORRECT (the new tokens' stored norms). */
+fa_tq_status fa_tq_attn_append_ex(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                                  uint64_t seed, uint32_t flags, int32_t head_dim,
+                                  const void *q, fa_tq_dtype q_dtype,
+                                  const void *k_new, const void *v_new, fa_tq_dtype kv_dtype,
+                                  fa_tq_layout k_layout, fa_tq_layout v_layout,
+                                  int32_t n_new, const int32_t *pos,
+                                  uint8_t *k_codes, uint16_t *k_norms,
+                                  uint8_t *v_codes, uint16_t *v_norms,
+                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t t_max, float scale, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -58,9 +58,14 @@ _SIGS = {
     "fa_tq_encode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
                                     _P, ctypes.c_int, Layout, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P]),
-    "fa_tq_decode_kv": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
-                                       _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                       ctypes.c_int32, _P, ctypes.c_int, Layout, _P]),
+    "fa_tq_encode_ex": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_uint32,
+                                       ctypes.c_int32, _P, ctypes.c_int, Layout, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                                       _P]),
+    "fa_tq_decode_kv": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_uint32,
+                                       ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int, Layout,
+                                       _P]),
     "fa_tq_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_int32,
                                     _P, _P, ctypes.c_int64, _P, _P]),
     "fa_tq_attn_decode": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook),
@@ -75,6 +80,22 @@ _SIGS = {
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
                                          _P, ctypes.c_size_t, _P]),
 }
+# The _ex entry points take the variant flags right after the seed.
+for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
+    _r, _a = _SIGS[_name]
+    _SIGS[_name + "_ex"] = (_r, _a[:3] + [ctypes.c_uint32] + _a[3:])
+
+TWO_SIGNS = 1       # FA_TQ_TWO_SIGNS: R = D2 H D1 / sqrt(128)
+NORM_CORRECT = 2    # FA_TQ_NORM_CORRECT: stored norm n / ||c[codes]|| (encode)
+
+
+def _with_flags(lib, name, args, flags, seed_at):
+    """The plain entry point for flags 0, else its _ex form with the flags right after
+    the seed (argument ``seed_at``)."""
+    if not flags:
+        return getattr(lib, name), args
+    k = seed_at + 1
+    return getattr(lib, name + "_ex"), args[:k] + (ctypes.c_uint32(flags),) + args[k:]
 
 
 def load(path: str | None = None):
@@ -172,18 +193,13 @@ def cache_buffers(batch, n_kv_heads, t_max, head_dim, bits, device="cuda"):
 
 
 def encode(cb: Codebook, seed: int, x, t_max: int | None = None, t0=None, codes=None,
-           norms=None, stream=None):
+           norms=None, stream=None, flags: int = 0):
     """Encode x [B, Hkv, T, d] (bf16/fp32, channel stride 1) into the packed cache."""
-    lib = load()
     B, H, T, d = x.shape
-    if x.stride(3) != 1:
-        raise ValueError("channel stride must be 1")
     t_max = T if t_max is None else t_max
     if codes is None or norms is None:
         codes, norms = cache_buffers(B, H, t_max, d, cb.bits, x.device)
-    lay = Layout(x.stride(0), x.stride(1), x.stride(2))
-    _check(lib.fa_tq_encode(ctypes.byref(cb), seed, d, _ptr(x), _dtype_code(x), lay, B, H, T,
-                            _ptr(t0), t_max, _ptr(codes), _ptr(norms), _stream(stream)))
+    encode_call(cb, seed, x, codes, norms, t_max, t0, stream, flags)()
     return codes, norms
 
 
@@ -202,7 +218,7 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
 
 
 def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None, out=None,
-              out_dtype=None, stream=None):
+              out_dtype=None, stream=None, flags: int = 0):
     """Restore a packed cache [B, Hkv, T_max, nblk, cb] to a K or V tensor: tokens
     [0, n_tokens) of every row into out [B, Hkv, n_tokens, head_dim] (any strides
     with channel stride 1, bf16 or float32; bf16 by default)."""
@@ -222,8 +238,8 @@ def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None
     if tuple(out.shape) != (B, H, n_tokens, d) or out.stride(3) != 1:
         raise ValueError(f"out {tuple(out.shape)} for a cache of {tuple(codes.shape)}")
     lay = Layout(out.stride(0), out.stride(1), out.stride(2))
-    _check(lib.fa_tq_decode_kv(ctypes.byref(cb), seed, d, _ptr(codes), _ptr(norms), B, H,
-                               n_tokens, t_max, _ptr(out), _dtype_code(out), lay,
+    _check(lib.fa_tq_decode_kv(ctypes.byref(cb), seed, flags, d, _ptr(codes), _ptr(norms), B,
+                               H, n_tokens, t_max, _ptr(out), _dtype_code(out), lay,
                                _stream(stream)))
     return out
 
@@ -237,22 +253,18 @@ def attn_workspace(batch, n_q_heads, n_kv_heads, t_max, head_dim=QK, device="cud
 
 
 def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,
-                v_norms, seq_lens, scale: float, out=None, workspace=None, stream=None):
+                v_norms, seq_lens, scale: float, out=None, workspace=None, stream=None,
+                flags: int = 0):
     """Single-query decode attention.  q [B, Hq, d]; caches [B, Hkv, T_max, nblk, cb]."""
     import torch
-    lib = load()
     B, Hq, d = q.shape
     Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    need = attn_workspace_bytes(B, Hq, Hkv, t_max, d)
     if workspace is None:
         workspace = attn_workspace(B, Hq, Hkv, t_max, d, q.device)
-    _check(lib.fa_tq_attn_decode(ctypes.byref(cb_k), ctypes.byref(cb_v), seed, d, _ptr(q),
-                                 _dtype_code(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
-                                 _ptr(v_norms), _ptr(seq_lens), B, Hq, Hkv, t_max,
-                                 float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)))
+    attn_decode_call(cb_k, cb_v, seed, q, k_codes, k_norms, v_codes, v_norms, seq_lens, scale,
+                     out, workspace, stream, flags)()
     return out
 
 
@@ -271,7 +283,8 @@ def _expect_cache(codes, norms, B, H, t_max, d, bits, name):
 
 
 def attn_append(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos, k_codes,
-                k_norms, v_codes, v_norms, scale: float, out=None, workspace=None, stream=None):
+                k_norms, v_codes, v_norms, scale: float, out=None, workspace=None, stream=None,
+                flags: int = 0):
     """Append k_new/v_new [B, Hkv, n_new, d] at positions pos [B] (slot = position mod
     T_max) into the packed caches, then decode attention for q [B, Hq, d]."""
     import torch
@@ -282,14 +295,14 @@ def attn_append(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos,
     if workspace is None:
         workspace = attn_workspace(B, Hq, Hkv, t_max, d, q.device)
     attn_append_call(cb_k, cb_v, seed, q, k_new, v_new, pos, k_codes, k_norms, v_codes,
-                     v_norms, scale, out, workspace, stream)()
+                     v_norms, scale, out, workspace, stream, flags)()
     return out
 
 
 # ------------------------------------------------------------ prepared device calls
 
 def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = None, t0=None,
-                stream=None):
+                stream=None, flags: int = 0):
     """``encode`` with its arguments marshalled once: returns a callable that launches
     fa_tq_encode on the same tensors (for tight loops where per-call Python work
     would dominate the kernel)."""
@@ -302,7 +315,7 @@ def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = No
             ctypes.c_int(_dtype_code(x)), Layout(x.stride(0), x.stride(1), x.stride(2)),
             ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(T), _ptr(t0),
             ctypes.c_int32(t_max), _ptr(codes), _ptr(norms), _stream(stream))
-    fn = lib.fa_tq_encode
+    fn, args = _with_flags(lib, "fa_tq_encode", args, flags, 1)
     keep = (cb, x, codes, norms, t0)
 
     def call():
@@ -312,7 +325,8 @@ def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = No
 
 
 def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,
-                     v_norms, seq_lens, scale: float, out, workspace, stream=None):
+                     v_norms, seq_lens, scale: float, out, workspace, stream=None,
+                     flags: int = 0):
     """``attn_decode`` with its arguments marshalled once (see ``encode_call``)."""
     lib = load()
     B, Hq, d = q.shape
@@ -323,7 +337,7 @@ def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_no
             ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max),
             ctypes.c_float(scale), _ptr(out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel()), _stream(stream))
-    fn = lib.fa_tq_attn_decode
+    fn, args = _with_flags(lib, "fa_tq_attn_decode", args, flags, 2)
     keep = (cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, seq_lens, out, workspace)
 
     def call():
@@ -334,7 +348,8 @@ def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_no
 
 
 def attn_append_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new, pos, k_codes,
-                     k_norms, v_codes, v_norms, scale: float, out, workspace, stream=None):
+                     k_norms, v_codes, v_norms, scale: float, out, workspace, stream=None,
+                     flags: int = 0):
     """``attn_append`` with its arguments marshalled once (see ``encode_call``)."""
     import torch
     lib = load()
@@ -361,7 +376,7 @@ def attn_append_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new,
             ctypes.c_int32(B), ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max),
             ctypes.c_float(scale), _ptr(out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel()), _stream(stream))
-    fn = lib.fa_tq_attn_append
+    fn, args = _with_flags(lib, "fa_tq_attn_append", args, flags, 2)
     keep = (cb_k, cb_v, q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, out, workspace)
 
     def call():

@@ -93,6 +93,11 @@ __device__ __forceinline__ bool sign_neg(const SignWords& sw, int e) {
   const int q = (e >> 3) & 3, k = e >> 5, i = e & 7;
   return (sw.w[0][q] >> (8 * k + i)) & 1u;
 }
+// The second sign vector s2 (R = D2 H D1 / sqrt(128)); +1 everywhere without it.
+__device__ __forceinline__ bool sign2_neg(const SignWords& sw, int e) {
+  const int q = (e >> 3) & 3, k = e >> 5, i = e & 7;
+  return sw.two && ((sw.w2[0][q] >> (8 * k + i)) & 1u);
+}
 
 template <int KB, int VB>
 __global__ void __launch_bounds__(kWaves * 64) attn_split_kernel(AttnLaunch a, KTable tk,
@@ -107,7 +112,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_split_kernel(AttnLaunch a, K
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = a.hq / a.hkv;
 
-  // Rotate the group's queries once: q' = H (s * q) / sqrt(128).
+  // Rotate the group's queries once: q' = s2 * H (s * q) / sqrt(128).
   if (tid < 16) {
     centk[tid] = tk.c[tid];
     centv[tid] = tv.c[tid];
@@ -131,7 +136,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_split_kernel(AttnLaunch a, K
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < G * QK; idx += kWaves * 64) qr[idx / QK][idx % QK] *= kInvSqrtQK;
+  for (int idx = tid; idx < G * QK; idx += kWaves * 64)
+    qr[idx / QK][idx % QK] *= sign2_neg(sw, idx % QK) ? -kInvSqrtQK : kInvSqrtQK;
   __syncthreads();
 
   const int split = blockIdx.x * kWaves + wave;
@@ -283,7 +289,8 @@ __global__ void __launch_bounds__(QK) attn_merge_kernel(AttnLaunch a, SignWords 
       num += w * ws_o[(r0 + s) * QK + e];
     }
   }
-  o[e] = den > 0.0f ? num / den : 0.0f;
+  const float oe = den > 0.0f ? num / den : 0.0f;
+  o[e] = sign2_neg(sw, e) ? -oe : oe;
   __syncthreads();
   for (int len = 1; len < QK; len <<= 1) {
     float u = 0.0f, v = 0.0f;

@@ -262,15 +262,22 @@ __device__ __forceinline__ uint32_t row_up(uint32_t x, int d) {
     return __shfl_up(x, d, 16);
 }
 
-// Sign of element e of the first 128-block (SignWords quad layout).
+// Sign of element e of the first 128-block (SignWords quad layout), of s1 and of the
+// second sign vector s2 (R = D2 H D1 / sqrt(128); s2 = +1 without it).
 __device__ __forceinline__ bool sign_bit(const SignWords& sw, int e) {
   const int c = e >> 3;
   return (sw.w[0][c & 3] >> (8 * (c >> 2) + (e & 7))) & 1u;
 }
+__device__ __forceinline__ bool sign_bit2(const SignWords& sw, int e) {
+  const int c = e >> 3;
+  return sw.two && ((sw.w2[0][c & 3] >> (8 * (c >> 2) + (e & 7))) & 1u);
+}
 
 // Inverse rotation of one head's merged output held as elements 2 lane, 2 lane + 1
-// (fp32, unnormalized Walsh-Hadamard, then signs and 1/sqrt(128)), stored to dst.
+// (fp32: s2, unnormalized Walsh-Hadamard, then s1 and 1/sqrt(128)), stored to dst.
 __device__ __forceinline__ void rotate_out(float2 o, const SignWords& sw, int lane, float* dst) {
+  o.x = sign_bit2(sw, 2 * lane) ? -o.x : o.x;
+  o.y = sign_bit2(sw, 2 * lane + 1) ? -o.y : o.y;
   float u = o.x + o.y, v = o.x - o.y;
 #pragma unroll
   for (int L = 1; L < 64; L <<= 1) {
@@ -378,8 +385,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     }
   }
 
-  // ---- q' = H (s * q): stride 64 in-lane, strides 32 .. 1 across lanes; the largest
-  // |q'| of each head to LDS
+  // ---- q' = s2 * H (s * q): stride 64 in-lane, strides 32 .. 1 across lanes; the
+  // largest |q'| of each head to LDS
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     float x0 = sign_bit(sw, lane) ? -qx[hs][0] : qx[hs][0];
@@ -392,8 +399,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
       u = up ? pu - u : u + pu;
       v = up ? pv - v : v + pv;
     }
-    qx[hs][0] = u;
-    qx[hs][1] = v;
+    qx[hs][0] = sign_bit2(sw, lane) ? -u : u;
+    qx[hs][1] = sign_bit2(sw, lane + 64) ? -v : v;
     float mx = fmaxf(fabsf(u), fabsf(v));
 #pragma unroll
     for (int s2 = 32; s2 >= 1; s2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s2, 64));

@@ -14,6 +14,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "fa_tq_internal.h"
 
 namespace fatq {
@@ -178,7 +180,22 @@ __device__ __forceinline__ void lds_barrier() {
 // lies outside the boundaries' exponent range hold no boundary and their base
 // follows from the sign alone; only the few cells inside the range (and the +0
 // cell) count boundaries.
-__device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTable& t) {
+// Entry of cell c: (threshold, base) or, for the corrected norm, (threshold, base,
+// c[base]^2, c[base + 1]^2) so that the chosen code's squared centroid comes with the
+// compare.
+__device__ __forceinline__ void set_cell(uint2* cells, uint32_t c, float thr, uint32_t base,
+                                         const KTable&) {
+  cells[c] = make_uint2(__float_as_uint(thr), base);
+}
+__device__ __forceinline__ void set_cell(uint4* cells, uint32_t c, float thr, uint32_t base,
+                                         const KTable& t) {
+  const float c0 = t.c[base], c1 = t.c[base + 1 < 16 ? base + 1 : 15];
+  cells[c] = make_uint4(__float_as_uint(thr), base, __float_as_uint(c0 * c0),
+                        __float_as_uint(c1 * c1));
+}
+
+template <typename Cell>
+__device__ __forceinline__ void fill_cells(Cell* cells, float* bext, const KTable& t) {
   const int nb = t.nb;
   if (threadIdx.x < 16) bext[threadIdx.x] = static_cast<int>(threadIdx.x) < nb ? t.b[threadIdx.x] : INFINITY;
   // Exponent range of the nonzero boundaries, and how many boundaries are < 0 / <= 0
@@ -205,7 +222,7 @@ __device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTab
     if ((e >= emin && e <= emax) || c == 0) continue;
     const bool neg = c >= kNegCell;
     const uint32_t base = e < emin ? (neg ? nneg : nle0) : (neg ? 0u : static_cast<uint32_t>(nb));
-    cells[c] = make_uint2(__float_as_uint(bext[base]), base);
+    set_cell(cells, c, bext[base], base, t);
   }
   // cells inside the range (4 per exponent and sign) and the +0 cell: count the
   // boundaries below the smallest member
@@ -222,7 +239,7 @@ __device__ __forceinline__ void fill_cells(uint2* cells, float* bext, const KTab
 #pragma unroll
     for (int m = 0; m < 15; ++m)
       if (m < nb) base += t.b[m] < umin ? 1u : 0u;
-    cells[c] = make_uint2(__float_as_uint(bext[base]), base);
+    set_cell(cells, c, bext[base], base, t);
   }
 }
 
@@ -240,6 +257,38 @@ __device__ __forceinline__ uint32_t bucketize8(const float (&y)[8], float g,
     acc = (acc << W) + cell.y + (u > __uint_as_float(cell.x) ? 1u : 0u);
   }
   return acc;
+}
+
+// As bucketize8, also returning the canonical fp32 sum of c[code_i]^2 over the 8
+// coordinates (pairwise: index bit 0, then 1, then 2).
+template <int W>
+__device__ __forceinline__ uint32_t bucketize8_sq(const float (&y)[8], float g,
+                                                  const uint4* cells, float& sq) {
+  uint32_t acc = 0;
+  float c2[8];
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    const float u = y[i] * g;
+    const uint32_t off = (__float_as_uint(u) >> (kCellShift - 4)) & ((kCells - 1u) << 4);
+    const uint4 cell = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(cells) + off);
+    const bool up = u > __uint_as_float(cell.x);
+    acc = (acc << W) + cell.y + (up ? 1u : 0u);
+    c2[i] = __uint_as_float(up ? cell.w : cell.z);
+  }
+  sq = ((c2[0] + c2[1]) + (c2[2] + c2[3])) + ((c2[4] + c2[5]) + (c2[6] + c2[7]));
+  return acc;
+}
+
+// Mirror masks of the second sign vector: with a mirror-symmetric codebook,
+// code(-u) = L - 1 - code(u) (up to u exactly on a boundary), so the sign change of
+// coordinate i becomes an XOR of its code field with L - 1.  Field width W, 8
+// coordinates of chunk byte `bits8` (bit i: coordinate i is negated).
+template <int W>
+__device__ __forceinline__ uint32_t mirror_mask(uint32_t bits8, uint32_t fieldmask) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m |= ((bits8 >> i) & 1u) * (fieldmask << (W * i));
+  return m;
 }
 
 // Cross-lane butterfly stage on one 8-element chunk: v <- v + mu * v(partner), the
@@ -399,11 +448,12 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
 // pairs; the x-stride is a multiple of nblk, so a quad keeps one block index j
 // (one sign slice) for the whole kernel.  The next block's input is loaded while
 // the current one is processed.
-template <int BITS, bool BF16>
+template <int BITS, bool BF16, bool NC>
 __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
                                                           SignWords sw) {
   constexpr int CB = code_bytes_of<BITS>();
-  __shared__ uint2 cells[BITS == 8 ? 1 : kCells];
+  typedef typename std::conditional<NC, uint4, uint2>::type Cell;
+  __shared__ Cell cells[BITS == 8 ? 1 : kCells];
   __shared__ float bext[16];
   if constexpr (BITS != 8) {
     fill_cells(cells, bext, tab);
@@ -424,6 +474,15 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   const float mu1 = (q & 1) ? -1.0f : 1.0f;
   const float mu2 = (q & 2) ? -1.0f : 1.0f;
   const uint32_t carried = ((q ^ (q >> 1)) & 1u) << 31;
+  // second sign vector: code mirror masks per chunk (zero without it)
+  const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;
+  uint32_t mirror[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b8 = (s2bits >> (8 * k)) & 0xFFu;
+    mirror[k] = BITS == 2 ? mirror_mask<2>(b8, 3u) : BITS == 3 ? mirror_mask<4>(b8, 7u)
+                                                              : mirror_mask<4>(b8, 15u);
+  }
 
   const int rows = a.batch * a.heads;
   constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
@@ -503,7 +562,7 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
           uint32_t code[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float t8 = x[k][i] * G;
+            const float t8 = x[k][i] * ((s2bits >> (8 * k + i)) & 1u ? -G : G);
             const float w = t8 + 127.5f;
             code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
           }
@@ -516,18 +575,23 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
       } else {
         const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
         const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
-        nbits = __half_as_ushort(__float2half_rn(n32));
+        float sq[4];
+        auto codes8 = [&](int k) {
+          constexpr int W = BITS == 2 ? 2 : 4;
+          if constexpr (NC) return bucketize8_sq<W>(x[k], g, cells, sq[k]) ^ mirror[k];
+          else return bucketize8<W>(x[k], g, cells) ^ mirror[k];
+        };
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int c = q + 4 * k;
           if constexpr (BITS == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(bucketize8<4>(x[k], g, cells), rc, co + 4 * c, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(codes8(k), rc, co + 4 * c, 0, 0);
           } else if constexpr (BITS == 2) {
-            __builtin_amdgcn_raw_buffer_store_b16(
-                static_cast<uint16_t>(bucketize8<2>(x[k], g, cells)), rc, co + 2 * c, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(codes8(k)), rc,
+                                                  co + 2 * c, 0, 0);
           } else {
             // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
-            const uint32_t w = bucketize8<4>(x[k], g, cells);
+            const uint32_t w = codes8(k);
             uint32_t lo = w & 0x33333333u;
             lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
             lo = (lo | (lo >> 4)) & 0x00FF00FFu;
@@ -539,6 +603,18 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
             __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(lo), rc, co + 2 * c, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(hi), rc, co + 32 + c, 0, 0);
           }
+        }
+        if constexpr (NC) {
+          // corrected norm n / ||c[codes]||: squared centroids summed in the input
+          // norm's order (bits 0-2 in the chunk, 3-4 across the quad, 5-6 across chunks)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sq[k] = quad_add<0xB1>(sq[k]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sq[k] = quad_add<0x4E>(sq[k]);
+          const float r32 = __builtin_sqrtf((sq[0] + sq[1]) + (sq[2] + sq[3]));
+          nbits = __half_as_ushort(__float2half_rn(r32 > 0.0f ? n32 / r32 : 0.0f));
+        } else {
+          nbits = __half_as_ushort(__float2half_rn(n32));
         }
       }
       __builtin_amdgcn_raw_buffer_store_b16(nbits, rn, valid && q == 0 ? 2 * cblk : kOOB, 0, 0);
@@ -593,6 +669,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
     const uint8_t* crow = d.codes + cblk * CB;
     const float n = __half2float(__ushort_as_half(d.norms[cblk]));
     const uint32_t sbits = sw.w[j][q];
+    const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;   // R^T = D1 H D2 / sqrt(128)
     float v[4][8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -600,10 +677,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
       load_chunk<BITS>(crow, q + 4 * k, code);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        float r;
         if constexpr (BITS == 8)
-          v[k][i] = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
+          r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
         else
-          v[k][i] = n * cent[code[i]];
+          r = n * cent[code[i]];
+        v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
       }
     }
     fwht_quad(v, q);
@@ -669,25 +748,23 @@ dim3 encode_grid(const EncodeLaunch& a) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
-                         hipStream_t stream) {
+                         bool norm_correct, hipStream_t stream) {
   const dim3 grid = encode_grid(a), block(kEncThreads);
-#define FATQ_ENC(B, F) \
-  hipLaunchKernelGGL((encode_kernel<B, F>), grid, block, 0, stream, a, tab, sw)
-  if (a.x_is_bf16) {
-    switch (tab.bits) {
-      case 2: FATQ_ENC(2, true); break;
-      case 3: FATQ_ENC(3, true); break;
-      case 4: FATQ_ENC(4, true); break;
-      default: FATQ_ENC(8, true); break;
-    }
-  } else {
-    switch (tab.bits) {
-      case 2: FATQ_ENC(2, false); break;
-      case 3: FATQ_ENC(3, false); break;
-      case 4: FATQ_ENC(4, false); break;
-      default: FATQ_ENC(8, false); break;
-    }
+#define FATQ_ENC(B, F, N) \
+  hipLaunchKernelGGL((encode_kernel<B, F, N>), grid, block, 0, stream, a, tab, sw)
+#define FATQ_ENC_BITS(F, N)              \
+  switch (tab.bits) {                    \
+    case 2: FATQ_ENC(2, F, N); break;    \
+    case 3: FATQ_ENC(3, F, N); break;    \
+    case 4: FATQ_ENC(4, F, N); break;    \
+    default: FATQ_ENC(8, F, false); break; \
   }
+  if (a.x_is_bf16) {
+    if (norm_correct) { FATQ_ENC_BITS(true, true) } else { FATQ_ENC_BITS(true, false) }
+  } else {
+    if (norm_correct) { FATQ_ENC_BITS(false, true) } else { FATQ_ENC_BITS(false, false) }
+  }
+#undef FATQ_ENC_BITS
 #undef FATQ_ENC
   return hipGetLastError();
 }

@@ -140,17 +140,43 @@ void make_signs(uint64_t seed, int head_dim, int8_t* out) {
   for (int i = 0; i < head_dim; ++i) out[i] = (g.next() >> 63) ? -1 : 1;
 }
 
-fatq::SignWords make_sign_words(uint64_t seed, int head_dim) {
-  std::vector<int8_t> s(head_dim);
-  make_signs(seed, head_dim, s.data());
+// Sign words of s1 (draws 0 .. d-1 of the seed's stream) and, for the two-sign
+// rotation, s2 (draws d .. 2d-1).
+fatq::SignWords make_sign_words(uint64_t seed, int head_dim, bool two = false) {
+  std::vector<int8_t> s(2 * static_cast<size_t>(head_dim));
+  make_signs(seed, 2 * head_dim, s.data());
   fatq::SignWords sw;
   std::memset(&sw, 0, sizeof(sw));
+  sw.two = two ? 1 : 0;
   for (int j = 0; j < head_dim / fatq::QK; ++j)
     for (int q = 0; q < 4; ++q)
       for (int k = 0; k < 4; ++k)
-        for (int i = 0; i < 8; ++i)
-          if (s[fatq::QK * j + 8 * (q + 4 * k) + i] < 0) sw.w[j][q] |= 1u << (8 * k + i);
+        for (int i = 0; i < 8; ++i) {
+          const int e = fatq::QK * j + 8 * (q + 4 * k) + i;
+          if (s[e] < 0) sw.w[j][q] |= 1u << (8 * k + i);
+          if (two && s[head_dim + e] < 0) sw.w2[j][q] |= 1u << (8 * k + i);
+        }
   return sw;
+}
+
+// Flags of the _ex entry points.  Encode takes both; decode and attention take the
+// rotation flag only (the corrected norm is a property of the stored norms).
+fa_tq_status check_flags(uint32_t flags, uint32_t allowed, const fa_tq_codebook* cb,
+                         const char* who) {
+  if (flags & ~allowed) return fail(FA_TQ_EINVAL, "%s: unknown flags 0x%x", who, flags & ~allowed);
+  if ((flags & FA_TQ_NORM_CORRECT) && cb && cb->bits == 8)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: the corrected norm needs a 2-4 bit codebook", who);
+  if ((flags & FA_TQ_TWO_SIGNS) && cb && cb->bits != 8) {
+    // the encoder applies s2 by mirroring codes through the table's symmetry
+    const int L = cb->levels;
+    bool sym = true;
+    for (int j = 0; j + 1 < L; ++j) sym = sym && cb->boundaries[j] == -cb->boundaries[L - 2 - j];
+    for (int j = 0; j < L; ++j) sym = sym && cb->centroids[j] == -cb->centroids[L - 1 - j];
+    if (!sym)
+      return fail(FA_TQ_EUNSUPPORTED,
+                  "%s: the two-sign rotation needs a mirror-symmetric codebook", who);
+  }
+  return ok();
 }
 
 fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool allow8,
@@ -216,7 +242,7 @@ fa_tq_status launched(hipError_t e, const char* what) {
 }
 
 fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t seed,
-                         int32_t head_dim,
+                         uint32_t flags, int32_t head_dim,
                           const void* x, fa_tq_dtype x_dtype, fa_tq_layout x_layout,
                           int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
                           const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
@@ -224,6 +250,8 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   fatq::KTable tab;
   fa_tq_status st = check_codebook(cb, who, true, &tab);
   if (st != FA_TQ_OK) return st;
+  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT, cb, who)) != FA_TQ_OK)
+    return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
@@ -262,13 +290,15 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   a.codes = codes;
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  return launched(fatq::launch_encode(a, tab, sw, static_cast<hipStream_t>(stream)),
+  const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
+  return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0,
+                                      static_cast<hipStream_t>(stream)),
                   who);
 }
 
 fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
-                       const fa_tq_codebook* cb_v, uint64_t seed, int32_t head_dim,
+                       const fa_tq_codebook* cb_v, uint64_t seed, uint32_t flags,
+                       int32_t head_dim,
                        const void* q, fa_tq_dtype q_dtype, const uint8_t* k_codes,
                        const uint16_t* k_norms, const uint8_t* v_codes,
                        const uint16_t* v_norms, const int32_t* seq_lens, const int32_t* pos,
@@ -280,6 +310,7 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   if (st != FA_TQ_OK) return st;
   if ((st = check_codebook(cb_v, who, false, &tv)) != FA_TQ_OK)
     return st;
+  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS, nullptr, who)) != FA_TQ_OK) return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (head_dim != fatq::QK)
     return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (this build: 128)", who,
@@ -327,7 +358,7 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   a.scale = scale;
   a.out = out;
   a.workspace = workspace;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
   if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
     // the MFMA kernels address one (batch, KV head) row of codes with 32-bit offsets
     if (static_cast<int64_t>(t_max) * 64 >= (int64_t{1} << 31))
@@ -401,8 +432,17 @@ fa_tq_status fa_tq_encode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
                           int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
                           const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
                           void* stream) {
-  return encode_impl("fa_tq_encode", cb, seed, head_dim, x, x_dtype, x_layout, batch,
+  return encode_impl("fa_tq_encode", cb, seed, 0, head_dim, x, x_dtype, x_layout, batch,
                      n_kv_heads, n_tokens, t0, t_max, codes, norms, stream, false);
+}
+
+fa_tq_status fa_tq_encode_ex(const fa_tq_codebook* cb, uint64_t seed, uint32_t flags,
+                             int32_t head_dim, const void* x, fa_tq_dtype x_dtype,
+                             fa_tq_layout x_layout, int32_t batch, int32_t n_kv_heads,
+                             int32_t n_tokens, const int32_t* t0, int32_t t_max,
+                             uint8_t* codes, uint16_t* norms, void* stream) {
+  return encode_impl("fa_tq_encode_ex", cb, seed, flags, head_dim, x, x_dtype, x_layout,
+                     batch, n_kv_heads, n_tokens, t0, t_max, codes, norms, stream, false);
 }
 
 fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
@@ -435,14 +475,18 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
                   "fa_tq_decode");
 }
 
-fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
-                             const uint8_t* codes, const uint16_t* norms, int32_t batch,
-                             int32_t n_kv_heads, int32_t n_tokens, int32_t t_max, void* out,
-                             fa_tq_dtype out_dtype, fa_tq_layout out_layout, void* stream) {
+fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t flags,
+                             int32_t head_dim, const uint8_t* codes, const uint16_t* norms,
+                             int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                             int32_t t_max, void* out, fa_tq_dtype out_dtype,
+                             fa_tq_layout out_layout, void* stream) {
   static const char* who = "fa_tq_decode_kv";
   fatq::KTable tab;
   fa_tq_status st = check_codebook(cb, who, true, &tab);
   if (st != FA_TQ_OK) return st;
+  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS, nullptr, who)) != FA_TQ_OK) return st;
+  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT, cb, who)) != FA_TQ_OK)
+    return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
@@ -470,7 +514,7 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, int32_t he
   d.sh = out_layout.stride_h;
   d.st = out_layout.stride_t;
   d.out_bf16 = out_dtype == FA_TQ_BF16;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim);
+  const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
   return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -482,9 +526,22 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook*
                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t t_max, float scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
+  return fa_tq_attn_decode_ex(cb_k, cb_v, seed, 0, head_dim, q, q_dtype, k_codes, k_norms,
+                              v_codes, v_norms, seq_lens, batch, n_q_heads, n_kv_heads, t_max,
+                              scale, out, workspace, workspace_bytes, stream);
+}
+
+fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                                  uint64_t seed, uint32_t flags, int32_t head_dim,
+                                  const void* q, fa_tq_dtype q_dtype, const uint8_t* k_codes,
+                                  const uint16_t* k_norms, const uint8_t* v_codes,
+                                  const uint16_t* v_norms, const int32_t* seq_lens,
+                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t t_max, float scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (batch > 0 && !seq_lens) return fail(FA_TQ_EINVAL, "fa_tq_attn_decode: seq_lens is NULL");
-  return attn_impl("fa_tq_attn_decode", cb_k, cb_v, seed, head_dim, q, q_dtype, k_codes,
-                   k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
+  return attn_impl("fa_tq_attn_decode", cb_k, cb_v, seed, flags, head_dim, q, q_dtype,
+                   k_codes, k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
                    n_kv_heads, t_max, scale, out, workspace, workspace_bytes, stream);
 }
 
@@ -497,6 +554,22 @@ fa_tq_status fa_tq_attn_append(const fa_tq_codebook* cb_k, const fa_tq_codebook*
                                uint16_t* v_norms, int32_t batch, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t t_max, float scale, float* out,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_tq_attn_append_ex(cb_k, cb_v, seed, 0, head_dim, q, q_dtype, k_new, v_new,
+                              kv_dtype, k_layout, v_layout, n_new, pos, k_codes, k_norms,
+                              v_codes, v_norms, batch, n_q_heads, n_kv_heads, t_max, scale, out,
+                              workspace, workspace_bytes, stream);
+}
+
+fa_tq_status fa_tq_attn_append_ex(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                                  uint64_t seed, uint32_t flags, int32_t head_dim,
+                                  const void* q, fa_tq_dtype q_dtype, const void* k_new,
+                                  const void* v_new, fa_tq_dtype kv_dtype,
+                                  fa_tq_layout k_layout, fa_tq_layout v_layout, int32_t n_new,
+                                  const int32_t* pos, uint8_t* k_codes, uint16_t* k_norms,
+                                  uint8_t* v_codes, uint16_t* v_norms, int32_t batch,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t t_max,
+                                  float scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   static const char* who = "fa_tq_attn_append";
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max <= 0)
     return fail(FA_TQ_EINVAL, "%s: bad sizes", who);
@@ -508,18 +581,18 @@ fa_tq_status fa_tq_attn_append(const fa_tq_codebook* cb_k, const fa_tq_codebook*
   // rejected call leaves the cache untouched.
   fa_tq_status st;
   for (bool check_only : {true, false}) {
-    if ((st = encode_impl(who, cb_k, seed, head_dim, k_new, kv_dtype, k_layout, batch,
+    if ((st = encode_impl(who, cb_k, seed, flags, head_dim, k_new, kv_dtype, k_layout, batch,
                           n_kv_heads, n_new, pos, t_max, k_codes, k_norms, stream, true,
                           check_only)) != FA_TQ_OK)
       return st;
-    if ((st = encode_impl(who, cb_v, seed, head_dim, v_new, kv_dtype, v_layout, batch,
+    if ((st = encode_impl(who, cb_v, seed, flags, head_dim, v_new, kv_dtype, v_layout, batch,
                           n_kv_heads, n_new, pos, t_max, v_codes, v_norms, stream, true,
                           check_only)) != FA_TQ_OK)
       return st;
-    if ((st = attn_impl(who, cb_k, cb_v, seed, head_dim, q, q_dtype, k_codes, k_norms,
-                        v_codes, v_norms, nullptr, pos, n_new, batch, n_q_heads, n_kv_heads,
-                        t_max, scale, out, workspace, workspace_bytes, stream, check_only)) !=
-        FA_TQ_OK)
+    if ((st = attn_impl(who, cb_k, cb_v, seed, flags & FA_TQ_TWO_SIGNS, head_dim, q, q_dtype,
+                        k_codes, k_norms, v_codes, v_norms, nullptr, pos, n_new, batch,
+                        n_q_heads, n_kv_heads, t_max, scale, out, workspace, workspace_bytes,
+                        stream, check_only)) != FA_TQ_OK)
       return st;
   }
   return ok();

@@ -17,6 +17,10 @@ constexpr int MAX_BLK = FA_TQ_MAX_HEAD_DIM / FA_TQ_QK;
 // of element 128 j + e is -1.
 struct SignWords {
   uint32_t w[MAX_BLK][4];
+  // The second sign vector s2 of the two-sign rotation R = D2 H D1 / sqrt(128)
+  // ([turboq] "Encode pipeline" step 2), same layout; two == 0: s2 = all +1.
+  uint32_t w2[MAX_BLK][4];
+  int32_t two;
 };
 
 // Codebook as the kernels read it (uniform kernel arguments).
@@ -43,8 +47,9 @@ struct EncodeLaunch {
   int32_t x_is_bf16;
 };
 
+// norm_correct: store n / ||c[codes]|| ([turboq] "Encode pipeline" step 4; bits 2-4).
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
-                         hipStream_t stream);
+                         bool norm_correct, hipStream_t stream);
 // Decode of tokens [0, tokens) of `rows` cache rows of t_max slots each (row =
 // b * heads + h) into out[b][h][t][:] at element strides (sb, sh, st).
 struct DecodeLaunch {

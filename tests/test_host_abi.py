@@ -133,3 +133,35 @@ def test_attn_validation_before_launch(lib):
     c8 = fa.codebook_init(128, 8)
     assert _attn_raw(lib, c8, cv, 128, 1, 32, 8, 64, big) == fa.FA_TQ_EUNSUPPORTED
     assert _attn_raw(lib, ck, cv, 128, 0, 32, 8, 64, big) == fa.FA_TQ_OK
+
+
+def _encode_ex_raw(lib, cb, flags, B=1, ptr=1 << 20):
+    P = ctypes.c_void_p(ptr)
+    lay = fa.Layout(128, 128, 128)
+    return lib.fa_tq_encode_ex(ctypes.byref(cb), 42, flags, 128, P, fa.FA_TQ_BF16, lay, B, 1, 1,
+                               None, 1, P, P, None)
+
+
+def test_variant_flags_validated_before_launch(lib):
+    """Unknown flags, the corrected norm with the 8-bit grid, and the two-sign
+    rotation with a codebook that is not mirror symmetric are rejected (no device
+    needed); valid flags with an empty batch are an OK no-op."""
+    c4, c8 = fa.codebook_init(128, 4), fa.codebook_init(128, 8)
+    assert _encode_ex_raw(lib, c4, 4) == fa.FA_TQ_EINVAL
+    assert _encode_ex_raw(lib, c8, fa.NORM_CORRECT) == fa.FA_TQ_EUNSUPPORTED
+    b = np.array(c4.boundaries[:15], np.float32)
+    c = np.array(c4.centroids[:16], np.float32)
+    c[3] *= 1.01                                    # still ascending, no longer symmetric
+    skew = fa.codebook_from_arrays(4, b, c)
+    assert _encode_ex_raw(lib, skew, fa.TWO_SIGNS) == fa.FA_TQ_EUNSUPPORTED
+    assert "mirror" in lib.fa_tq_last_error().decode()
+    assert _encode_ex_raw(lib, c4, fa.TWO_SIGNS | fa.NORM_CORRECT, B=0) == fa.FA_TQ_OK
+    P = ctypes.c_void_p(1 << 20)
+    # decode and attention accept only the rotation flag
+    lay = fa.Layout(0, 128, 128)
+    assert lib.fa_tq_decode_kv(ctypes.byref(c4), 42, fa.NORM_CORRECT, 128, P, P, 1, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay, None) == fa.FA_TQ_EINVAL
+    c2 = fa.codebook_init(128, 2)
+    assert lib.fa_tq_attn_decode_ex(ctypes.byref(c4), ctypes.byref(c2), 42, fa.NORM_CORRECT, 128,
+                                    P, 1, P, P, P, P, P, 1, 32, 8, 64, 0.088, P, P, 1 << 40,
+                                    None) == fa.FA_TQ_EINVAL

@@ -178,19 +178,22 @@ def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph of 8 calls"}
 
 
-def restore_bf16(fa, w, cbk, seed, cache, reps=20) -> dict:
+def restore_bf16(fa, w, cbk, seed, caches, reps=20) -> dict:
     """GPU time of fa_tq_decode_kv restoring the whole K cache to bf16 in the LMCache
-    layout [tokens][heads * head_dim] (the serde restore path)."""
+    layout [tokens][heads * head_dim] (the serde restore path), over the rotating
+    cache copies of the step."""
     import torch
     B, Hkv, T, d = w.batch, w.n_kv_heads, w.tokens, w.head_dim
     lm = torch.empty((B, T, Hkv * d), dtype=torch.bfloat16, device="cuda")
     view = lm.view(B, T, Hkv, d).permute(0, 2, 1, 3)
-    fa.decode_kv(cbk, seed, cache[0], cache[1], out=view)
+    for c in caches:
+        fa.decode_kv(cbk, seed, c[0], c[1], out=view)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        fa.decode_kv(cbk, seed, cache[0], cache[1], out=view)
+    for i in range(reps):
+        c = caches[i % len(caches)]
+        fa.decode_kv(cbk, seed, c[0], c[1], out=view)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
@@ -202,18 +205,19 @@ def restore_bf16(fa, w, cbk, seed, cache, reps=20) -> dict:
             "what": "packed K cache -> bf16 [tokens][heads*head_dim]"}
 
 
-def encode_variants(fa, w, cbk, seed, k, cache, reps=20) -> dict:
+def encode_variants(fa, w, cbk, seed, ks, caches, reps=20) -> dict:
     """GPU time of the K encode with the second sign vector and the corrected norm
-    (fa_tq_encode_ex), same input and cache as the step's K encode."""
+    (fa_tq_encode_ex), over the same rotating input and cache copies as the step."""
     import torch
     flags = fa.TWO_SIGNS | fa.NORM_CORRECT
-    call = fa.encode_call(cbk, seed, k, cache[0], cache[1], flags=flags)
-    call()
+    calls = [fa.encode_call(cbk, seed, k, c[0], c[1], flags=flags) for k, c in zip(ks, caches)]
+    for c in calls:
+        c()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        call()
+    for i in range(reps):
+        calls[i % len(calls)]()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
@@ -353,8 +357,8 @@ def main():
             rec["vectors_per_s"] = round(nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true>",
-             "encode_v": f"encode_kernel<{w.v_bits}, true>"}.get(dom, dom)
+    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false>",
+             "encode_v": f"encode_kernel<{w.v_bits}, true, false>"}.get(dom, dom)
     traffic = traffic_for(kname)
     roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
@@ -384,8 +388,8 @@ def main():
     }
     if not args.no_append:
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
-        rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches[0])
-        rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks[0], caches[0])
+        rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)
+        rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks, caches)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

@@ -51,7 +51,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .rotation import QK, fwht_stages_f32, forward64, inverse64
+from .rotation import QK, fwht_stages, fwht_stages_f32, forward64, inverse64, inverse64_whole
 
 C_SCALE = np.float32(1.0 / np.sqrt(128.0))
 K8 = np.float32(C_SCALE * np.float32(127.5))
@@ -152,6 +152,37 @@ def decode_mse(codes: np.ndarray, norms16: np.ndarray, s: np.ndarray,
     n = np.asarray(norms16, np.float16).astype(np.float64)
     v = _blocks(c[codes]) * n[..., None]
     return inverse64(v.reshape(codes.shape), s, s2)
+
+
+def encode_mse_whole(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
+    """Canonical fp32 encode with one rotation over the whole vector and the codebook
+    of dimension d = head_dim ([Spec] "Step 1" and "Step 2": R is d x d, one codebook
+    per (head_dim, bits)); d a power of two.  One norm per vector.
+
+    n32 = RN32(sqrt(pairwise sum of RN32(x_i^2))) over index bits 0 .. log2(d) - 1;
+    h = fp32 butterflies of s * x in stage order 1, 2, ..., d/2; g = RN32(c_d / n32)
+    with c_d = RN32(1/sqrt(d)) (0 when n32 == 0); u = RN32(h * g);
+    code = #{j : b_j < u}.  Returns (codes uint8 [..., d], norms fp16 [...], u)."""
+    x = np.asarray(x)
+    assert x.dtype == np.float32
+    d = x.shape[-1]
+    assert d & (d - 1) == 0, "the whole-vector transform needs a power-of-two length"
+    n32 = norm_f32(x)
+    h, _ = fwht_stages(x * np.asarray(s, np.float32), dtype=np.float32)
+    c_d = np.float32(1.0 / np.sqrt(float(d)))
+    g = np.zeros_like(n32)
+    np.divide(c_d, n32, out=g, where=n32 > 0)
+    u = h * g[..., None]
+    codes = np.searchsorted(np.asarray(boundaries, np.float32), u, side="left")
+    return codes.astype(np.uint8), n32.astype(np.float16), u
+
+
+def decode_mse_whole(codes: np.ndarray, norms16: np.ndarray, s: np.ndarray,
+                     centroids: np.ndarray) -> np.ndarray:
+    """fp64 decode of the whole-vector mode: x_hat = s * H_d (n16 * c[code]) / sqrt(d)."""
+    c = np.asarray(centroids, np.float32).astype(np.float64)
+    n = np.asarray(norms16, np.float16).astype(np.float64)
+    return inverse64_whole(c[np.asarray(codes)] * n[..., None], s)
 
 
 def encode_u8(x: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None):

@@ -90,3 +90,18 @@ def inverse64(y: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None) -> np.
     yb = _blocked(y)
     h, _ = fwht_stages(yb, np.float64)
     return (h / np.sqrt(QK)).reshape(np.shape(y)) * np.asarray(s, np.float64)
+
+
+def forward64_whole(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One transform over the whole vector ([Spec] "Step 1": R is d x d with d =
+    head_dim, a power of two): R x = H_d (s * x) / sqrt(d), fp64."""
+    x = np.asarray(x, np.float64) * np.asarray(s, np.float64)
+    y, _ = fwht_stages(x, np.float64)
+    return y / np.sqrt(x.shape[-1])
+
+
+def inverse64_whole(y: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """R^T y = s * H_d y / sqrt(d) over the whole vector, fp64."""
+    y = np.asarray(y, np.float64)
+    h, _ = fwht_stages(y, np.float64)
+    return h / np.sqrt(y.shape[-1]) * np.asarray(s, np.float64)

@@ -25,7 +25,8 @@ Other modes:
 
 After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv restoring
 the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
-second sign vector and corrected norm, and ``append_decode`` reports the decode-loop call
+second sign vector and corrected norm, ``prefill_encode_d256`` a head_dim-256 encode in
+the whole-vector and blocked modes, and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
 positions are captured in one HIP graph and replayed, so the figure is GPU time per
@@ -228,6 +229,43 @@ def encode_variants(fa, w, cbk, seed, ks, caches, reps=20) -> dict:
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "flags": "two signs + corrected norm"}
 
 
+def prefill_whole(fa, seed, reps=10) -> dict:
+    """Encode of a prefill-shaped K slice (8 x 8 KV heads x 16384 tokens, head_dim 256,
+    bf16 AR(1) rho 0.9, 512 MiB: larger than the last-level cache) with 4-bit codes,
+    in the whole-vector mode (one 256-point rotation, the d = 256 codebook, one norm
+    per vector) and in the blocked mode (two 128-blocks), for comparison."""
+    import torch
+    import workloads
+    w = workloads.WORKLOADS["prefill"]
+    k, v = workloads.make_kv(w, "cuda", tokens=16384, batch=8)
+    del v
+    B, H, T, d = k.shape
+    out = {}
+    for mode, cb, flags, nnorm in (("whole", fa.codebook_init(256, 4), fa.WHOLE_VECTOR, 1),
+                                   ("blocked", fa.codebook_init(128, 4), 0, 2)):
+        codes, norms = fa.cache_buffers(B, H, T, d, 4)
+        norms = norms[..., :nnorm].contiguous()
+        call = fa.encode_call(cb, seed, k, codes, norms, flags=flags)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nvec = B * H * T
+        nbytes = nvec * (2 * d + 2 * 64 + 2 * nnorm)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[mode] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
+                     "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del codes, norms
+    del k
+    return out
+
+
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
     """The oracle as it stands, on ``n_slices`` (batch, KV head) slices of the workload
     (default: all of them): encode their K and V blocks in canonical fp32 and run fp64
@@ -390,6 +428,7 @@ def main():
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)
         rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks, caches)
+        rec["prefill_encode_d256"] = prefill_whole(fa, seed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

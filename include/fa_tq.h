@@ -62,10 +62,19 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  *     recon_norm being the norm of the block's centroid values c[code_i] (fp32,
  *     squares summed pairwise as for the input norm), so a decoded block keeps its
  *     input norm up to the fp16 rounding of the stored value.
+ *   FA_TQ_WHOLE_VECTOR (encode and fa_tq_decode_kv only; no other flag): [Spec]
+ *     "Step 1"/"Step 2" read literally, one rotation R = D H_d / sqrt(d) over the
+ *     whole head_dim d (128 or 256) with a codebook built for dim = d, and one fp16
+ *     norm per vector: norms[B][Hkv][T_max] instead of [B][Hkv][T_max][nblk].  The
+ *     codes are packed per consecutive 128 elements exactly as the blocked layout.
+ *     Arithmetic as the blocked mode over d elements (squares summed over index
+ *     bits 0, 1, ... in order, butterflies in stage order 1 .. d/2, c_d =
+ *     fp32(1/sqrt(d))).
  * Entry points without _ex use flags 0.
  */
 #define FA_TQ_TWO_SIGNS 1u
 #define FA_TQ_NORM_CORRECT 2u
+#define FA_TQ_WHOLE_VECTOR 4u
 
 /*
  * Scalar quantizer for one 128-element block ([Spec] "Step 2: Lloyd-Max Scalar
@@ -174,7 +183,7 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
  * stride_h = head_dim, stride_t = hidden with batch 1.
  *   codes, norms: device, SoA layout above (T_max = t_max, Hkv = n_kv_heads).
  *   out: device, 16-byte aligned; strides non-negative multiples of 8 elements.
- * flags: 0 or FA_TQ_TWO_SIGNS (the rotation the cache was encoded with).
+ * flags: 0, FA_TQ_TWO_SIGNS or FA_TQ_WHOLE_VECTOR (how the cache was encoded).
  * batch, n_kv_heads or n_tokens == 0 is an OK no-op; n_tokens <= t_max.
  */
 fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, uint32_t flags,

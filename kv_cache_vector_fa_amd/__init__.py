@@ -87,6 +87,7 @@ for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
 
 TWO_SIGNS = 1       # FA_TQ_TWO_SIGNS: R = D2 H D1 / sqrt(128)
 NORM_CORRECT = 2    # FA_TQ_NORM_CORRECT: stored norm n / ||c[codes]|| (encode)
+WHOLE_VECTOR = 4    # FA_TQ_WHOLE_VECTOR: one rotation over head_dim, one norm per vector
 
 
 def _with_flags(lib, name, args, flags, seed_at):
@@ -199,6 +200,8 @@ def encode(cb: Codebook, seed: int, x, t_max: int | None = None, t0=None, codes=
     t_max = T if t_max is None else t_max
     if codes is None or norms is None:
         codes, norms = cache_buffers(B, H, t_max, d, cb.bits, x.device)
+        if flags & WHOLE_VECTOR:        # one norm per vector
+            norms = norms[..., :1].contiguous()
     encode_call(cb, seed, x, codes, norms, t_max, t0, stream, flags)()
     return codes, norms
 
@@ -229,7 +232,8 @@ def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None
     n_tokens = t_max if n_tokens is None else n_tokens
     if cbytes != code_bytes(cb.bits):
         raise ValueError(f"code rows of {cbytes} bytes for {cb.bits}-bit codes")
-    if not codes.is_contiguous() or tuple(norms.shape) != (B, H, t_max, nblk) or \
+    nnorm = 1 if flags & WHOLE_VECTOR else nblk
+    if not codes.is_contiguous() or tuple(norms.shape) != (B, H, t_max, nnorm) or \
             not norms.is_contiguous():
         raise ValueError("codes/norms must be the contiguous packed cache")
     if out is None:

@@ -710,6 +710,185 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-vector mode ([Spec] "Step 1": one d x d rotation, d = head_dim a power of
+// two; "Step 2": the codebook of that dimension; one norm per vector).  One
+// wavefront per vector, lane l holding elements E l .. E l + E - 1 (E = d / 64):
+// index bits below log2(E) in-lane, the six above across lanes (lane bit k = index
+// bit log2(E) + k).  Canonical fp32 order as the blocked mode: squares summed over
+// index bits 0, 1, ... in order, butterflies in stage order 1, 2, ..., d/2,
+// g = RN32(c_d / n32) with c_d = RN32(1/sqrt(d)), u = RN32(h g).  Codes are packed
+// per consecutive 128 elements exactly as the blocked layout.
+
+// Sign of element e from a flat bit array (bit e set: -1).
+__device__ __forceinline__ uint32_t flat_bits(const FlatSigns& fs, int e, int n) {
+  return (fs.bits[e >> 5] >> (e & 31)) & ((1u << n) - 1u);
+}
+
+// In-wave Walsh-Hadamard butterflies (unnormalized) of a vector held E per lane.
+template <int E>
+__device__ __forceinline__ void fwht_wave(float (&v)[E], int lane) {
+#pragma unroll
+  for (int L = 1; L < E; L <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if ((i & L) == 0) {
+        const float x = v[i], y = v[i + L];
+        v[i] = x + y;
+        v[i + L] = x - y;
+      }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool up = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float p = __shfl_xor(v[i], m, 64);
+      v[i] = up ? p - v[i] : v[i] + p;
+    }
+  }
+}
+
+// Store fields of W bits, (code_i & mask) >> shift for the lane's E codes, LSB-first
+// from element el of a 128-block row; lanes pair up through shuffles when one lane
+// holds less than a byte (all lanes take part in the shuffles).
+template <int W, int E>
+__device__ __forceinline__ void put_fields(uint8_t* row, int el, const uint32_t (&code)[E],
+                                           uint32_t mask, int shift, int lane) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) f |= ((code[i] & mask) >> shift) << (W * i);
+  constexpr int bits = W * E;
+  if constexpr (bits >= 8) {
+#pragma unroll
+    for (int k = 0; k < bits / 8; ++k) row[(el * W) / 8 + k] = static_cast<uint8_t>(f >> (8 * k));
+  } else {
+    constexpr int group = 8 / bits;
+    uint32_t acc = f;
+#pragma unroll
+    for (int k = 1; k < group; ++k)
+      acc |= static_cast<uint32_t>(__shfl_down(static_cast<int>(f), k, 64)) << (bits * k);
+    if (lane % group == 0) row[(el * W) / 8] = static_cast<uint8_t>(acc);
+  }
+}
+
+template <int BITS, bool BF16, int E>
+__global__ void __launch_bounds__(kThreads) encode_whole_kernel(EncodeLaunch a, KTable tab,
+                                                                FlatSigns fs) {
+  constexpr int D = 64 * E;
+  constexpr int CB = code_bytes_of<BITS>();
+  __shared__ uint2 cells[kCells];
+  __shared__ float bext[16];
+  fill_cells(cells, bext, tab);
+  lds_barrier();
+  const int lane = threadIdx.x & 63;
+  const uint32_t sgn = flat_bits(fs, E * lane, E);
+  constexpr float c_d = D == 128 ? kInvSqrtQK : 0.0625f;   // RN32(1/sqrt(d)), d = 128 or 256
+  const int64_t nvec = static_cast<int64_t>(a.batch) * a.heads * a.tokens;
+  const int64_t wave0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  const int64_t nwave = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  for (int64_t vec = wave0; vec < nvec; vec += nwave) {
+    const int64_t row = vec / a.tokens;
+    const int t = static_cast<int>(vec - row * a.tokens);
+    const int64_t b = row / a.heads, h = row - b * a.heads;
+    const int64_t tt = static_cast<int64_t>(a.t0 ? a.t0[b] : 0) + t;
+    if (tt < 0 || tt >= a.t_max) continue;   // uniform over the wavefront
+    const int64_t xo = b * a.sb + h * a.sh + static_cast<int64_t>(t) * a.st + E * lane;
+    float x[E];
+    if constexpr (BF16) {
+      const uint16_t* xp = static_cast<const uint16_t*>(a.x) + xo;
+#pragma unroll
+      for (int i = 0; i < E; ++i) x[i] = __uint_as_float(static_cast<uint32_t>(xp[i]) << 16);
+    } else {
+      const float* xp = static_cast<const float*>(a.x) + xo;
+#pragma unroll
+      for (int i = 0; i < E; ++i) x[i] = xp[i];
+    }
+    // canonical norm: pairwise over the in-lane bits, then across lanes
+    float q[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) q[i] = x[i] * x[i];
+#pragma unroll
+    for (int L = 1; L < E; L <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; i += 2 * L) q[i] = q[i] + q[i + L];
+    float ss = q[0];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ss = ss + __shfl_xor(ss, m, 64);
+    const float n32 = __builtin_sqrtf(ss);
+#pragma unroll
+    for (int i = 0; i < E; ++i) x[i] = flip_sign(x[i], (sgn >> i) & 1u);
+    fwht_wave<E>(x, lane);
+    const float g = n32 > 0.0f ? c_d / n32 : 0.0f;
+    uint32_t code[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float u = x[i] * g;
+      const uint32_t off = (__float_as_uint(u) >> (kCellShift - 3)) & ((kCells - 1u) << 3);
+      const uint2 cell = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cells) + off);
+      code[i] = cell.y + (u > __uint_as_float(cell.x) ? 1u : 0u);
+    }
+    // element e = E lane + i sits in 128-block e / 128 at offset e % 128
+    const int e0 = E * lane, blk = e0 >> 7, el = e0 & 127;
+    uint8_t* crow = a.codes + ((row * a.t_max + tt) * (D / QK) + blk) * CB;
+    if constexpr (BITS == 4) {
+      put_fields<4, E>(crow, el, code, 15u, 0, lane);
+    } else if constexpr (BITS == 2) {
+      put_fields<2, E>(crow, el, code, 3u, 0, lane);
+    } else {
+      put_fields<2, E>(crow, el, code, 3u, 0, lane);        // low two bits
+      put_fields<1, E>(crow + 32, el, code, 4u, 2, lane);   // high bit plane
+    }
+    if (lane == 0) a.norms[row * a.t_max + tt] = __half_as_ushort(__float2half_rn(n32));
+  }
+}
+
+template <int BITS, bool BF16_OUT, int E>
+__global__ void __launch_bounds__(kThreads) decode_whole_kernel(DecodeLaunch d, KTable tab,
+                                                                FlatSigns fs) {
+  constexpr int D = 64 * E;
+  constexpr int CB = code_bytes_of<BITS>();
+  __shared__ float cent[16];
+  if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const uint32_t sgn = flat_bits(fs, E * lane, E);
+  constexpr float c_d = D == 128 ? kInvSqrtQK : 0.0625f;
+  const int64_t nvec = d.rows * d.tokens;
+  const int64_t wave0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  const int64_t nwave = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  const int e0 = E * lane, blk = e0 >> 7, el = e0 & 127;
+  for (int64_t vec = wave0; vec < nvec; vec += nwave) {
+    const int64_t row = vec / d.tokens;
+    const int64_t t = vec - row * d.tokens;
+    const uint8_t* crow = d.codes + ((row * d.t_max + t) * (D / QK) + blk) * CB;
+    const float n = __half2float(__ushort_as_half(d.norms[row * d.t_max + t]));
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int p = el + i;
+      uint32_t c;
+      if constexpr (BITS == 4) c = (crow[p >> 1] >> (4 * (p & 1))) & 15u;
+      else if constexpr (BITS == 2) c = (crow[p >> 2] >> (2 * (p & 3))) & 3u;
+      else c = ((crow[p >> 2] >> (2 * (p & 3))) & 3u) | (((crow[32 + (p >> 3)] >> (p & 7)) & 1u) << 2);
+      v[i] = n * cent[c];
+    }
+    fwht_wave<E>(v, lane);
+    const int64_t b = row / d.heads, h = row - b * d.heads;
+    const int64_t eo = b * d.sb + h * d.sh + t * d.st + e0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = flip_sign(v[i] * c_d, (sgn >> i) & 1u);
+    if constexpr (BF16_OUT) {
+      uint16_t* o = static_cast<uint16_t*>(d.out) + eo;
+#pragma unroll
+      for (int i = 0; i < E; ++i) o[i] = static_cast<uint16_t>(bf16_rne(v[i]));
+    } else {
+      float* o = static_cast<float*>(d.out) + eo;
+#pragma unroll
+      for (int i = 0; i < E; ++i) o[i] = v[i];
+    }
+  }
+}
+
 int grid_for(int64_t blocks) {
   const int64_t quads_per_wg = kThreads / 4;
   int64_t g = (blocks + quads_per_wg - 1) / quads_per_wg;
@@ -789,6 +968,49 @@ hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWor
     }
   }
 #undef FATQ_DEC
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_whole(const EncodeLaunch& a, const KTable& tab, const FlatSigns& fs,
+                               int head_dim, hipStream_t stream) {
+  const int64_t nvec = static_cast<int64_t>(a.batch) * a.heads * a.tokens;
+  const dim3 grid(grid_for(nvec * 4)), block(kThreads);   // 4 vectors per workgroup pass
+#define FATQ_ENCW(B, F, E) \
+  hipLaunchKernelGGL((encode_whole_kernel<B, F, E>), grid, block, 0, stream, a, tab, fs)
+#define FATQ_ENCW_BITS(F, E)          \
+  switch (tab.bits) {                 \
+    case 2: FATQ_ENCW(2, F, E); break; \
+    case 3: FATQ_ENCW(3, F, E); break; \
+    default: FATQ_ENCW(4, F, E); break; \
+  }
+  if (head_dim == 128) {
+    if (a.x_is_bf16) { FATQ_ENCW_BITS(true, 2) } else { FATQ_ENCW_BITS(false, 2) }
+  } else {
+    if (a.x_is_bf16) { FATQ_ENCW_BITS(true, 4) } else { FATQ_ENCW_BITS(false, 4) }
+  }
+#undef FATQ_ENCW_BITS
+#undef FATQ_ENCW
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_whole(const DecodeLaunch& d, const KTable& tab, const FlatSigns& fs,
+                               int head_dim, hipStream_t stream) {
+  const dim3 grid(grid_for(d.rows * d.tokens * 4)), block(kThreads);
+#define FATQ_DECW(B, F, E) \
+  hipLaunchKernelGGL((decode_whole_kernel<B, F, E>), grid, block, 0, stream, d, tab, fs)
+#define FATQ_DECW_BITS(F, E)          \
+  switch (tab.bits) {                 \
+    case 2: FATQ_DECW(2, F, E); break; \
+    case 3: FATQ_DECW(3, F, E); break; \
+    default: FATQ_DECW(4, F, E); break; \
+  }
+  if (head_dim == 128) {
+    if (d.out_bf16) { FATQ_DECW_BITS(true, 2) } else { FATQ_DECW_BITS(false, 2) }
+  } else {
+    if (d.out_bf16) { FATQ_DECW_BITS(true, 4) } else { FATQ_DECW_BITS(false, 4) }
+  }
+#undef FATQ_DECW_BITS
+#undef FATQ_DECW
   return hipGetLastError();
 }
 

@@ -159,10 +159,34 @@ fatq::SignWords make_sign_words(uint64_t seed, int head_dim, bool two = false) {
   return sw;
 }
 
+fatq::FlatSigns make_flat_signs(uint64_t seed, int head_dim) {
+  std::vector<int8_t> s(head_dim);
+  make_signs(seed, head_dim, s.data());
+  fatq::FlatSigns fs;
+  std::memset(&fs, 0, sizeof(fs));
+  for (int e = 0; e < head_dim; ++e)
+    if (s[e] < 0) fs.bits[e >> 5] |= 1u << (e & 31);
+  return fs;
+}
+
+// Whole-vector mode: head_dim 128 or 256, a 2-4 bit codebook of that dimension.
+fa_tq_status check_whole(const fa_tq_codebook* cb, int32_t head_dim, const char* who) {
+  if (head_dim != 128 && head_dim != 256)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: whole-vector mode for head_dim 128 or 256 (got %d)",
+                who, head_dim);
+  if (cb && cb->bits == 8)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: whole-vector mode needs a 2-4 bit codebook", who);
+  return ok();
+}
+
 // Flags of the _ex entry points.  Encode takes both; decode and attention take the
 // rotation flag only (the corrected norm is a property of the stored norms).
 fa_tq_status check_flags(uint32_t flags, uint32_t allowed, const fa_tq_codebook* cb,
                          const char* who) {
+  if ((flags & FA_TQ_WHOLE_VECTOR) && !(allowed & FA_TQ_WHOLE_VECTOR))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: the whole-vector mode has encode and decode only", who);
+  if ((flags & FA_TQ_WHOLE_VECTOR) && (flags & ~FA_TQ_WHOLE_VECTOR))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: the whole-vector mode takes no other flag", who);
   if (flags & ~allowed) return fail(FA_TQ_EINVAL, "%s: unknown flags 0x%x", who, flags & ~allowed);
   if ((flags & FA_TQ_NORM_CORRECT) && cb && cb->bits == 8)
     return fail(FA_TQ_EUNSUPPORTED, "%s: the corrected norm needs a 2-4 bit codebook", who);
@@ -180,11 +204,11 @@ fa_tq_status check_flags(uint32_t flags, uint32_t allowed, const fa_tq_codebook*
 }
 
 fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool allow8,
-                            fatq::KTable* tab) {
+                            fatq::KTable* tab, int32_t dim = fatq::QK) {
   if (!cb) return fail(FA_TQ_EINVAL, "%s: codebook pointer is NULL", what);
-  if (cb->dim != fatq::QK)
-    return fail(FA_TQ_EINVAL, "%s: codebook dim %d, tables are per 128-element block", what,
-                cb->dim);
+  if (cb->dim != dim)
+    return fail(FA_TQ_EINVAL, "%s: codebook dim %d, expected %d (the transform length)", what,
+                cb->dim, dim);
   const int bits = cb->bits;
   if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8))
     return fail(FA_TQ_EINVAL, "%s: bits %d not in {2, 3, 4, 8}", what, bits);
@@ -248,9 +272,12 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
                           const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
                           void* stream, bool ring, bool check_only = false) {
   fatq::KTable tab;
-  fa_tq_status st = check_codebook(cb, who, true, &tab);
+  const bool whole = (flags & FA_TQ_WHOLE_VECTOR) != 0;
+  fa_tq_status st = check_flags(
+      flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT | (ring ? 0u : FA_TQ_WHOLE_VECTOR), cb, who);
   if (st != FA_TQ_OK) return st;
-  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT, cb, who)) != FA_TQ_OK)
+  if (whole && (st = check_whole(cb, head_dim, who)) != FA_TQ_OK) return st;
+  if ((st = check_codebook(cb, who, true, &tab, whole ? head_dim : fatq::QK)) != FA_TQ_OK)
     return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
@@ -290,6 +317,12 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   a.codes = codes;
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
+  if (whole) {
+    const fatq::FlatSigns fs = make_flat_signs(seed, head_dim);
+    return launched(fatq::launch_encode_whole(a, tab, fs, head_dim,
+                                              static_cast<hipStream_t>(stream)),
+                    who);
+  }
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
   return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0,
                                       static_cast<hipStream_t>(stream)),
@@ -482,10 +515,11 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
                              fa_tq_layout out_layout, void* stream) {
   static const char* who = "fa_tq_decode_kv";
   fatq::KTable tab;
-  fa_tq_status st = check_codebook(cb, who, true, &tab);
+  const bool whole = (flags & FA_TQ_WHOLE_VECTOR) != 0;
+  fa_tq_status st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_WHOLE_VECTOR, nullptr, who);
   if (st != FA_TQ_OK) return st;
-  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS, nullptr, who)) != FA_TQ_OK) return st;
-  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT, cb, who)) != FA_TQ_OK)
+  if (whole && (st = check_whole(cb, head_dim, who)) != FA_TQ_OK) return st;
+  if ((st = check_codebook(cb, who, true, &tab, whole ? head_dim : fatq::QK)) != FA_TQ_OK)
     return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
@@ -514,6 +548,12 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
   d.sh = out_layout.stride_h;
   d.st = out_layout.stride_t;
   d.out_bf16 = out_dtype == FA_TQ_BF16;
+  if (whole) {
+    const fatq::FlatSigns fs = make_flat_signs(seed, head_dim);
+    return launched(fatq::launch_decode_whole(d, tab, fs, head_dim,
+                                              static_cast<hipStream_t>(stream)),
+                    who);
+  }
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
   return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)), who);
 }

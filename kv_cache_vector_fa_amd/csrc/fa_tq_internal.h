@@ -31,6 +31,11 @@ struct KTable {
   int32_t bits;
 };
 
+// Signs of a whole vector as a flat bit array: bit e set when element e is negated.
+struct FlatSigns {
+  uint32_t bits[FA_TQ_MAX_HEAD_DIM / 32];
+};
+
 // fp32 nearest to 1/sqrt(128) (the scale of [Spec] Step 1), and the 8-bit grid
 // constant fp32(kInvSqrtQK * 127.5).
 constexpr float kInvSqrtQK = static_cast<float>(0.08838834764831845);
@@ -64,6 +69,13 @@ struct DecodeLaunch {
 
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          hipStream_t stream);
+
+// Whole-vector mode (one rotation over head_dim = 128 or 256, one norm per vector,
+// norms[rows][t_max]); codes as the blocked layout.
+hipError_t launch_encode_whole(const EncodeLaunch& a, const KTable& tab, const FlatSigns& fs,
+                               int head_dim, hipStream_t stream);
+hipError_t launch_decode_whole(const DecodeLaunch& d, const KTable& tab, const FlatSigns& fs,
+                               int head_dim, hipStream_t stream);
 
 struct AttnLaunch {
   const void* q;

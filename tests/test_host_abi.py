@@ -147,7 +147,10 @@ def test_variant_flags_validated_before_launch(lib):
     rotation with a codebook that is not mirror symmetric are rejected (no device
     needed); valid flags with an empty batch are an OK no-op."""
     c4, c8 = fa.codebook_init(128, 4), fa.codebook_init(128, 8)
-    assert _encode_ex_raw(lib, c4, 4) == fa.FA_TQ_EINVAL
+    assert _encode_ex_raw(lib, c4, 8) == fa.FA_TQ_EINVAL
+    # whole-vector mode: no other flag, head_dim 128/256, codebook of that dimension
+    assert _encode_ex_raw(lib, c4, fa.WHOLE_VECTOR | fa.TWO_SIGNS) == fa.FA_TQ_EUNSUPPORTED
+    assert _encode_ex_raw(lib, c8, fa.WHOLE_VECTOR) == fa.FA_TQ_EUNSUPPORTED
     assert _encode_ex_raw(lib, c8, fa.NORM_CORRECT) == fa.FA_TQ_EUNSUPPORTED
     b = np.array(c4.boundaries[:15], np.float32)
     c = np.array(c4.centroids[:16], np.float32)
@@ -162,6 +165,15 @@ def test_variant_flags_validated_before_launch(lib):
     assert lib.fa_tq_decode_kv(ctypes.byref(c4), 42, fa.NORM_CORRECT, 128, P, P, 1, 1, 1, 1, P,
                                fa.FA_TQ_BF16, lay, None) == fa.FA_TQ_EINVAL
     c2 = fa.codebook_init(128, 2)
+    assert lib.fa_tq_attn_decode_ex(ctypes.byref(c4), ctypes.byref(c2), 42, fa.WHOLE_VECTOR, 128,
+                                    P, 1, P, P, P, P, P, 1, 32, 8, 64, 0.088, P, P, 1 << 40,
+                                    None) == fa.FA_TQ_EUNSUPPORTED
+    c256 = fa.codebook_init(256, 4)
+    lay256 = fa.Layout(0, 256, 256)
+    assert lib.fa_tq_decode_kv(ctypes.byref(c4), 42, fa.WHOLE_VECTOR, 256, P, P, 1, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay256, None) == fa.FA_TQ_EINVAL   # dim 128 table
+    assert lib.fa_tq_decode_kv(ctypes.byref(c256), 42, fa.WHOLE_VECTOR, 512, P, P, 1, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay256, None) == fa.FA_TQ_EUNSUPPORTED
     assert lib.fa_tq_attn_decode_ex(ctypes.byref(c4), ctypes.byref(c2), 42, fa.NORM_CORRECT, 128,
                                     P, 1, P, P, P, P, P, 1, 32, 8, 64, 0.088, P, P, 1 << 40,
                                     None) == fa.FA_TQ_EINVAL

@@ -176,70 +176,56 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// bext: 16 floats of LDS for the boundaries followed by +inf.  Cells whose exponent
-// lies outside the boundaries' exponent range hold no boundary and their base
-// follows from the sign alone; only the few cells inside the range (and the +0
-// cell) count boundaries.
 // Entry of cell c: (threshold, base) or, for the corrected norm, (threshold, base,
 // c[base]^2, c[base + 1]^2) so that the chosen code's squared centroid comes with the
 // compare.
-__device__ __forceinline__ void set_cell(uint2* cells, uint32_t c, float thr, uint32_t base,
-                                         const KTable&) {
-  cells[c] = make_uint2(__float_as_uint(thr), base);
+__device__ __forceinline__ void set_cell(uint2* cells, uint32_t c, uint4 e) {
+  cells[c] = make_uint2(e.x, e.y);
 }
-__device__ __forceinline__ void set_cell(uint4* cells, uint32_t c, float thr, uint32_t base,
-                                         const KTable& t) {
-  const float c0 = t.c[base], c1 = t.c[base + 1 < 16 ? base + 1 : 15];
-  cells[c] = make_uint4(__float_as_uint(thr), base, __float_as_uint(c0 * c0),
-                        __float_as_uint(c1 * c1));
-}
+__device__ __forceinline__ void set_cell(uint4* cells, uint32_t c, uint4 e) { cells[c] = e; }
 
+// Fill the 2048 cells.  Cells whose exponent lies outside [emin, emax] (the nonzero
+// boundaries' range) hold no boundary and take one of four host-made entries by
+// sign and side; the few inside it, and the +0 cell, count the boundaries below
+// their smallest member.  Everything read from the codebook is uniform, so it
+// arrives in one batch of scalar loads.
 template <typename Cell>
-__device__ __forceinline__ void fill_cells(Cell* cells, float* bext, const KTable& t) {
-  const int nb = t.nb;
-  if (threadIdx.x < 16) bext[threadIdx.x] = static_cast<int>(threadIdx.x) < nb ? t.b[threadIdx.x] : INFINITY;
-  // Exponent range of the nonzero boundaries, and how many boundaries are < 0 / <= 0
-  // (uniform values).
-  uint32_t emin = 0xFFu, emax = 0u, nneg = 0u, nle0 = 0u;
+__device__ __forceinline__ void fill_cells(Cell* cells, const KTable& t) {
+  float b[15], c[16];
 #pragma unroll
-  for (int m = 0; m < 15; ++m) {
-    if (m < nb) {
-      const float bm = t.b[m];
-      const uint32_t e = (__float_as_uint(bm) >> 23) & 0xFFu;
-      if (bm != 0.0f) {
-        emin = e < emin ? e : emin;
-        emax = e > emax ? e : emax;
+  for (int m = 0; m < 15; ++m) b[m] = t.b[m];   // +inf past the last boundary
+#pragma unroll
+  for (int m = 0; m < 16; ++m) c[m] = t.c[m];
+  const uint32_t emin = t.emin, emax = t.emax;
+  auto out = [&](int k) {
+    return make_uint4(t.cell_out[k][0], t.cell_out[k][1], t.cell_out[k][2], t.cell_out[k][3]);
+  };
+  const uint4 below_pos = out(0), below_neg = out(1), above_pos = out(2), above_neg = out(3);
+  for (uint32_t cc = threadIdx.x; cc < kCells; cc += blockDim.x) {
+    const uint32_t e = (cc >> 2) & 0xFFu;
+    const bool neg = cc >= kNegCell;
+    uint4 ent;
+    if ((e >= emin && e <= emax) || cc == 0) {
+      const uint32_t lo = cc << kCellShift;
+      const float umin = __uint_as_float(neg ? (lo | ((1u << kCellShift) - 1u)) : lo);
+      // boundaries ascend: the last one below umin fixes base, threshold and centroids
+      uint32_t base = 0;
+      float thr = b[0], c0 = c[0], c1 = c[1];
+#pragma unroll
+      for (int m = 0; m < 15; ++m) {
+        const bool below = b[m] < umin;
+        base += below ? 1u : 0u;
+        thr = below ? (m + 1 < 15 ? b[m + 1] : INFINITY) : thr;
+        c0 = below ? c[m + 1] : c0;
+        c1 = below ? c[m + 2 < 16 ? m + 2 : 15] : c1;
       }
-      nneg += bm < 0.0f ? 1u : 0u;
-      nle0 += bm <= 0.0f ? 1u : 0u;
+      ent = make_uint4(__float_as_uint(thr), base, __float_as_uint(c0 * c0),
+                       __float_as_uint(c1 * c1));
+    } else {
+      const uint4 lo = neg ? below_neg : below_pos, hi = neg ? above_neg : above_pos;
+      ent = e < emin ? lo : hi;
     }
-  }
-  if (emin > emax) emin = emax = 0;   // no nonzero boundary: only the +0 cell counts
-  lds_barrier();
-  // cells outside the range
-  for (uint32_t c = threadIdx.x; c < kCells; c += blockDim.x) {
-    const uint32_t e = (c >> 2) & 0xFFu;
-    if ((e >= emin && e <= emax) || c == 0) continue;
-    const bool neg = c >= kNegCell;
-    const uint32_t base = e < emin ? (neg ? nneg : nle0) : (neg ? 0u : static_cast<uint32_t>(nb));
-    set_cell(cells, c, bext[base], base, t);
-  }
-  // cells inside the range (4 per exponent and sign) and the +0 cell: count the
-  // boundaries below the smallest member
-  const uint32_t per_sign = 4 * (emax - emin + 1);
-  for (uint32_t i = threadIdx.x; i < 2 * per_sign + 1; i += blockDim.x) {
-    uint32_t c;
-    if (i == 2 * per_sign) c = 0;
-    else c = (i < per_sign ? 0u : kNegCell) + 4 * emin + (i % per_sign);
-    if (c == 0 && i != 2 * per_sign) continue;   // +0 cell handled once
-    const bool neg = c >= kNegCell;
-    const uint32_t lo = c << kCellShift;
-    const float umin = __uint_as_float(neg ? (lo | ((1u << kCellShift) - 1u)) : lo);
-    uint32_t base = 0;
-#pragma unroll
-    for (int m = 0; m < 15; ++m)
-      if (m < nb) base += t.b[m] < umin ? 1u : 0u;
-    set_cell(cells, c, bext[base], base, t);
+    set_cell(cells, cc, ent);
   }
 }
 
@@ -454,18 +440,53 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   constexpr int CB = code_bytes_of<BITS>();
   typedef typename std::conditional<NC, uint4, uint2>::type Cell;
   __shared__ Cell cells[BITS == 8 ? 1 : kCells];
-  __shared__ float bext[16];
-  if constexpr (BITS != 8) {
-    fill_cells(cells, bext, tab);
-    lds_barrier();
-  }
   const int q = threadIdx.x & 3;
   const uint32_t f0 = blockIdx.x * (kEncThreads / 4) + (threadIdx.x >> 2);
   const uint32_t nblk = static_cast<uint32_t>(a.nblk);
   const int j = static_cast<int>(f0 % nblk);
   const int t_first = static_cast<int>(f0 / nblk);
   const int t_step = static_cast<int>(gridDim.x * (kEncThreads / 4) / nblk);
+  const int rows = a.batch * a.heads;
+  constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
+  const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + QK * a.nblk) * ES);
+  const uint32_t cbytes = static_cast<uint32_t>(a.t_max) * a.nblk * CB;
+  const uint32_t nbytes = static_cast<uint32_t>(a.t_max) * a.nblk * 2;
+  struct Row {
+    Rsrc rx, rc, rn;
+    int tbase;
+  };
+  auto open_row = [&](int row) {
+    const int b = row / a.heads;
+    const int h = row - b * a.heads;
+    Row r;
+    r.tbase = a.t0 ? a.t0[b] : 0;
+    r.rx = make_rsrc(static_cast<const char*>(a.x) + (b * a.sb + h * a.sh) * ES, xbytes);
+    const int64_t crow = static_cast<int64_t>(row) * a.t_max * a.nblk;
+    r.rc = make_rsrc(a.codes + crow * CB, cbytes);
+    r.rn = make_rsrc(a.norms + crow, nbytes);
+    return r;
+  };
+  // byte offset of block (t, j) in the input row; kOOB past the last token
+  auto xoff = [&](int t) {
+    return t < a.tokens ? static_cast<uint32_t>((t * a.st + QK * j) * ES) : kOOB;
+  };
+
+  // The per-lane sign words (kernel arguments read through vector loads) and the
+  // first block's input go out before the cell table is filled; nothing waits for
+  // them until the fill is done.
+  int row = blockIdx.y;
+  if (row >= rows) return;   // uniform over the workgroup
   const uint32_t sbits = sw.w[j][q];
+  const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;
+  Row R = open_row(row);
+  int t = t_first;
+  RawBlock<BF16> ba, bb;
+  load_raw<BF16>(R.rx, xoff(t), q, ba);
+  if constexpr (BITS != 8) {
+    fill_cells(cells, tab);
+    lds_barrier();
+  }
+
   uint32_t smask[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i)
@@ -475,7 +496,6 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   const float mu2 = (q & 2) ? -1.0f : 1.0f;
   const uint32_t carried = ((q ^ (q >> 1)) & 1u) << 31;
   // second sign vector: code mirror masks per chunk (zero without it)
-  const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;
   uint32_t mirror[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -484,164 +504,151 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
                                                               : mirror_mask<4>(b8, 15u);
   }
 
-  const int rows = a.batch * a.heads;
-  constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
-  const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + QK * a.nblk) * ES);
-  const uint32_t cbytes = static_cast<uint32_t>(a.t_max) * a.nblk * CB;
-  const uint32_t nbytes = static_cast<uint32_t>(a.t_max) * a.nblk * 2;
-  for (int row = blockIdx.y; row < rows; row += gridDim.y) {
-    const int b = row / a.heads;
-    const int h = row - b * a.heads;
-    const int tbase = a.t0 ? a.t0[b] : 0;
-    const Rsrc rx = make_rsrc(static_cast<const char*>(a.x) + (b * a.sb + h * a.sh) * ES, xbytes);
-    const int64_t crow = static_cast<int64_t>(row) * a.t_max * a.nblk;
-    const Rsrc rc = make_rsrc(a.codes + crow * CB, cbytes);
-    const Rsrc rn = make_rsrc(a.norms + crow, nbytes);
-    // byte offset of block (t, j) in the input row; kOOB past the last token
-    auto xoff = [&](int t) {
-      return t < a.tokens ? static_cast<uint32_t>((t * a.st + QK * j) * ES) : kOOB;
-    };
-    auto process = [&](const RawBlock<BF16>& cur, int t) {
-      float x[4][8], p[4];
-      widen<BF16>(cur, smask, sbits, x, p);
-      // canonical norm: levels 3-4 across the quad, 5-6 across chunks
+
+  auto process = [&](const RawBlock<BF16>& cur, int t) {
+    float x[4][8], p[4];
+    widen<BF16>(cur, smask, sbits, x, p);
+    // canonical norm: levels 3-4 across the quad, 5-6 across chunks
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p[k] = quad_add<0xB1>(p[k]);
+    for (int k = 0; k < 4; ++k) p[k] = quad_add<0xB1>(p[k]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p[k] = quad_add<0x4E>(p[k]);
-      const float n32 = __builtin_sqrtf((p[0] + p[1]) + (p[2] + p[3]));
-      // Walsh-Hadamard butterflies, stages 1, 2, 4 (in-chunk), 8, 16 (across the
-      // quad), 32, 64 (across chunks)
+    for (int k = 0; k < 4; ++k) p[k] = quad_add<0x4E>(p[k]);
+    const float n32 = __builtin_sqrtf((p[0] + p[1]) + (p[2] + p[3]));
+    // Walsh-Hadamard butterflies, stages 1, 2, 4 (in-chunk), 8, 16 (across the
+    // quad), 32, 64 (across chunks)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bfly(x[k][0], x[k][1]); bfly(x[k][2], x[k][3]);
+      bfly(x[k][4], x[k][5]); bfly(x[k][6], x[k][7]);
+      bfly(x[k][0], x[k][2]); bfly(x[k][1], x[k][3]);
+      bfly(x[k][4], x[k][6]); bfly(x[k][5], x[k][7]);
+      bfly(x[k][0], x[k][4]); bfly(x[k][1], x[k][5]);
+      bfly(x[k][2], x[k][6]); bfly(x[k][3], x[k][7]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xstage<0xB1>(x[k], mu1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xstage<0x4E>(x[k], mu2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bfly(x[0][i], x[1][i]);
+      bfly(x[2][i], x[3][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bfly(x[0][i], x[2][i]);
+      bfly(x[1][i], x[3][i]);
+    }
+
+    // position tbase + t, or its ring slot; 0 <= tbase + t < 2^32 when tbase >= 0
+    int64_t tt = static_cast<int64_t>(R.tbase) + t;
+    if (a.ring && tt >= 0)
+      tt = static_cast<uint32_t>(tt) % static_cast<uint32_t>(a.t_max);
+    const bool valid = t < a.tokens && tt >= 0 && tt < a.t_max;
+    const uint32_t cblk = static_cast<uint32_t>(tt * a.nblk + j);
+    const uint32_t co = valid ? cblk * CB : kOOB;
+    uint16_t nbits;
+    if constexpr (BITS == 8) {
+      // turboq8 grid: per-block absmax scale, codes round((y / s) * 127.5 + 127.5)
+      float amax = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[k][i]));
+      amax = quad_max<0xB1>(amax);
+      amax = quad_max<0x4E>(amax);
+      const __half s16 = __float2half_rn(fp32_value(amax * kInvSqrtQK));
+      const float s32 = __half2float(s16);
+      const float G = __uint_as_float(__float_as_uint(s32 > 0.0f ? kGrid8 / s32 : 0.0f) ^ carried);
+      nbits = __half_as_ushort(s16);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        bfly(x[k][0], x[k][1]); bfly(x[k][2], x[k][3]);
-        bfly(x[k][4], x[k][5]); bfly(x[k][6], x[k][7]);
-        bfly(x[k][0], x[k][2]); bfly(x[k][1], x[k][3]);
-        bfly(x[k][4], x[k][6]); bfly(x[k][5], x[k][7]);
-        bfly(x[k][0], x[k][4]); bfly(x[k][1], x[k][5]);
-        bfly(x[k][2], x[k][6]); bfly(x[k][3], x[k][7]);
-      }
+        uint32_t code[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) xstage<0xB1>(x[k], mu1);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) xstage<0x4E>(x[k], mu2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bfly(x[0][i], x[1][i]);
-        bfly(x[2][i], x[3][i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bfly(x[0][i], x[2][i]);
-        bfly(x[1][i], x[3][i]);
-      }
-
-      // position tbase + t, or its ring slot; 0 <= tbase + t < 2^32 when tbase >= 0
-      int64_t tt = static_cast<int64_t>(tbase) + t;
-      if (a.ring && tt >= 0)
-        tt = static_cast<uint32_t>(tt) % static_cast<uint32_t>(a.t_max);
-      const bool valid = t < a.tokens && tt >= 0 && tt < a.t_max;
-      const uint32_t cblk = static_cast<uint32_t>(tt * a.nblk + j);
-      const uint32_t co = valid ? cblk * CB : kOOB;
-      uint16_t nbits;
-      if constexpr (BITS == 8) {
-        // turboq8 grid: per-block absmax scale, codes round((y / s) * 127.5 + 127.5)
-        float amax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[k][i]));
-        amax = quad_max<0xB1>(amax);
-        amax = quad_max<0x4E>(amax);
-        const __half s16 = __float2half_rn(fp32_value(amax * kInvSqrtQK));
-        const float s32 = __half2float(s16);
-        const float G = __uint_as_float(__float_as_uint(s32 > 0.0f ? kGrid8 / s32 : 0.0f) ^ carried);
-        nbits = __half_as_ushort(s16);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t code[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float t8 = x[k][i] * ((s2bits >> (8 * k + i)) & 1u ? -G : G);
-            const float w = t8 + 127.5f;
-            code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
-          }
-          const uint32_t lo = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
-          const uint32_t hi = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
-          const uint32_t o = co + 8 * (q + 4 * k);
-          __builtin_amdgcn_raw_buffer_store_b32(lo, rc, o, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(hi, rc, o + 4, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          const float t8 = x[k][i] * ((s2bits >> (8 * k + i)) & 1u ? -G : G);
+          const float w = t8 + 127.5f;
+          code[i] = static_cast<uint32_t>(fminf(fmaxf(rintf(w), 0.0f), 255.0f));
         }
-      } else {
-        const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
-        const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
-        float sq[4];
-        auto codes8 = [&](int k) {
-          constexpr int W = BITS == 2 ? 2 : 4;
-          if constexpr (NC) return bucketize8_sq<W>(x[k], g, cells, sq[k]) ^ mirror[k];
-          else return bucketize8<W>(x[k], g, cells) ^ mirror[k];
-        };
+        const uint32_t lo = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
+        const uint32_t hi = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
+        const uint32_t o = co + 8 * (q + 4 * k);
+        __builtin_amdgcn_raw_buffer_store_b32(lo, R.rc, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(hi, R.rc, o + 4, 0, 0);
+      }
+    } else {
+      const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
+      const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
+      float sq[4];
+      auto codes8 = [&](int k) {
+        constexpr int W = BITS == 2 ? 2 : 4;
+        if constexpr (NC) return bucketize8_sq<W>(x[k], g, cells, sq[k]) ^ mirror[k];
+        else return bucketize8<W>(x[k], g, cells) ^ mirror[k];
+      };
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = q + 4 * k;
-          if constexpr (BITS == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(codes8(k), rc, co + 4 * c, 0, 0);
-          } else if constexpr (BITS == 2) {
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(codes8(k)), rc,
-                                                  co + 2 * c, 0, 0);
-          } else {
-            // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
-            const uint32_t w = codes8(k);
-            uint32_t lo = w & 0x33333333u;
-            lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
-            lo = (lo | (lo >> 4)) & 0x00FF00FFu;
-            lo = (lo | (lo >> 8)) & 0x0000FFFFu;
-            uint32_t hi = (w >> 2) & 0x11111111u;
-            hi = (hi | (hi >> 3)) & 0x03030303u;
-            hi = (hi | (hi >> 6)) & 0x000F000Fu;
-            hi = (hi | (hi >> 12)) & 0xFFu;
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(lo), rc, co + 2 * c, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(hi), rc, co + 32 + c, 0, 0);
-          }
-        }
-        if constexpr (NC) {
-          // corrected norm n / ||c[codes]||: squared centroids summed in the input
-          // norm's order (bits 0-2 in the chunk, 3-4 across the quad, 5-6 across chunks)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) sq[k] = quad_add<0xB1>(sq[k]);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) sq[k] = quad_add<0x4E>(sq[k]);
-          const float r32 = __builtin_sqrtf((sq[0] + sq[1]) + (sq[2] + sq[3]));
-          nbits = __half_as_ushort(__float2half_rn(r32 > 0.0f ? n32 / r32 : 0.0f));
+      for (int k = 0; k < 4; ++k) {
+        const int c = q + 4 * k;
+        if constexpr (BITS == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(codes8(k), R.rc, co + 4 * c, 0, 0);
+        } else if constexpr (BITS == 2) {
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(codes8(k)), R.rc,
+                                                co + 2 * c, 0, 0);
         } else {
-          nbits = __half_as_ushort(__float2half_rn(n32));
+          // 3-bit codes in nibbles, then the two planes of [turboq] block_turboq3_0
+          const uint32_t w = codes8(k);
+          uint32_t lo = w & 0x33333333u;
+          lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
+          lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+          lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+          uint32_t hi = (w >> 2) & 0x11111111u;
+          hi = (hi | (hi >> 3)) & 0x03030303u;
+          hi = (hi | (hi >> 6)) & 0x000F000Fu;
+          hi = (hi | (hi >> 12)) & 0xFFu;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(lo), R.rc, co + 2 * c, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(hi), R.rc, co + 32 + c, 0, 0);
         }
       }
-      __builtin_amdgcn_raw_buffer_store_b16(nbits, rn, valid && q == 0 ? 2 * cblk : kOOB, 0, 0);
-    };
-    // Ping-pong buffers: block t + t_step loads while block t is processed.  The trip
-    // count is uniform over the wavefront (lane 0 holds its smallest t); lanes past the
-    // last token load zeros and store nothing.
-    // The stores of one block go to offsets past every range here (dropped by the
-    // hardware) after the first load: the loop is then entered with the same
-    // outstanding-memory pattern as every later iteration (loads, then that block's
-    // stores), so the compiler's wait before each block covers only its own loads.
-    // The scheduling barriers keep each prefetch ahead of the block it overlaps.
-    int t = t_first;
-    RawBlock<BF16> ba, bb;
-    load_raw<BF16>(rx, xoff(t), q, ba);
-    dummy_stores<BITS>(rc, rn);
+      if constexpr (NC) {
+        // corrected norm n / ||c[codes]||: squared centroids summed in the input
+        // norm's order (bits 0-2 in the chunk, 3-4 across the quad, 5-6 across chunks)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sq[k] = quad_add<0xB1>(sq[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sq[k] = quad_add<0x4E>(sq[k]);
+        const float r32 = __builtin_sqrtf((sq[0] + sq[1]) + (sq[2] + sq[3]));
+        nbits = __half_as_ushort(__float2half_rn(r32 > 0.0f ? n32 / r32 : 0.0f));
+      } else {
+        nbits = __half_as_ushort(__float2half_rn(n32));
+      }
+    }
+    __builtin_amdgcn_raw_buffer_store_b16(nbits, R.rn, valid && q == 0 ? 2 * cblk : kOOB, 0, 0);
+  };
+  // Ping-pong buffers: block t + t_step loads while block t is processed.  The trip
+  // count is uniform over the wavefront (lane 0 holds its smallest t); lanes past the
+  // last token load zeros and store nothing.
+  // The stores of one block go to offsets past every range here (dropped by the
+  // hardware) after the first load: the loop is then entered with the same
+  // outstanding-memory pattern as every later iteration (loads, then that block's
+  // stores), so the compiler's wait before each block covers only its own loads.
+  // The scheduling barriers keep each prefetch ahead of the block it overlaps.
+  for (;;) {
+    dummy_stores<BITS>(R.rc, R.rn);
     while (__builtin_amdgcn_readfirstlane(t) < a.tokens) {
-      load_raw<BF16>(rx, xoff(t + t_step), q, bb);
+      load_raw<BF16>(R.rx, xoff(t + t_step), q, bb);
       __builtin_amdgcn_sched_barrier(0);
       process(ba, t);
       t += t_step;
       if (__builtin_amdgcn_readfirstlane(t) >= a.tokens) break;
-      load_raw<BF16>(rx, xoff(t + t_step), q, ba);
+      load_raw<BF16>(R.rx, xoff(t + t_step), q, ba);
       __builtin_amdgcn_sched_barrier(0);
       process(bb, t);
       t += t_step;
     }
+    row += gridDim.y;
+    if (row >= rows) break;
+    R = open_row(row);
+    t = t_first;
+    load_raw<BF16>(R.rx, xoff(t), q, ba);
   }
 }
 
@@ -777,8 +784,7 @@ __global__ void __launch_bounds__(kThreads) encode_whole_kernel(EncodeLaunch a, 
   constexpr int D = 64 * E;
   constexpr int CB = code_bytes_of<BITS>();
   __shared__ uint2 cells[kCells];
-  __shared__ float bext[16];
-  fill_cells(cells, bext, tab);
+  fill_cells(cells, tab);
   lds_barrier();
   const int lane = threadIdx.x & 63;
   const uint32_t sgn = flat_bits(fs, E * lane, E);

@@ -203,6 +203,42 @@ fa_tq_status check_flags(uint32_t flags, uint32_t allowed, const fa_tq_codebook*
   return ok();
 }
 
+// Uniform parameters of the encoder's cell table (see KTable): a cell is the set
+// of fp32 values sharing sign, exponent and two leading mantissa bits; the cells
+// whose exponent lies outside the nonzero boundaries' range hold no boundary, so
+// base = #{j : b_j < any value of the cell} follows from the sign and the side.
+void fill_cell_params(fatq::KTable* tab) {
+  const int nb = tab->nb;
+  for (int j = nb; j < 15; ++j) tab->b[j] = INFINITY;
+  uint32_t emin = 0xFFu, emax = 0u, nneg = 0u, nle0 = 0u;
+  for (int j = 0; j < nb; ++j) {
+    const float bj = tab->b[j];
+    uint32_t u;
+    std::memcpy(&u, &bj, 4);
+    const uint32_t e = (u >> 23) & 0xFFu;
+    if (bj != 0.0f) {
+      emin = e < emin ? e : emin;
+      emax = e > emax ? e : emax;
+    }
+    nneg += bj < 0.0f ? 1u : 0u;
+    nle0 += bj <= 0.0f ? 1u : 0u;
+  }
+  if (emin > emax) emin = emax = 0;   // no nonzero boundary: only the zero cells count
+  tab->emin = emin;
+  tab->emax = emax;
+  const uint32_t bases[4] = {nle0, nneg, static_cast<uint32_t>(nb), 0u};
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t base = bases[k];
+    const float thr = base < static_cast<uint32_t>(nb) ? tab->b[base] : INFINITY;
+    const float c0 = tab->c[base], c1 = tab->c[base + 1 < 16 ? base + 1 : 15];
+    const float q0 = c0 * c0, q1 = c1 * c1;   // fp32 products, as the kernel's
+    std::memcpy(&tab->cell_out[k][0], &thr, 4);
+    tab->cell_out[k][1] = base;
+    std::memcpy(&tab->cell_out[k][2], &q0, 4);
+    std::memcpy(&tab->cell_out[k][3], &q1, 4);
+  }
+}
+
 fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool allow8,
                             fatq::KTable* tab, int32_t dim = fatq::QK) {
   if (!cb) return fail(FA_TQ_EINVAL, "%s: codebook pointer is NULL", what);
@@ -248,6 +284,7 @@ fa_tq_status check_codebook(const fa_tq_codebook* cb, const char* what, bool all
       return fail(FA_TQ_EINVAL, "%s: centroid %d is not finite", what, j);
     tab->c[j] = cb->centroids[j];
   }
+  fill_cell_params(tab);
   return ok();
 }
 

@@ -23,12 +23,19 @@ struct SignWords {
   int32_t two;
 };
 
-// Codebook as the kernels read it (uniform kernel arguments).
+// Codebook as the kernels read it (uniform kernel arguments).  For the 2-4 bit
+// codebooks the host also derives what the encoder's cell table needs: the biased
+// exponent range [emin, emax] of the nonzero boundaries, and the entries of the
+// cells outside that range, which hold no boundary: (threshold, base, c[base]^2,
+// c[base + 1]^2) as fp32 bits for positive cells below the range, negative cells
+// below it, positive cells above it, negative cells above it.
 struct KTable {
-  float b[15];   // boundaries (nb used)
+  float b[15];   // boundaries (nb used, +inf after them)
   float c[16];   // centroids
   int32_t nb;    // levels - 1
   int32_t bits;
+  uint32_t emin, emax;
+  uint32_t cell_out[4][4];
 };
 
 // Signs of a whole vector as a flat bit array: bit e set when element e is negated.

@@ -268,6 +268,11 @@ __device__ __forceinline__ bool sign_bit(const SignWords& sw, int e) {
   const int c = e >> 3;
   return (sw.w[0][c & 3] >> (8 * (c >> 2) + (e & 7))) & 1u;
 }
+// Bit of element e in its sign word (the word sw.w[0][(e >> 3) & 3]).
+__device__ __forceinline__ bool bit_of(uint32_t word, int e) {
+  const int c = e >> 3;
+  return (word >> (8 * (c >> 2) + (e & 7))) & 1u;
+}
 __device__ __forceinline__ bool sign_bit2(const SignWords& sw, int e) {
   const int c = e >> 3;
   return sw.two && ((sw.w2[0][c & 3] >> (8 * (c >> 2) + (e & 7))) & 1u);
@@ -312,8 +317,33 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   const int G = GT > 0 ? GT : a.hq / a.hkv;
   constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
 
+  // ---- loads that need only the kernel arguments go out first (query elements, sign
+  // words and centroids, all indexed per lane), so that waiting for them later
+  // leaves the code loads in flight: wave w rotates heads w and w + 4; lane holds
+  // elements lane and lane + 64 of each
+  // (raw bits here; widened after the loads are waited for)
+  uint32_t qraw[2][2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const int h = wave + kWaves * hs;
+    const int hc = h < G ? h : 0;
+    const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + hc) * QK;
+    if (a.q_is_bf16) {
+      const uint16_t* qb = static_cast<const uint16_t*>(a.q) + qo;
+      qraw[hs][0] = qb[lane];
+      qraw[hs][1] = qb[lane + 64];
+    } else {
+      const uint32_t* qf = static_cast<const uint32_t*>(a.q) + qo;
+      qraw[hs][0] = qf[lane];
+      qraw[hs][1] = qf[lane + 64];
+    }
+  }
+  // sign words of elements lane and lane + 64 (the same word; see sign_bit)
+  const uint32_t sw1 = sw.w[0][(lane >> 3) & 3], sw2 = sw.w2[0][(lane >> 3) & 3];
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- the sequence range, then the first super tile's loads (in flight during setup)
-  const int64_t len64 = a.pos ? static_cast<int64_t>(a.pos[b]) + a.n_new : a.seq_lens[b];
+  const int64_t len64 = static_cast<int64_t>(a.lens[b]) + a.len_add;
   const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
   const int c0 = split * a.chunk;
   const int c1 = min(len, c0 + a.chunk);
@@ -328,31 +358,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   Codes<KB, VB> buf0, buf1;
   issue_loads<KB, VB>(rows, buf0, st, st < c1, lane);
 
-  // ---- query loads: wave w rotates heads w and w + 4; lane holds elements lane and
-  // lane + 64 of each
-  float qx[2][2];
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const int h = wave + kWaves * hs;
-    const int hc = h < G ? h : 0;
-    const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + hc) * QK;
-    if (a.q_is_bf16) {
-      const uint16_t* qb = static_cast<const uint16_t*>(a.q) + qo;
-      qx[hs][0] = __uint_as_float(static_cast<uint32_t>(qb[lane]) << 16);
-      qx[hs][1] = __uint_as_float(static_cast<uint32_t>(qb[lane + 64]) << 16);
-    } else {
-      const float* qf = static_cast<const float*>(a.q) + qo;
-      qx[hs][0] = qf[lane];
-      qx[hs][1] = qf[lane + 64];
-    }
-  }
-
   // ---- centroid splits, then the operand table (thread r fills row r)
-  if (tid < 32) {
-    const int i = tid & 15;
+  {
+    // centroid tid % 16 of the key (tid < 16) or value codebook, selected from the
+    // uniform kernel arguments (straight-line selects: no per-lane argument loads)
+    float c = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float ki = tk.c[i], vi = tv.c[i];
+      c = (tid & 15) == i ? (tid < 16 ? ki : vi) : c;
+    }
     _Float16 hi, lo;
-    split_h(kCScale * (tid < 16 ? tk.c[i] : tv.c[i]), hi, lo);
-    sp[tid >> 4][i] = pack_h2(hi, lo);
+    split_h(kCScale * c, hi, lo);
+    if (tid < 32) sp[tid >> 4][tid & 15] = pack_h2(hi, lo);
   }
   lds_barrier();
   if (tid < 256) {
@@ -387,10 +405,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
 
   // ---- q' = s2 * H (s * q): stride 64 in-lane, strides 32 .. 1 across lanes; the
   // largest |q'| of each head to LDS
+  float qx[2][2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      qx[hs][i] = __uint_as_float(a.q_is_bf16 ? qraw[hs][i] << 16 : qraw[hs][i]);
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
-    float x0 = sign_bit(sw, lane) ? -qx[hs][0] : qx[hs][0];
-    float x1 = sign_bit(sw, lane + 64) ? -qx[hs][1] : qx[hs][1];
+    float x0 = bit_of(sw1, lane) ? -qx[hs][0] : qx[hs][0];
+    float x1 = bit_of(sw1, lane + 64) ? -qx[hs][1] : qx[hs][1];
     float u = x0 + x1, v = x0 - x1;
 #pragma unroll
     for (int L = 32; L >= 1; L >>= 1) {
@@ -399,8 +423,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
       u = up ? pu - u : u + pu;
       v = up ? pv - v : v + pv;
     }
-    qx[hs][0] = sign_bit2(sw, lane) ? -u : u;
-    qx[hs][1] = sign_bit2(sw, lane + 64) ? -v : v;
+    qx[hs][0] = sw.two && bit_of(sw2, lane) ? -u : u;
+    qx[hs][1] = sw.two && bit_of(sw2, lane + 64) ? -v : v;
     float mx = fmaxf(fabsf(u), fabsf(v));
 #pragma unroll
     for (int s2 = 32; s2 >= 1; s2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s2, 64));

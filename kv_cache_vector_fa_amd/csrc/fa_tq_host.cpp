@@ -226,8 +226,9 @@ void fill_cell_params(fatq::KTable* tab) {
   if (emin > emax) emin = emax = 0;   // no nonzero boundary: only the zero cells count
   tab->emin = emin;
   tab->emax = emax;
-  const uint32_t bases[4] = {nle0, nneg, static_cast<uint32_t>(nb), 0u};
-  for (int k = 0; k < 4; ++k) {
+  // the +0 cell: #{b_j < +0} = nneg, and its threshold may be a zero boundary
+  const uint32_t bases[5] = {nle0, nneg, static_cast<uint32_t>(nb), 0u, nneg};
+  for (int k = 0; k < 5; ++k) {
     const uint32_t base = bases[k];
     const float thr = base < static_cast<uint32_t>(nb) ? tab->b[base] : INFINITY;
     const float c0 = tab->c[base], c1 = tab->c[base + 1 < 16 ? base + 1 : 15];
@@ -421,6 +422,8 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   a.seq_lens = seq_lens;
   a.pos = pos;
   a.n_new = n_new;
+  a.lens = pos ? pos : seq_lens;
+  a.len_add = pos ? n_new : 0;
   a.batch = batch;
   a.hq = n_q_heads;
   a.hkv = n_kv_heads;

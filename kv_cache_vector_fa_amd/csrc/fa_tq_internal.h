@@ -28,14 +28,14 @@ struct SignWords {
 // exponent range [emin, emax] of the nonzero boundaries, and the entries of the
 // cells outside that range, which hold no boundary: (threshold, base, c[base]^2,
 // c[base + 1]^2) as fp32 bits for positive cells below the range, negative cells
-// below it, positive cells above it, negative cells above it.
+// below it, positive cells above it, negative cells above it, and the cell of +0.
 struct KTable {
   float b[15];   // boundaries (nb used, +inf after them)
   float c[16];   // centroids
   int32_t nb;    // levels - 1
   int32_t bits;
   uint32_t emin, emax;
-  uint32_t cell_out[4][4];
+  uint32_t cell_out[5][4];
 };
 
 // Signs of a whole vector as a flat bit array: bit e set when element e is negated.
@@ -57,6 +57,7 @@ struct EncodeLaunch {
   uint8_t* codes;
   uint16_t* norms;
   int32_t x_is_bf16;
+  int32_t t_step;        // token stride of one quad (set by the launcher from its grid)
 };
 
 // norm_correct: store n / ||c[codes]|| ([turboq] "Encode pipeline" step 4; bits 2-4).
@@ -94,6 +95,8 @@ struct AttnLaunch {
   const int32_t* seq_lens;   // tokens per sequence, or (when pos is set)
   const int32_t* pos;        //   min(pos[b] + n_new, t_max)
   int32_t n_new;
+  const int32_t* lens;       // set by the launchers: pos ? pos : seq_lens,
+  int32_t len_add;           //   and pos ? n_new : 0 (one load per sequence)
   int32_t batch, hq, hkv, t_max;
   float scale;
   float* out;

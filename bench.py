@@ -12,8 +12,12 @@ the two norms, plus the query and output.  Buffers rotate over several copies so
 that consecutive steps do not find the previous step's data in the 256 MB
 last-level cache.
 
-Per-kernel durations come from HIP events recorded between the launches of every
-timed step (on the stream the library launches on).  The ``roofline.traffic``
+The K timed steps run phase by phase: the K encodes of the K cache back to back, then
+the K encodes of the V cache, then the K attentions, step i's attention reading the
+cache copy its encodes wrote (every copy holds the same codes).  HIP events at the
+phase boundaries (on the stream the library launches on) give each kernel's mean
+launch-to-launch time without the dispatch of a different kernel in between, the
+figure rocprofv3's kernel durations are compared with.  The ``roofline.traffic``
 figure is read from the committed rocprofv3 counter summary in ``profiles/`` when
 the kernel's source file still has the hash recorded there, else it is null.
 
@@ -367,20 +371,19 @@ def main():
         for c in calls:
             c[i % R]()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        for j, c in enumerate(calls):
-            ev[3 * i + j].record()
+    for j, c in enumerate(calls):
+        ev[j].record()
+        for i in range(K):
             c[i % R]()
-    ev[3 * K].record()
+    ev[3].record()
     t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[3 * K]) / K
-    kms = [sum(ev[3 * i + j].elapsed_time(ev[3 * i + j + 1]) for i in range(K)) / K
-           for j in range(3)]
+    ms = ev[0].elapsed_time(ev[3]) / K
+    kms = [ev[j].elapsed_time(ev[j + 1]) / K for j in range(3)]
 
     nblk = B * Hkv * T * (d // 128)
     nbytes = (enc_bytes(nblk, 256, w.k_bits), enc_bytes(nblk, 256, w.v_bits),

@@ -332,6 +332,31 @@ __device__ __forceinline__ float quad_max(float x) {
                       0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false)));
 }
 
+// Whole-vector mode, head_dim 256: the butterfly stage between the vector's two
+// 128-blocks.  Their quads are adjacent and the second holds its chunks in reversed
+// lane order, so lane i and lane 7 - i of a half row hold the same chunk of the two
+// blocks: row_half_mirror is the partner.  v <- v + mu * v(partner) as in xstage.
+__device__ __forceinline__ void xstage_mirror(float (&v)[8], float mu) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+        "+v"(v[6]), "+v"(v[7])
+      : "v"(mu));
+}
+__device__ __forceinline__ float mirror_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+}
+
 // One block's input in the quad layout: raw words (bf16: 4 x 16 B per lane; fp32:
 // 8 x 16 B per lane).
 template <bool BF16>
@@ -434,18 +459,23 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
 // pairs; the x-stride is a multiple of nblk, so a quad keeps one block index j
 // (one sign slice) for the whole kernel.  The next block's input is loaded while
 // the current one is processed.
-template <int BITS, bool BF16, bool NC>
+// WV: whole-vector mode for head_dim 256 ([Spec] "Step 1", one 256-point transform;
+// nblk = 2): the two quads of a vector also run the last butterfly stage between
+// them, share one norm (and store it once) and scale by RN32(1/16).
+template <int BITS, bool BF16, bool NC, bool WV>
 __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
                                                           SignWords sw) {
+  static_assert(!WV || (BITS != 8 && !NC), "whole-vector mode: 2-4 bit codebooks");
   constexpr int CB = code_bytes_of<BITS>();
   typedef typename std::conditional<NC, uint4, uint2>::type Cell;
   __shared__ Cell cells[BITS == 8 ? 1 : kCells];
-  const int q = threadIdx.x & 3;
   const uint32_t f0 = blockIdx.x * (kEncThreads / 4) + (threadIdx.x >> 2);
   const uint32_t nblk = static_cast<uint32_t>(a.nblk);
   const int j = static_cast<int>(f0 % nblk);
+  // chunk index of the lane (reversed in a whole vector's second quad, see xstage_mirror)
+  const int q = WV && (j & 1) ? 3 - static_cast<int>(threadIdx.x & 3) : threadIdx.x & 3;
   const int t_first = static_cast<int>(f0 / nblk);
-  const int t_step = static_cast<int>(gridDim.x * (kEncThreads / 4) / nblk);
+  const int t_step = a.t_step;   // gridDim.x * quads per workgroup / nblk
   const int rows = a.batch * a.heads;
   constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
   const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + QK * a.nblk) * ES);
@@ -463,7 +493,9 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
     r.rx = make_rsrc(static_cast<const char*>(a.x) + (b * a.sb + h * a.sh) * ES, xbytes);
     const int64_t crow = static_cast<int64_t>(row) * a.t_max * a.nblk;
     r.rc = make_rsrc(a.codes + crow * CB, cbytes);
-    r.rn = make_rsrc(a.norms + crow, nbytes);
+    // one norm per block, or per vector in the whole-vector mode
+    r.rn = WV ? make_rsrc(a.norms + static_cast<int64_t>(row) * a.t_max, nbytes / 2)
+              : make_rsrc(a.norms + crow, nbytes);
     return r;
   };
   // byte offset of block (t, j) in the input row; kOOB past the last token
@@ -494,7 +526,9 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   // mu of the two cross-lane stages, and the sign the lane's results carry after them
   const float mu1 = (q & 1) ? -1.0f : 1.0f;
   const float mu2 = (q & 2) ? -1.0f : 1.0f;
-  const uint32_t carried = ((q ^ (q >> 1)) & 1u) << 31;
+  const uint32_t carried = (((q ^ (q >> 1)) & 1u) ^ (WV ? (j & 1) : 0)) << 31;
+  const float mu3 = (j & 1) ? -1.0f : 1.0f;   // the stage between the two blocks (WV)
+  constexpr float c_scale = WV ? 0.0625f : kInvSqrtQK;   // RN32(1/sqrt(d))
   // second sign vector: code mirror masks per chunk (zero without it)
   uint32_t mirror[4];
 #pragma unroll
@@ -513,9 +547,11 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
     for (int k = 0; k < 4; ++k) p[k] = quad_add<0xB1>(p[k]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) p[k] = quad_add<0x4E>(p[k]);
-    const float n32 = __builtin_sqrtf((p[0] + p[1]) + (p[2] + p[3]));
+    float ss = (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (WV) ss = mirror_add(ss);   // level 7: the vector's two blocks
+    const float n32 = __builtin_sqrtf(ss);
     // Walsh-Hadamard butterflies, stages 1, 2, 4 (in-chunk), 8, 16 (across the
-    // quad), 32, 64 (across chunks)
+    // quad), 32, 64 (across chunks), and 128 across the two quads of a whole vector
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       bfly(x[k][0], x[k][1]); bfly(x[k][2], x[k][3]);
@@ -538,6 +574,10 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
     for (int i = 0; i < 8; ++i) {
       bfly(x[0][i], x[2][i]);
       bfly(x[1][i], x[3][i]);
+    }
+    if constexpr (WV) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage_mirror(x[k], mu3);
     }
 
     // position tbase + t, or its ring slot; 0 <= tbase + t < 2^32 when tbase >= 0
@@ -577,7 +617,7 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
         __builtin_amdgcn_raw_buffer_store_b32(hi, R.rc, o + 4, 0, 0);
       }
     } else {
-      const float g0 = n32 > 0.0f ? kInvSqrtQK / n32 : 0.0f;
+      const float g0 = n32 > 0.0f ? c_scale / n32 : 0.0f;
       const float g = __uint_as_float(__float_as_uint(g0) ^ carried);
       float sq[4];
       auto codes8 = [&](int k) {
@@ -621,7 +661,9 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
         nbits = __half_as_ushort(__float2half_rn(n32));
       }
     }
-    __builtin_amdgcn_raw_buffer_store_b16(nbits, R.rn, valid && q == 0 ? 2 * cblk : kOOB, 0, 0);
+    const uint32_t nidx = WV ? static_cast<uint32_t>(tt) : cblk;
+    __builtin_amdgcn_raw_buffer_store_b16(
+        nbits, R.rn, valid && q == 0 && (!WV || j == 0) ? 2 * nidx : kOOB, 0, 0);
   };
   // Ping-pong buffers: block t + t_step loads while block t is processed.  The trip
   // count is uniform over the wavefront (lane 0 holds its smallest t); lanes past the
@@ -652,10 +694,13 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   }
 }
 
-// Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block.
-template <int BITS, bool BF16_OUT>
+// Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block.  WV: whole
+// vectors of head_dim 256 (nblk = 2): one norm per vector, the butterfly stage
+// between the vector's two blocks (adjacent quads), scale 1/16.
+template <int BITS, bool BF16_OUT, bool WV>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
                                                           SignWords sw) {
+  static_assert(!WV || BITS != 8, "whole-vector mode: 2-4 bit codebooks");
   constexpr int CB = code_bytes_of<BITS>();
   __shared__ float cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
@@ -674,7 +719,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
     const int j = static_cast<int>(rem - t * d.nblk);
     const int64_t cblk = (row * d.t_max + t) * d.nblk + j;
     const uint8_t* crow = d.codes + cblk * CB;
-    const float n = __half2float(__ushort_as_half(d.norms[cblk]));
+    const float n = __half2float(__ushort_as_half(d.norms[WV ? row * d.t_max + t : cblk]));
     const uint32_t sbits = sw.w[j][q];
     const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;   // R^T = D1 H D2 / sqrt(128)
     float v[4][8];
@@ -693,6 +738,14 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
       }
     }
     fwht_quad(v, q);
+    if constexpr (WV) {
+      // the two quads of a vector are 4 lanes apart (blocks enumerated j = 0, 1)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[k][i] = xbfly(v[k][i], 4, j & 1);
+    }
+    constexpr float c_scale = WV ? 0.0625f : kInvSqrtQK;
     const int64_t b = row / d.heads, h = row - b * d.heads;
     const int64_t eo = b * d.sb + h * d.sh + t * d.st + static_cast<int64_t>(QK) * j;
 #pragma unroll
@@ -700,7 +753,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
       float r[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        r[i] = flip_sign(v[k][i] * kInvSqrtQK, (sbits >> (8 * k + i)) & 1u);
+        r[i] = flip_sign(v[k][i] * c_scale, (sbits >> (8 * k + i)) & 1u);
       const int c = q + 4 * k;
       if constexpr (BF16_OUT) {
         uint32_t w[4];
@@ -717,183 +770,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   }
 }
 
-// ---------------------------------------------------------------------------
-// Whole-vector mode ([Spec] "Step 1": one d x d rotation, d = head_dim a power of
-// two; "Step 2": the codebook of that dimension; one norm per vector).  One
-// wavefront per vector, lane l holding elements E l .. E l + E - 1 (E = d / 64):
-// index bits below log2(E) in-lane, the six above across lanes (lane bit k = index
-// bit log2(E) + k).  Canonical fp32 order as the blocked mode: squares summed over
-// index bits 0, 1, ... in order, butterflies in stage order 1, 2, ..., d/2,
-// g = RN32(c_d / n32) with c_d = RN32(1/sqrt(d)), u = RN32(h g).  Codes are packed
-// per consecutive 128 elements exactly as the blocked layout.
-
-// Sign of element e from a flat bit array (bit e set: -1).
-__device__ __forceinline__ uint32_t flat_bits(const FlatSigns& fs, int e, int n) {
-  return (fs.bits[e >> 5] >> (e & 31)) & ((1u << n) - 1u);
-}
-
-// In-wave Walsh-Hadamard butterflies (unnormalized) of a vector held E per lane.
-template <int E>
-__device__ __forceinline__ void fwht_wave(float (&v)[E], int lane) {
-#pragma unroll
-  for (int L = 1; L < E; L <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      if ((i & L) == 0) {
-        const float x = v[i], y = v[i + L];
-        v[i] = x + y;
-        v[i + L] = x - y;
-      }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool up = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float p = __shfl_xor(v[i], m, 64);
-      v[i] = up ? p - v[i] : v[i] + p;
-    }
-  }
-}
-
-// Store fields of W bits, (code_i & mask) >> shift for the lane's E codes, LSB-first
-// from element el of a 128-block row; lanes pair up through shuffles when one lane
-// holds less than a byte (all lanes take part in the shuffles).
-template <int W, int E>
-__device__ __forceinline__ void put_fields(uint8_t* row, int el, const uint32_t (&code)[E],
-                                           uint32_t mask, int shift, int lane) {
-  uint32_t f = 0;
-#pragma unroll
-  for (int i = 0; i < E; ++i) f |= ((code[i] & mask) >> shift) << (W * i);
-  constexpr int bits = W * E;
-  if constexpr (bits >= 8) {
-#pragma unroll
-    for (int k = 0; k < bits / 8; ++k) row[(el * W) / 8 + k] = static_cast<uint8_t>(f >> (8 * k));
-  } else {
-    constexpr int group = 8 / bits;
-    uint32_t acc = f;
-#pragma unroll
-    for (int k = 1; k < group; ++k)
-      acc |= static_cast<uint32_t>(__shfl_down(static_cast<int>(f), k, 64)) << (bits * k);
-    if (lane % group == 0) row[(el * W) / 8] = static_cast<uint8_t>(acc);
-  }
-}
-
-template <int BITS, bool BF16, int E>
-__global__ void __launch_bounds__(kThreads) encode_whole_kernel(EncodeLaunch a, KTable tab,
-                                                                FlatSigns fs) {
-  constexpr int D = 64 * E;
-  constexpr int CB = code_bytes_of<BITS>();
-  __shared__ uint2 cells[kCells];
-  fill_cells(cells, tab);
-  lds_barrier();
-  const int lane = threadIdx.x & 63;
-  const uint32_t sgn = flat_bits(fs, E * lane, E);
-  constexpr float c_d = D == 128 ? kInvSqrtQK : 0.0625f;   // RN32(1/sqrt(d)), d = 128 or 256
-  const int64_t nvec = static_cast<int64_t>(a.batch) * a.heads * a.tokens;
-  const int64_t wave0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
-  const int64_t nwave = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
-  for (int64_t vec = wave0; vec < nvec; vec += nwave) {
-    const int64_t row = vec / a.tokens;
-    const int t = static_cast<int>(vec - row * a.tokens);
-    const int64_t b = row / a.heads, h = row - b * a.heads;
-    const int64_t tt = static_cast<int64_t>(a.t0 ? a.t0[b] : 0) + t;
-    if (tt < 0 || tt >= a.t_max) continue;   // uniform over the wavefront
-    const int64_t xo = b * a.sb + h * a.sh + static_cast<int64_t>(t) * a.st + E * lane;
-    float x[E];
-    if constexpr (BF16) {
-      const uint16_t* xp = static_cast<const uint16_t*>(a.x) + xo;
-#pragma unroll
-      for (int i = 0; i < E; ++i) x[i] = __uint_as_float(static_cast<uint32_t>(xp[i]) << 16);
-    } else {
-      const float* xp = static_cast<const float*>(a.x) + xo;
-#pragma unroll
-      for (int i = 0; i < E; ++i) x[i] = xp[i];
-    }
-    // canonical norm: pairwise over the in-lane bits, then across lanes
-    float q[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) q[i] = x[i] * x[i];
-#pragma unroll
-    for (int L = 1; L < E; L <<= 1)
-#pragma unroll
-      for (int i = 0; i < E; i += 2 * L) q[i] = q[i] + q[i + L];
-    float ss = q[0];
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) ss = ss + __shfl_xor(ss, m, 64);
-    const float n32 = __builtin_sqrtf(ss);
-#pragma unroll
-    for (int i = 0; i < E; ++i) x[i] = flip_sign(x[i], (sgn >> i) & 1u);
-    fwht_wave<E>(x, lane);
-    const float g = n32 > 0.0f ? c_d / n32 : 0.0f;
-    uint32_t code[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float u = x[i] * g;
-      const uint32_t off = (__float_as_uint(u) >> (kCellShift - 3)) & ((kCells - 1u) << 3);
-      const uint2 cell = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cells) + off);
-      code[i] = cell.y + (u > __uint_as_float(cell.x) ? 1u : 0u);
-    }
-    // element e = E lane + i sits in 128-block e / 128 at offset e % 128
-    const int e0 = E * lane, blk = e0 >> 7, el = e0 & 127;
-    uint8_t* crow = a.codes + ((row * a.t_max + tt) * (D / QK) + blk) * CB;
-    if constexpr (BITS == 4) {
-      put_fields<4, E>(crow, el, code, 15u, 0, lane);
-    } else if constexpr (BITS == 2) {
-      put_fields<2, E>(crow, el, code, 3u, 0, lane);
-    } else {
-      put_fields<2, E>(crow, el, code, 3u, 0, lane);        // low two bits
-      put_fields<1, E>(crow + 32, el, code, 4u, 2, lane);   // high bit plane
-    }
-    if (lane == 0) a.norms[row * a.t_max + tt] = __half_as_ushort(__float2half_rn(n32));
-  }
-}
-
-template <int BITS, bool BF16_OUT, int E>
-__global__ void __launch_bounds__(kThreads) decode_whole_kernel(DecodeLaunch d, KTable tab,
-                                                                FlatSigns fs) {
-  constexpr int D = 64 * E;
-  constexpr int CB = code_bytes_of<BITS>();
-  __shared__ float cent[16];
-  if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const uint32_t sgn = flat_bits(fs, E * lane, E);
-  constexpr float c_d = D == 128 ? kInvSqrtQK : 0.0625f;
-  const int64_t nvec = d.rows * d.tokens;
-  const int64_t wave0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
-  const int64_t nwave = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
-  const int e0 = E * lane, blk = e0 >> 7, el = e0 & 127;
-  for (int64_t vec = wave0; vec < nvec; vec += nwave) {
-    const int64_t row = vec / d.tokens;
-    const int64_t t = vec - row * d.tokens;
-    const uint8_t* crow = d.codes + ((row * d.t_max + t) * (D / QK) + blk) * CB;
-    const float n = __half2float(__ushort_as_half(d.norms[row * d.t_max + t]));
-    float v[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const int p = el + i;
-      uint32_t c;
-      if constexpr (BITS == 4) c = (crow[p >> 1] >> (4 * (p & 1))) & 15u;
-      else if constexpr (BITS == 2) c = (crow[p >> 2] >> (2 * (p & 3))) & 3u;
-      else c = ((crow[p >> 2] >> (2 * (p & 3))) & 3u) | (((crow[32 + (p >> 3)] >> (p & 7)) & 1u) << 2);
-      v[i] = n * cent[c];
-    }
-    fwht_wave<E>(v, lane);
-    const int64_t b = row / d.heads, h = row - b * d.heads;
-    const int64_t eo = b * d.sb + h * d.sh + t * d.st + e0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = flip_sign(v[i] * c_d, (sgn >> i) & 1u);
-    if constexpr (BF16_OUT) {
-      uint16_t* o = static_cast<uint16_t*>(d.out) + eo;
-#pragma unroll
-      for (int i = 0; i < E; ++i) o[i] = static_cast<uint16_t>(bf16_rne(v[i]));
-    } else {
-      float* o = static_cast<float*>(d.out) + eo;
-#pragma unroll
-      for (int i = 0; i < E; ++i) o[i] = v[i];
-    }
-  }
-}
 
 int grid_for(int64_t blocks) {
   const int64_t quads_per_wg = kThreads / 4;
@@ -933,90 +809,67 @@ dim3 encode_grid(const EncodeLaunch& a) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
-                         bool norm_correct, hipStream_t stream) {
+                         bool norm_correct, bool whole, hipStream_t stream) {
   const dim3 grid = encode_grid(a), block(kEncThreads);
-#define FATQ_ENC(B, F, N) \
-  hipLaunchKernelGGL((encode_kernel<B, F, N>), grid, block, 0, stream, a, tab, sw)
-#define FATQ_ENC_BITS(F, N)              \
-  switch (tab.bits) {                    \
-    case 2: FATQ_ENC(2, F, N); break;    \
-    case 3: FATQ_ENC(3, F, N); break;    \
-    case 4: FATQ_ENC(4, F, N); break;    \
-    default: FATQ_ENC(8, F, false); break; \
+  EncodeLaunch la = a;
+  la.t_step = static_cast<int32_t>(grid.x * (kEncThreads / 4) / a.nblk);
+#define FATQ_ENC(B, F, N, W) \
+  hipLaunchKernelGGL((encode_kernel<B, F, N, W>), grid, block, 0, stream, la, tab, sw)
+#define FATQ_ENC_BITS(F, N)                     \
+  switch (tab.bits) {                           \
+    case 2: FATQ_ENC(2, F, N, false); break;    \
+    case 3: FATQ_ENC(3, F, N, false); break;    \
+    case 4: FATQ_ENC(4, F, N, false); break;    \
+    default: FATQ_ENC(8, F, false, false); break; \
   }
-  if (a.x_is_bf16) {
+#define FATQ_ENC_WV(F)                          \
+  switch (tab.bits) {                           \
+    case 2: FATQ_ENC(2, F, false, true); break; \
+    case 3: FATQ_ENC(3, F, false, true); break; \
+    default: FATQ_ENC(4, F, false, true); break; \
+  }
+  // head_dim 128 in the whole-vector mode is the blocked encode itself
+  if (whole && a.nblk == 2) {
+    if (a.x_is_bf16) { FATQ_ENC_WV(true) } else { FATQ_ENC_WV(false) }
+  } else if (a.x_is_bf16) {
     if (norm_correct) { FATQ_ENC_BITS(true, true) } else { FATQ_ENC_BITS(true, false) }
   } else {
     if (norm_correct) { FATQ_ENC_BITS(false, true) } else { FATQ_ENC_BITS(false, false) }
   }
+#undef FATQ_ENC_WV
 #undef FATQ_ENC_BITS
 #undef FATQ_ENC
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
-                         hipStream_t stream) {
+                         bool whole, hipStream_t stream) {
   const dim3 grid(grid_for(d.rows * d.tokens * d.nblk)), block(kThreads);
-#define FATQ_DEC(B, F) hipLaunchKernelGGL((decode_kernel<B, F>), grid, block, 0, stream, d, tab, sw)
-  if (d.out_bf16) {
-    switch (tab.bits) {
-      case 2: FATQ_DEC(2, true); break;
-      case 3: FATQ_DEC(3, true); break;
-      case 4: FATQ_DEC(4, true); break;
-      default: FATQ_DEC(8, true); break;
-    }
-  } else {
-    switch (tab.bits) {
-      case 2: FATQ_DEC(2, false); break;
-      case 3: FATQ_DEC(3, false); break;
-      case 4: FATQ_DEC(4, false); break;
-      default: FATQ_DEC(8, false); break;
-    }
+#define FATQ_DEC(B, F, W) \
+  hipLaunchKernelGGL((decode_kernel<B, F, W>), grid, block, 0, stream, d, tab, sw)
+#define FATQ_DEC_BITS(F)                 \
+  switch (tab.bits) {                    \
+    case 2: FATQ_DEC(2, F, false); break; \
+    case 3: FATQ_DEC(3, F, false); break; \
+    case 4: FATQ_DEC(4, F, false); break; \
+    default: FATQ_DEC(8, F, false); break; \
   }
+#define FATQ_DEC_WV(F)                   \
+  switch (tab.bits) {                    \
+    case 2: FATQ_DEC(2, F, true); break;  \
+    case 3: FATQ_DEC(3, F, true); break;  \
+    default: FATQ_DEC(4, F, true); break; \
+  }
+  if (whole && d.nblk == 2) {
+    if (d.out_bf16) { FATQ_DEC_WV(true) } else { FATQ_DEC_WV(false) }
+  } else if (d.out_bf16) {
+    FATQ_DEC_BITS(true)
+  } else {
+    FATQ_DEC_BITS(false)
+  }
+#undef FATQ_DEC_WV
+#undef FATQ_DEC_BITS
 #undef FATQ_DEC
-  return hipGetLastError();
-}
-
-hipError_t launch_encode_whole(const EncodeLaunch& a, const KTable& tab, const FlatSigns& fs,
-                               int head_dim, hipStream_t stream) {
-  const int64_t nvec = static_cast<int64_t>(a.batch) * a.heads * a.tokens;
-  const dim3 grid(grid_for(nvec * 4)), block(kThreads);   // 4 vectors per workgroup pass
-#define FATQ_ENCW(B, F, E) \
-  hipLaunchKernelGGL((encode_whole_kernel<B, F, E>), grid, block, 0, stream, a, tab, fs)
-#define FATQ_ENCW_BITS(F, E)          \
-  switch (tab.bits) {                 \
-    case 2: FATQ_ENCW(2, F, E); break; \
-    case 3: FATQ_ENCW(3, F, E); break; \
-    default: FATQ_ENCW(4, F, E); break; \
-  }
-  if (head_dim == 128) {
-    if (a.x_is_bf16) { FATQ_ENCW_BITS(true, 2) } else { FATQ_ENCW_BITS(false, 2) }
-  } else {
-    if (a.x_is_bf16) { FATQ_ENCW_BITS(true, 4) } else { FATQ_ENCW_BITS(false, 4) }
-  }
-#undef FATQ_ENCW_BITS
-#undef FATQ_ENCW
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_whole(const DecodeLaunch& d, const KTable& tab, const FlatSigns& fs,
-                               int head_dim, hipStream_t stream) {
-  const dim3 grid(grid_for(d.rows * d.tokens * 4)), block(kThreads);
-#define FATQ_DECW(B, F, E) \
-  hipLaunchKernelGGL((decode_whole_kernel<B, F, E>), grid, block, 0, stream, d, tab, fs)
-#define FATQ_DECW_BITS(F, E)          \
-  switch (tab.bits) {                 \
-    case 2: FATQ_DECW(2, F, E); break; \
-    case 3: FATQ_DECW(3, F, E); break; \
-    default: FATQ_DECW(4, F, E); break; \
-  }
-  if (head_dim == 128) {
-    if (d.out_bf16) { FATQ_DECW_BITS(true, 2) } else { FATQ_DECW_BITS(false, 2) }
-  } else {
-    if (d.out_bf16) { FATQ_DECW_BITS(true, 4) } else { FATQ_DECW_BITS(false, 4) }
-  }
-#undef FATQ_DECW_BITS
-#undef FATQ_DECW
   return hipGetLastError();
 }
 

@@ -159,16 +159,6 @@ fatq::SignWords make_sign_words(uint64_t seed, int head_dim, bool two = false) {
   return sw;
 }
 
-fatq::FlatSigns make_flat_signs(uint64_t seed, int head_dim) {
-  std::vector<int8_t> s(head_dim);
-  make_signs(seed, head_dim, s.data());
-  fatq::FlatSigns fs;
-  std::memset(&fs, 0, sizeof(fs));
-  for (int e = 0; e < head_dim; ++e)
-    if (s[e] < 0) fs.bits[e >> 5] |= 1u << (e & 31);
-  return fs;
-}
-
 // Whole-vector mode: head_dim 128 or 256, a 2-4 bit codebook of that dimension.
 fa_tq_status check_whole(const fa_tq_codebook* cb, int32_t head_dim, const char* who) {
   if (head_dim != 128 && head_dim != 256)
@@ -355,14 +345,8 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   a.codes = codes;
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
-  if (whole) {
-    const fatq::FlatSigns fs = make_flat_signs(seed, head_dim);
-    return launched(fatq::launch_encode_whole(a, tab, fs, head_dim,
-                                              static_cast<hipStream_t>(stream)),
-                    who);
-  }
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
-  return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0,
+  return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0, whole,
                                       static_cast<hipStream_t>(stream)),
                   who);
 }
@@ -544,7 +528,7 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
   d.st = head_dim;
   d.out_bf16 = 0;
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)),
+  return launched(fatq::launch_decode(d, tab, sw, false, static_cast<hipStream_t>(stream)),
                   "fa_tq_decode");
 }
 
@@ -588,14 +572,9 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
   d.sh = out_layout.stride_h;
   d.st = out_layout.stride_t;
   d.out_bf16 = out_dtype == FA_TQ_BF16;
-  if (whole) {
-    const fatq::FlatSigns fs = make_flat_signs(seed, head_dim);
-    return launched(fatq::launch_decode_whole(d, tab, fs, head_dim,
-                                              static_cast<hipStream_t>(stream)),
-                    who);
-  }
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
-  return launched(fatq::launch_decode(d, tab, sw, static_cast<hipStream_t>(stream)), who);
+  return launched(fatq::launch_decode(d, tab, sw, whole, static_cast<hipStream_t>(stream)),
+                  who);
 }
 
 fa_tq_status fa_tq_attn_decode(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,

@@ -38,11 +38,6 @@ struct KTable {
   uint32_t cell_out[5][4];
 };
 
-// Signs of a whole vector as a flat bit array: bit e set when element e is negated.
-struct FlatSigns {
-  uint32_t bits[FA_TQ_MAX_HEAD_DIM / 32];
-};
-
 // fp32 nearest to 1/sqrt(128) (the scale of [Spec] Step 1), and the 8-bit grid
 // constant fp32(kInvSqrtQK * 127.5).
 constexpr float kInvSqrtQK = static_cast<float>(0.08838834764831845);
@@ -61,8 +56,10 @@ struct EncodeLaunch {
 };
 
 // norm_correct: store n / ||c[codes]|| ([turboq] "Encode pipeline" step 4; bits 2-4).
+// whole: whole-vector mode ([Spec] "Step 1": one rotation over head_dim = 128 or 256,
+// one norm per vector, norms[rows][t_max]; codes as the blocked layout).
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
-                         bool norm_correct, hipStream_t stream);
+                         bool norm_correct, bool whole, hipStream_t stream);
 // Decode of tokens [0, tokens) of `rows` cache rows of t_max slots each (row =
 // b * heads + h) into out[b][h][t][:] at element strides (sb, sh, st).
 struct DecodeLaunch {
@@ -76,14 +73,7 @@ struct DecodeLaunch {
 };
 
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
-                         hipStream_t stream);
-
-// Whole-vector mode (one rotation over head_dim = 128 or 256, one norm per vector,
-// norms[rows][t_max]); codes as the blocked layout.
-hipError_t launch_encode_whole(const EncodeLaunch& a, const KTable& tab, const FlatSigns& fs,
-                               int head_dim, hipStream_t stream);
-hipError_t launch_decode_whole(const DecodeLaunch& d, const KTable& tab, const FlatSigns& fs,
-                               int head_dim, hipStream_t stream);
+                         bool whole, hipStream_t stream);
 
 struct AttnLaunch {
   const void* q;

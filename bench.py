@@ -8,9 +8,10 @@ Llama-3-8B-shaped layer: 1 x 32768 tokens, 32 query / 8 KV heads, head_dim 128.
 Prints one JSON line.  ``value`` = algorithmic bytes of a step / step time (GB/s).
 Algorithmic bytes: encode = input bytes + packed code bytes + 2-byte norm per
 128-block; attention = per (sequence, token, KV head) the K and V code bytes and
-the two norms, plus the query and output.  Buffers rotate over several copies so
-that consecutive steps do not find the previous step's data in the 256 MB
-last-level cache.
+the two norms, plus the query and output.  Inputs rotate over 4 copies (a step
+streams 160 MB of encode traffic, so a copy comes back after 480 MB) and packed
+caches over 32 copies (840 MB, which the attention phase cycles through), so no call
+finds its data in the 256 MB last-level cache.
 
 The K timed steps run phase by phase: the K encodes of the K cache back to back, then
 the K encodes of the V cache, then the K attentions, step i's attention reading the
@@ -70,7 +71,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama_layer")
-    p.add_argument("--copies", type=int, default=4, help="input/cache copies rotated per step")
+    p.add_argument("--copies", type=int, default=4, help="input copies rotated per step")
+    p.add_argument("--cache-copies", type=int, default=32, help="packed-cache copies rotated")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-append", action="store_true", help="skip the append_decode figure")
     p.add_argument("--calibrate-copy", action="store_true")
@@ -108,6 +110,16 @@ def summarize_rocprof(d: str) -> None:
         for r in csv.DictReader(open(f)):
             print(f"{short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                   f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        dur = {}
+        for r in csv.DictReader(open(f)):
+            if "Kernel_Name" in r and "Start_Timestamp" in r and "End_Timestamp" in r:
+                dur.setdefault(short_kernel(r["Kernel_Name"]), []).append(
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        print(f"# {os.path.basename(f)}: kernel | dispatches | p10_ns | median_ns | p90_ns")
+        for k, v in dur.items():
+            p10, p50, p90 = np.percentile(v, [10, 50, 90])
+            print(f"{k} | {len(v)} | {p10:.0f} | {p50:.0f} | {p90:.0f}")
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         agg, disp = {}, {}
         for r in csv.DictReader(open(f)):
@@ -354,22 +366,24 @@ def main():
     ks = [k] + [k.clone() for _ in range(R - 1)]
     vs = [v] + [v.clone() for _ in range(R - 1)]
     cbk, cbv = fa.codebook_init(128, w.k_bits), fa.codebook_init(128, w.v_bits)
+    C = max(R, args.cache_copies)
     caches = [fa.cache_buffers(B, Hkv, T, d, w.k_bits) + fa.cache_buffers(B, Hkv, T, d, w.v_bits)
-              for _ in range(R)]
+              for _ in range(C)]
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     ws = fa.attn_workspace(B, Hq, Hkv, T, d)
     scale = 1 / np.sqrt(d)
     # arguments marshalled once per buffer copy: a launch costs one ctypes call
-    enc_k = [fa.encode_call(cbk, seed, ks[i], caches[i][0], caches[i][1]) for i in range(R)]
-    enc_v = [fa.encode_call(cbv, seed, vs[i], caches[i][2], caches[i][3]) for i in range(R)]
+    # step i: input copy i % R, cache copy i % C
+    enc_k = [fa.encode_call(cbk, seed, ks[i % R], caches[i][0], caches[i][1]) for i in range(C)]
+    enc_v = [fa.encode_call(cbv, seed, vs[i % R], caches[i][2], caches[i][3]) for i in range(C)]
     attn = [fa.attn_decode_call(cbk, cbv, seed, q, *caches[i], lens, scale, out, ws)
-            for i in range(R)]
+            for i in range(C)]
     names = ("encode_k", "encode_v", "attn_decode")
     calls = (enc_k, enc_v, attn)
 
     for i in range(args.warmup):
         for c in calls:
-            c[i % R]()
+            c[i % C]()
     K = args.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
@@ -377,7 +391,7 @@ def main():
     for j, c in enumerate(calls):
         ev[j].record()
         for i in range(K):
-            c[i % R]()
+            c[i % C]()
     ev[3].record()
     t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
@@ -398,8 +412,8 @@ def main():
             rec["vectors_per_s"] = round(nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false>",
-             "encode_v": f"encode_kernel<{w.v_bits}, true, false>"}.get(dom, dom)
+    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false, false>",
+             "encode_v": f"encode_kernel<{w.v_bits}, true, false, false>"}.get(dom, dom)
     traffic = traffic_for(kname)
     roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
@@ -420,7 +434,8 @@ def main():
         "data": "synthetic (seeded; bf16 AR(1) rho 0.9 with lognormal channel scales)",
         "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "tokens": T, "head_dim": d, "k_bits": w.k_bits, "v_bits": w.v_bits,
-                   "step": "encode K + encode V + decode attention", "copies": R},
+                   "step": "encode K + encode V + decode attention", "copies": R,
+                   "cache_copies": C},
         "step_algorithmic_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
         "host_us_per_step": round(t_host / K * 1e6, 1),

@@ -86,7 +86,7 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  * the arrays are unused and must be zero.
  */
 typedef struct {
-    int32_t dim;            /* 128: tables are per QK block */
+    int32_t dim;            /* 128 (per QK block); head_dim for FA_TQ_WHOLE_VECTOR */
     int32_t bits;           /* 2, 3, 4, or 8 */
     int32_t levels;         /* 1 << bits */
     float boundaries[15];   /* levels - 1 used, strictly ascending */

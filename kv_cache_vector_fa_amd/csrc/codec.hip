@@ -436,7 +436,9 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
         const float lo = __uint_as_float(f << 16), hi = __uint_as_float(f & 0xffff0000u);
         x[k][2 * m] = lo;
         x[k][2 * m + 1] = hi;
-        s[m] = lo * lo + hi * hi;
+        // a bf16 square is exact in fp32 (for |x| >= 2^-63), so one fma is
+        // RN32(RN32(lo^2) + RN32(hi^2))
+        s[m] = __builtin_fmaf(hi, hi, lo * lo);
       }
     } else {
       const uint4 a = r.w[2 * k], b = r.w[2 * k + 1];

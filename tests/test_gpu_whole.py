@@ -112,3 +112,22 @@ def test_whole_prefill_slice_sampled(gpu_lib):
     flips = compare_codes(gc.reshape(-1, 64), oc.reshape(-1, 128), 4, "prefill whole")
     compare_norms(norms[:, :, toks].cpu().numpy(), on, "prefill whole")
     say(f"prefill slice whole-vector: {flips} flips in {oc.size}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_whole_decode_bf16_is_rounded_fp32(gpu_lib, bits):
+    """head_dim 256 whole-vector decode to bf16 is the round-to-nearest-even of the
+    fp32 decode (the same arithmetic, rounded at the store), in a strided output."""
+    torch = _torch()
+    fa = gpu_lib
+    x = torch.randn((2, 3, 77, 256), device="cuda").to(torch.bfloat16)
+    cb = fa.codebook_init(256, bits)
+    codes, norms = fa.encode(cb, SEED, x, flags=fa.WHOLE_VECTOR)
+    f32 = fa.decode_kv(cb, SEED, codes, norms, out_dtype=torch.float32, flags=fa.WHOLE_VECTOR)
+    wide = torch.zeros((2, 3, 77, 384), dtype=torch.bfloat16, device="cuda")
+    out = wide[..., 64:320]
+    fa.decode_kv(cb, SEED, codes, norms, out=out, flags=fa.WHOLE_VECTOR)
+    torch.cuda.synchronize()
+    want = codec.round_bf16(f32.cpu().numpy().astype(np.float64))
+    np.testing.assert_array_equal(bf16_to_f32(out), want.astype(np.float32))
+    assert torch.all(wide[..., :64] == 0) and torch.all(wide[..., 320:] == 0)

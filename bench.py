@@ -13,12 +13,14 @@ streams 160 MB of encode traffic, so a copy comes back after 480 MB) and packed
 caches over 32 copies (840 MB, which the attention phase cycles through), so no call
 finds its data in the 256 MB last-level cache.
 
-The K timed steps run phase by phase: the K encodes of the K cache back to back, then
-the K encodes of the V cache, then the K attentions, step i's attention reading the
-cache copy its encodes wrote (every copy holds the same codes).  HIP events at the
-phase boundaries (on the stream the library launches on) give each kernel's mean
-launch-to-launch time without the dispatch of a different kernel in between, the
-figure rocprofv3's kernel durations are compared with.  The ``roofline.traffic``
+The K timed steps run in rounds of R steps, phase by phase within a round: R encodes
+of the K cache back to back, then R encodes of the V cache, then R attentions, step
+i's attention reading the cache copy its encodes wrote (every copy holds the same
+codes).  HIP events at the phase boundaries (on the stream the library launches on)
+give each kernel's mean launch-to-launch time without the dispatch of a different
+kernel in between, the figure rocprofv3's kernel durations are compared with; the
+rounds spread every kernel over the whole timed region, so a clock change on the
+box does not land on one kernel only.  The ``roofline.traffic``
 figure is read from the committed rocprofv3 counter summary in ``profiles/`` when
 the kernel's source file still has the hash recorded there, else it is null.
 
@@ -57,6 +59,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn packed-KV GB/s + encode vectors/s, % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
+ROUND = 10   # timed steps per round (see the module docstring)
 CSRC = os.path.join(ROOT, "kv_cache_vector_fa_amd", "csrc")
 # kernel name prefix (as rocprofv3 reports it) -> source file that defines it
 KERNEL_SOURCE = {"encode_kernel": "codec.hip", "attn_mfma_kernel": "attn_mfma.hip",
@@ -385,19 +388,22 @@ def main():
         for c in calls:
             c[i % C]()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    rounds = [(s0, min(K, s0 + ROUND)) for s0 in range(0, K, ROUND)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * len(rounds) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j, c in enumerate(calls):
-        ev[j].record()
-        for i in range(K):
-            c[i % C]()
-    ev[3].record()
+    for r, (s0, s1) in enumerate(rounds):
+        for j, c in enumerate(calls):
+            ev[3 * r + j].record()
+            for i in range(s0, s1):
+                c[i % C]()
+    ev[-1].record()
     t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[3]) / K
-    kms = [ev[j].elapsed_time(ev[j + 1]) / K for j in range(3)]
+    ms = ev[0].elapsed_time(ev[-1]) / K
+    kms = [sum(ev[3 * r + j].elapsed_time(ev[3 * r + j + 1]) for r in range(len(rounds))) / K
+           for j in range(3)]
 
     nblk = B * Hkv * T * (d // 128)
     nbytes = (enc_bytes(nblk, 256, w.k_bits), enc_bytes(nblk, 256, w.v_bits),

@@ -248,6 +248,29 @@ def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None
     return out
 
 
+def decode_kv_call(cb: Codebook, seed: int, codes, norms, out, n_tokens: int | None = None,
+                   stream=None, flags: int = 0):
+    """``decode_kv`` with its arguments marshalled once (see ``encode_call``)."""
+    lib = load()
+    B, H, t_max, nblk, cbytes = codes.shape
+    d = nblk * QK
+    n_tokens = t_max if n_tokens is None else n_tokens
+    if tuple(out.shape) != (B, H, n_tokens, d) or out.stride(3) != 1:
+        raise ValueError(f"out {tuple(out.shape)} for a cache of {tuple(codes.shape)}")
+    lay = Layout(out.stride(0), out.stride(1), out.stride(2))
+    args = (ctypes.byref(cb), ctypes.c_uint64(seed), ctypes.c_uint32(flags), ctypes.c_int32(d),
+            _ptr(codes), _ptr(norms), ctypes.c_int32(B), ctypes.c_int32(H),
+            ctypes.c_int32(n_tokens), ctypes.c_int32(t_max), _ptr(out),
+            ctypes.c_int(_dtype_code(out)), lay, _stream(stream))
+    fn = lib.fa_tq_decode_kv
+    keep = (cb, codes, norms, out)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call
+
+
 def attn_workspace(batch, n_q_heads, n_kv_heads, t_max, head_dim=QK, device="cuda"):
     """A workspace for ``attn_decode`` / ``attn_append`` (reusable by later calls in
     order on one stream)."""

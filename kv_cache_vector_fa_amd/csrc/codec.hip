@@ -27,12 +27,8 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kEncThreads = FATQ_ENCODE_THREADS;
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float flip_sign(float x, uint32_t bit) {
   return __uint_as_float(__float_as_uint(x) ^ (bit << 31));
@@ -50,45 +46,6 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
   const float u = a, v = b;
   a = u + v;
   b = u - v;
-}
-
-// Butterfly across lanes: the lower lane of the pair keeps u + v, the upper one
-// v_lower - v_upper (the same (u + v, u - v) pair, computed in the owning lane).
-__device__ __forceinline__ float xbfly(float x, int mask, bool upper) {
-  const float p = __shfl_xor(x, mask, 64);
-  return upper ? (p - x) : (x + p);
-}
-
-// Unscaled Walsh-Hadamard transform of one block in quad layout, stage order
-// len = 1, 2, 4, 8, 16, 32, 64.
-__device__ __forceinline__ void fwht_quad(float (&v)[4][8], int q) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    bfly(v[k][0], v[k][1]); bfly(v[k][2], v[k][3]);
-    bfly(v[k][4], v[k][5]); bfly(v[k][6], v[k][7]);
-    bfly(v[k][0], v[k][2]); bfly(v[k][1], v[k][3]);
-    bfly(v[k][4], v[k][6]); bfly(v[k][5], v[k][7]);
-    bfly(v[k][0], v[k][4]); bfly(v[k][1], v[k][5]);
-    bfly(v[k][2], v[k][6]); bfly(v[k][3], v[k][7]);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[k][i] = xbfly(v[k][i], 1, q & 1);
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[k][i] = xbfly(v[k][i], 2, (q & 2) != 0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bfly(v[0][i], v[1][i]);
-    bfly(v[2][i], v[3][i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bfly(v[0][i], v[2][i]);
-    bfly(v[1][i], v[3][i]);
-  }
 }
 
 // Pack the 8 codes of chunk c of one block and store them at the packed row
@@ -696,9 +653,14 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   }
 }
 
-// Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block.  WV: whole
-// vectors of head_dim 256 (nblk = 2): one norm per vector, the butterfly stage
-// between the vector's two blocks (adjacent quads), scale 1/16.
+// Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block, in the
+// encoder's layout: grid (gx, gy), blockIdx.y over the (batch, head) rows and block
+// slots f = (token, block j) of a row strided by gridDim.x * 64 (a multiple of nblk, so
+// a quad keeps its j and its sign words).  The two cross-lane stages are DPP
+// multiply-adds as in the encoder: the upper lane of a pair keeps the negated
+// difference, a sign folded into the final scale.  WV: whole vectors of head_dim 256
+// (nblk = 2): one norm per vector, the second quad's chunks in reversed lane order and
+// the stage between the vector's two blocks by row_half_mirror, scale 1/16.
 template <int BITS, bool BF16_OUT, bool WV>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
                                                           SignWords sw) {
@@ -707,79 +669,99 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   __shared__ float cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
   __syncthreads();
-  const int q = threadIdx.x & 3;
-  const int64_t quad0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 2;
-  const int64_t nquad = (static_cast<int64_t>(gridDim.x) * kThreads) >> 2;
-  const int64_t per_row = d.tokens * d.nblk;
-  const int64_t nblocks = d.rows * per_row;
-  for (int64_t blk = quad0; blk < nblocks; blk += nquad) {
-    // block blk = (row, token t, block j) of the decoded range; its cache block sits
-    // in a row of t_max slots
-    const int64_t row = blk / per_row;
-    const int64_t rem = blk - row * per_row;
-    const int64_t t = rem / d.nblk;
-    const int j = static_cast<int>(rem - t * d.nblk);
-    const int64_t cblk = (row * d.t_max + t) * d.nblk + j;
-    const uint8_t* crow = d.codes + cblk * CB;
-    const float n = __half2float(__ushort_as_half(d.norms[WV ? row * d.t_max + t : cblk]));
-    const uint32_t sbits = sw.w[j][q];
-    const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;   // R^T = D1 H D2 / sqrt(128)
-    float v[4][8];
+  const uint32_t nblk = static_cast<uint32_t>(d.nblk);
+  const uint32_t f0 = blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
+  const uint32_t fstep = gridDim.x * (kThreads / 4);
+  const int j = static_cast<int>(f0 % nblk);
+  const int q = WV && (j & 1) ? 3 - static_cast<int>(threadIdx.x & 3) : threadIdx.x & 3;
+  const uint32_t sbits = sw.w[j][q];
+  const uint32_t s2bits = sw.w2[j][q];   // R^T = D1 H D2 / sqrt(128); zero without it
+  const float mu1 = (q & 1) ? -1.0f : 1.0f;
+  const float mu2 = (q & 2) ? -1.0f : 1.0f;
+  const float mu3 = (j & 1) ? -1.0f : 1.0f;
+  const uint32_t carried = (((q ^ (q >> 1)) & 1u) ^ (WV ? (j & 1) : 0)) << 31;
+  constexpr float c_scale = WV ? 0.0625f : kInvSqrtQK;   // RN32(1/sqrt(d))
+  const float scale = __uint_as_float(__float_as_uint(c_scale) ^ carried);
+  const uint32_t per_row = static_cast<uint32_t>(d.tokens) * nblk;
+  for (int64_t row = blockIdx.y; row < d.rows; row += gridDim.y) {
+    const uint8_t* crows = d.codes + row * d.t_max * nblk * CB;
+    const uint16_t* nrows = d.norms + row * d.t_max * (WV ? 1 : nblk);
+    const int64_t b = row / d.heads, h = row - b * d.heads;
+    const int64_t obase = b * d.sb + h * d.sh + static_cast<int64_t>(QK) * j;
+    for (uint32_t f = f0; f < per_row; f += fstep) {
+      const uint32_t t = f / nblk;
+      const uint8_t* crow = crows + static_cast<int64_t>(f) * CB;
+      const float n = __half2float(__ushort_as_half(nrows[WV ? t : f]));
+      float v[4][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t code[8];
-      load_chunk<BITS>(crow, q + 4 * k, code);
+      for (int k = 0; k < 4; ++k) {
+        uint32_t code[8];
+        load_chunk<BITS>(crow, q + 4 * k, code);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float r;
+          if constexpr (BITS == 8)
+            r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
+          else
+            r = n * cent[code[i]];
+          v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
+        }
+      }
+      // butterflies: stages 1, 2, 4 in-chunk, 8, 16 across the quad, 32, 64 across
+      // chunks, and 128 across a whole vector's two quads
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bfly(v[k][0], v[k][1]); bfly(v[k][2], v[k][3]);
+        bfly(v[k][4], v[k][5]); bfly(v[k][6], v[k][7]);
+        bfly(v[k][0], v[k][2]); bfly(v[k][1], v[k][3]);
+        bfly(v[k][4], v[k][6]); bfly(v[k][5], v[k][7]);
+        bfly(v[k][0], v[k][4]); bfly(v[k][1], v[k][5]);
+        bfly(v[k][2], v[k][6]); bfly(v[k][3], v[k][7]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage<0xB1>(v[k], mu1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage<0x4E>(v[k], mu2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float r;
-        if constexpr (BITS == 8)
-          r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
-        else
-          r = n * cent[code[i]];
-        v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
+        bfly(v[0][i], v[1][i]);
+        bfly(v[2][i], v[3][i]);
       }
-    }
-    fwht_quad(v, q);
-    if constexpr (WV) {
-      // the two quads of a vector are 4 lanes apart (blocks enumerated j = 0, 1)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int i = 0; i < 8; ++i) {
+        bfly(v[0][i], v[2][i]);
+        bfly(v[1][i], v[3][i]);
+      }
+      if constexpr (WV) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[k][i] = xbfly(v[k][i], 4, j & 1);
-    }
-    constexpr float c_scale = WV ? 0.0625f : kInvSqrtQK;
-    const int64_t b = row / d.heads, h = row - b * d.heads;
-    const int64_t eo = b * d.sb + h * d.sh + t * d.st + static_cast<int64_t>(QK) * j;
+        for (int k = 0; k < 4; ++k) xstage_mirror(v[k], mu3);
+      }
+      const int64_t eo = obase + static_cast<int64_t>(t) * d.st;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float r[8];
+      for (int k = 0; k < 4; ++k) {
+        float r[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        r[i] = flip_sign(v[k][i] * c_scale, (sbits >> (8 * k + i)) & 1u);
-      const int c = q + 4 * k;
-      if constexpr (BF16_OUT) {
-        uint32_t w[4];
+        for (int i = 0; i < 8; ++i) r[i] = flip_sign(v[k][i] * scale, (sbits >> (8 * k + i)) & 1u);
+        const int c = q + 4 * k;
+        if constexpr (BF16_OUT) {
+          // v_cvt_pk_bf16_f32: two fp32 to bf16, round to nearest even
+          uint32_t w[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = bf16_rne(r[2 * m]) | (bf16_rne(r[2 * m + 1]) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + eo + 8 * c) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-        float4* o = reinterpret_cast<float4*>(static_cast<float*>(d.out) + eo + 8 * c);
-        o[0] = make_float4(r[0], r[1], r[2], r[3]);
-        o[1] = make_float4(r[4], r[5], r[6], r[7]);
+          for (int m = 0; m < 4; ++m)
+            w[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                    f2{r[2 * m], r[2 * m + 1]}, bf16x2));
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + eo + 8 * c) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          float4* o = reinterpret_cast<float4*>(static_cast<float*>(d.out) + eo + 8 * c);
+          o[0] = make_float4(r[0], r[1], r[2], r[3]);
+          o[1] = make_float4(r[4], r[5], r[6], r[7]);
+        }
       }
     }
   }
 }
 
-
-int grid_for(int64_t blocks) {
-  const int64_t quads_per_wg = kThreads / 4;
-  int64_t g = (blocks + quads_per_wg - 1) / quads_per_wg;
-  if (g > 8192) g = 8192;
-  if (g < 1) g = 1;
-  return static_cast<int>(g);
-}
 
 // Encode grid: y over (batch, head) rows, x over the quads of a row; about
 // kEncodeWGs workgroups in total, x a multiple of what keeps 64 * x divisible by
@@ -844,9 +826,29 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
   return hipGetLastError();
 }
 
+// Decode grid: y over the rows, x over the block slots of a row (about 8192
+// workgroups in total), x a multiple of what keeps 64 * x divisible by nblk.
+dim3 decode_grid(const DecodeLaunch& d) {
+  const int64_t gy = d.rows < 65535 ? d.rows : 65535;
+  const int64_t per_row = d.tokens * d.nblk;
+  const int64_t wg_row = (per_row + kThreads / 4 - 1) / (kThreads / 4);
+  int64_t gx = 8192 / gy;
+  if (gx > wg_row) gx = wg_row;
+  if (gx < 1) gx = 1;
+  int64_t g = kThreads / 4, n = d.nblk;
+  while (n != 0) {
+    const int64_t t = g % n;
+    g = n;
+    n = t;
+  }
+  const int64_t r = d.nblk / g;
+  gx = (gx + r - 1) / r * r;
+  return dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy > 0 ? gy : 1));
+}
+
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          bool whole, hipStream_t stream) {
-  const dim3 grid(grid_for(d.rows * d.tokens * d.nblk)), block(kThreads);
+  const dim3 grid = decode_grid(d), block(kThreads);
 #define FATQ_DEC(B, F, W) \
   hipLaunchKernelGGL((decode_kernel<B, F, W>), grid, block, 0, stream, d, tab, sw)
 #define FATQ_DEC_BITS(F)                 \

@@ -215,3 +215,48 @@ def test_encode_prefill_full_sampled(gpu_lib, bits):
     cbytes = gpu_lib.code_bytes(bits)
     compare_codes(gc.reshape(-1, cbytes), oc.reshape(-1, 128), bits, f"prefill {bits}")
     compare_norms(gn, on, f"prefill {bits}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_encode_and_restore_largest_row(gpu_lib, bits):
+    """The largest (batch, head) row the library accepts: 8388607 bf16 tokens of
+    head_dim 128 (2 GiB - 256 B of input in one row, byte offsets near 2^31).  Tokens
+    sampled over the whole row, the last ones included, are compared with the oracle,
+    and restored to bf16 (fa_tq_decode_kv) within the decode bound; one more token is
+    rejected."""
+    torch = _torch()
+    fa = gpu_lib
+    T = (1 << 31) // 256 - 1
+    say(f"encode largest row bits={bits} tokens={T}")
+    g = torch.Generator(device="cuda").manual_seed(77 + bits)
+    x = torch.empty((1, 1, T, 128), dtype=torch.bfloat16, device="cuda")
+    for s0 in range(0, T, 1 << 22):   # fill in slices (fp32 draws, then bf16)
+        s1 = min(T, s0 + (1 << 22))
+        x[0, 0, s0:s1] = torch.randn((s1 - s0, 128), generator=g, device="cuda").to(torch.bfloat16)
+    cb = fa.codebook_init(128, bits)
+    codes, norms = fa.encode(cb, SEED, x)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(bits)
+    pick = np.unique(np.concatenate([rng.choice(T, 2000, replace=False),
+                                     np.arange(T - 64, T), np.arange(64)]))
+    idx = torch.from_numpy(pick).cuda()
+    xs = x[0, 0].index_select(0, idx)
+    gc = codes[0, 0].index_select(0, idx).cpu().numpy()
+    gn = norms[0, 0].index_select(0, idx).cpu().numpy()
+    oc, on = _oracle_encode(bf16_to_f32(xs), bits, SEED)
+    cbytes = fa.code_bytes(bits)
+    compare_codes(gc.reshape(-1, cbytes), oc.reshape(-1, 128), bits, "largest row")
+    compare_norms(gn, on, "largest row")
+    # restore the whole row to bf16, check the sampled tokens against the fp64 decode
+    out = fa.decode_kv(cb, SEED, codes, norms)
+    torch.cuda.synchronize()
+    got = bf16_to_f32(out[0, 0].index_select(0, idx)).astype(np.float64)
+    s = o_signs.signs(SEED, 128)
+    oc2, on2 = oc.reshape(-1, 128), np.asarray(on).reshape(-1, 1)
+    ref = (codec.decode_u8(oc2, on2, s) if bits == 8 else
+           codec.decode_mse(oc2, on2, s, o_cb.codebook(bits)[1])).reshape(got.shape)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert rel.max() < 4e-3, rel.max()   # bf16 output: ~2^-9 relative per element
+    del out, codes, norms
+    with pytest.raises(fa.FaTqError):
+        fa.encode(cb, SEED, torch.empty((1, 1, T + 1, 128), dtype=torch.bfloat16, device="cuda"))

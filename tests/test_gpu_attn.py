@@ -162,3 +162,44 @@ def test_attn_long_context_full_sampled(gpu_lib):
     heads = [(0, 0), (1, 9), (3, 31)]
     _run(gpu_lib, q, kp, kn, vp, vn, lens, w.k_bits, w.v_bits, 1 / np.sqrt(128), heads=heads,
          where="long_context")
+
+
+def test_attn_largest_t_max(gpu_lib):
+    """The largest t_max of the matrix-core path (2^25 - 1 slots: K4 code rows of
+    2 GiB - 64 B, byte offsets near 2^31).  Every slot holds a cold key (codes 0)
+    except three hot ones (codes 15) at slots 0, 2^24 + 5 and t_max - 1; with key
+    norms of 60000 and a query along the hot direction the cold slots' softmax
+    weights are exactly zero in fp32 and in fp64, so the output is the oracle's
+    attention over the three hot slots (their values random codes and norms)."""
+    from oracle import rotation
+    torch = _torch()
+    fa = gpu_lib
+    T = (1 << 25) - 1
+    hot = [0, (1 << 24) + 5, T - 1]
+    say(f"attn largest t_max={T}")
+    dev = "cuda"
+    kp = torch.zeros((1, 1, T, 1, 64), dtype=torch.uint8, device=dev)
+    kn = torch.full((1, 1, T, 1), 60000.0, dtype=torch.float16, device=dev).view(torch.int16)
+    vp = torch.zeros((1, 1, T, 1, 32), dtype=torch.uint8, device=dev)
+    vn = torch.full((1, 1, T, 1), 1.0, dtype=torch.float16, device=dev).view(torch.int16)
+    rng = np.random.default_rng(5)
+    hv = rng.integers(0, 256, (3, 32), dtype=np.uint8)
+    hn = (1.0 + rng.random(3)).astype(np.float16)
+    for i, t in enumerate(hot):
+        kp[0, 0, t] = 0xFF
+        vp[0, 0, t, 0] = torch.from_numpy(hv[i]).to(dev)
+        vn[0, 0, t, 0] = int(hn[i:i + 1].view(np.int16)[0])
+    s = o_signs.signs(SEED, 128)
+    q = rotation.inverse64(np.full((1, 4, 128), 0.1), s).astype(np.float32)   # R q = 0.1
+    scale = 1 / np.sqrt(128)
+    ck, cv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    out = fa.attn_decode(ck, cv, SEED, torch.from_numpy(q).to(dev), kp, kn, vp, vn,
+                         torch.tensor([T], dtype=torch.int32, device=dev), scale)
+    torch.cuda.synchronize()
+    kp3 = np.full((1, 1, 3, 1, 64), 0xFF, np.uint8)
+    kn3 = np.full((1, 1, 3, 1), 60000.0, np.float16)
+    ref = o_att.attend_fused(q, kp3, kn3, hv.reshape(1, 1, 3, 1, 32), hn.reshape(1, 1, 3, 1),
+                             [3], 4, 2, o_cb.codebook(4)[1], o_cb.codebook(2)[1], s, scale)
+    err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+    say(f"largest t_max: max abs err {err:.3e}")
+    assert err <= ATTN_MAX_ABS

@@ -48,38 +48,9 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
   b = u - v;
 }
 
-// Pack the 8 codes of chunk c of one block and store them at the packed row
-// ([Spec] "Step 3: Packing", least-significant field first; 3 bits as the split
-// planes of [turboq] block_turboq3_0).
-template <int BITS>
-__device__ __forceinline__ void store_chunk(uint8_t* row, int c, const uint32_t (&code)[8]) {
-  if constexpr (BITS == 4) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
-    reinterpret_cast<uint32_t*>(row)[c] = w;
-  } else if constexpr (BITS == 2) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= code[i] << (2 * i);
-    reinterpret_cast<uint16_t*>(row)[c] = static_cast<uint16_t>(w);
-  } else if constexpr (BITS == 3) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo |= (code[i] & 3u) << (2 * i);
-      hi |= ((code[i] >> 2) & 1u) << i;
-    }
-    reinterpret_cast<uint16_t*>(row)[c] = static_cast<uint16_t>(lo);
-    row[32 + c] = static_cast<uint8_t>(hi);
-  } else {
-    uint2 w;
-    w.x = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
-    w.y = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
-    reinterpret_cast<uint2*>(row)[c] = w;
-  }
-}
-
+// The 8 codes of chunk c (elements 8c .. 8c + 7) of one packed block row ([Spec]
+// "Step 3: Packing", least-significant field first; 3 bits as the split planes of
+// [turboq] block_turboq3_0).
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint8_t* row, int c, uint32_t (&code)[8]) {
   if constexpr (BITS == 4) {

@@ -154,19 +154,45 @@ def decode_mse(codes: np.ndarray, norms16: np.ndarray, s: np.ndarray,
     return inverse64(v.reshape(codes.shape), s, s2)
 
 
+def pow2_length(d: int) -> int:
+    """Transform length of a head_dim-d vector: d itself when a power of two, else
+    the next power of two ([Spec] "Hadamard Transform Detail": a head_dim that is not
+    a power of two is zero-padded to the next one, transformed, and the padding is
+    dropped again after the inverse)."""
+    n = 1
+    while n < d:
+        n <<= 1
+    return n
+
+
+def pad_pow2(x: np.ndarray) -> np.ndarray:
+    """x [..., d] zero-padded to [..., pow2_length(d)] (same dtype)."""
+    x = np.asarray(x)
+    d = x.shape[-1]
+    dp = pow2_length(d)
+    if dp == d:
+        return x
+    out = np.zeros(x.shape[:-1] + (dp,), x.dtype)
+    out[..., :d] = x
+    return out
+
+
 def encode_mse_whole(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
     """Canonical fp32 encode with one rotation over the whole vector and the codebook
     of dimension d = head_dim ([Spec] "Step 1" and "Step 2": R is d x d, one codebook
-    per (head_dim, bits)); d a power of two.  One norm per vector.
+    per (head_dim, bits)).  A head_dim that is not a power of two is zero-padded to
+    d' = the next power of two first, and the transform, the codebook and the codes
+    are those of length d' (s has d' signs).  One norm per vector (the padding adds
+    nothing to it).
 
-    n32 = RN32(sqrt(pairwise sum of RN32(x_i^2))) over index bits 0 .. log2(d) - 1;
-    h = fp32 butterflies of s * x in stage order 1, 2, ..., d/2; g = RN32(c_d / n32)
-    with c_d = RN32(1/sqrt(d)) (0 when n32 == 0); u = RN32(h * g);
-    code = #{j : b_j < u}.  Returns (codes uint8 [..., d], norms fp16 [...], u)."""
+    n32 = RN32(sqrt(pairwise sum of RN32(x_i^2))) over index bits 0 .. log2(d') - 1;
+    h = fp32 butterflies of s * x in stage order 1, 2, ..., d'/2; g = RN32(c / n32)
+    with c = RN32(1/sqrt(d')) (0 when n32 == 0); u = RN32(h * g);
+    code = #{j : b_j < u}.  Returns (codes uint8 [..., d'], norms fp16 [...], u)."""
     x = np.asarray(x)
     assert x.dtype == np.float32
+    x = pad_pow2(x)
     d = x.shape[-1]
-    assert d & (d - 1) == 0, "the whole-vector transform needs a power-of-two length"
     n32 = norm_f32(x)
     h, _ = fwht_stages(x * np.asarray(s, np.float32), dtype=np.float32)
     c_d = np.float32(1.0 / np.sqrt(float(d)))
@@ -178,11 +204,14 @@ def encode_mse_whole(x: np.ndarray, s: np.ndarray, boundaries: np.ndarray):
 
 
 def decode_mse_whole(codes: np.ndarray, norms16: np.ndarray, s: np.ndarray,
-                     centroids: np.ndarray) -> np.ndarray:
-    """fp64 decode of the whole-vector mode: x_hat = s * H_d (n16 * c[code]) / sqrt(d)."""
+                     centroids: np.ndarray, head_dim: int | None = None) -> np.ndarray:
+    """fp64 decode of the whole-vector mode: x_hat = s * H_d' (n16 * c[code]) / sqrt(d')
+    over the d' codes, then the first head_dim coordinates (the padding is dropped;
+    head_dim defaults to d')."""
     c = np.asarray(centroids, np.float32).astype(np.float64)
     n = np.asarray(norms16, np.float16).astype(np.float64)
-    return inverse64_whole(c[np.asarray(codes)] * n[..., None], s)
+    x = inverse64_whole(c[np.asarray(codes)] * n[..., None], s)
+    return x if head_dim is None else x[..., :head_dim]
 
 
 def encode_u8(x: np.ndarray, s: np.ndarray, s2: np.ndarray | None = None):

@@ -198,7 +198,7 @@ def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph of 8 calls"}
 
 
-def restore_bf16(fa, w, cbk, seed, caches, reps=20) -> dict:
+def restore_bf16(fa, w, cbk, seed, caches, reps=64) -> dict:
     """GPU time of fa_tq_decode_kv restoring the whole K cache to bf16 in the LMCache
     layout [tokens][heads * head_dim] (the serde restore path), over the rotating
     cache copies of the step."""
@@ -418,8 +418,8 @@ def main():
             rec["vectors_per_s"] = round(nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false, false>",
-             "encode_v": f"encode_kernel<{w.v_bits}, true, false, false>"}.get(dom, dom)
+    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false, false, false>",
+             "encode_v": f"encode_kernel<{w.v_bits}, true, false, false, false>"}.get(dom, dom)
     traffic = traffic_for(kname)
     roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],

@@ -63,13 +63,17 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  *     squares summed pairwise as for the input norm), so a decoded block keeps its
  *     input norm up to the fp16 rounding of the stored value.
  *   FA_TQ_WHOLE_VECTOR (encode and fa_tq_decode_kv only; no other flag): [Spec]
- *     "Step 1"/"Step 2" read literally, one rotation R = D H_d / sqrt(d) over the
- *     whole head_dim d (128 or 256) with a codebook built for dim = d, and one fp16
- *     norm per vector: norms[B][Hkv][T_max] instead of [B][Hkv][T_max][nblk].  The
- *     codes are packed per consecutive 128 elements exactly as the blocked layout.
- *     Arithmetic as the blocked mode over d elements (squares summed over index
- *     bits 0, 1, ... in order, butterflies in stage order 1 .. d/2, c_d =
- *     fp32(1/sqrt(d))).
+ *     "Step 1"/"Step 2" read literally, one rotation R = D H_d' / sqrt(d') over the
+ *     whole head_dim d with a codebook built for dim = d', and one fp16 norm per
+ *     vector: norms[B][Hkv][T_max] instead of [B][Hkv][T_max][nblk].  d' = d for d
+ *     = 128 or 256; any other d in (64, 256] that is a multiple of 8 is zero-padded
+ *     to d' = 128 or 256, the next power of two ([Spec] "Hadamard Transform
+ *     Detail"): the codes are those of all d' transformed elements (nblk = d'/128),
+ *     the signs D are draws 0 .. d'-1, and decoding keeps the first d outputs of the
+ *     inverse.  The codes are packed per consecutive 128 elements exactly as the
+ *     blocked layout.  Arithmetic as the blocked mode over d' elements (squares
+ *     summed over index bits 0, 1, ... in order, the padding adding zeros;
+ *     butterflies in stage order 1 .. d'/2, c = fp32(1/sqrt(d'))).
  * Entry points without _ex use flags 0.
  */
 #define FA_TQ_TWO_SIGNS 1u
@@ -86,7 +90,7 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  * the arrays are unused and must be zero.
  */
 typedef struct {
-    int32_t dim;            /* 128 (per QK block); head_dim for FA_TQ_WHOLE_VECTOR */
+    int32_t dim;            /* 128 (per QK block); d' (128 or 256) for FA_TQ_WHOLE_VECTOR */
     int32_t bits;           /* 2, 3, 4, or 8 */
     int32_t levels;         /* 1 << bits */
     float boundaries[15];   /* levels - 1 used, strictly ascending */
@@ -154,7 +158,9 @@ fa_tq_status fa_tq_encode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
                           const int32_t *t0, int32_t t_max,
                           uint8_t *codes, uint16_t *norms, void *stream);
 
-/* fa_tq_encode with variant flags (FA_TQ_TWO_SIGNS, FA_TQ_NORM_CORRECT). */
+/* fa_tq_encode with variant flags (FA_TQ_TWO_SIGNS, FA_TQ_NORM_CORRECT, or
+ * FA_TQ_WHOLE_VECTOR alone; in the last, codes hold nblk = d'/128 blocks per
+ * vector and x holds head_dim elements). */
 fa_tq_status fa_tq_encode_ex(const fa_tq_codebook *cb, uint64_t seed, uint32_t flags,
                              int32_t head_dim, const void *x, fa_tq_dtype x_dtype,
                              fa_tq_layout x_layout, int32_t batch, int32_t n_kv_heads,
@@ -183,7 +189,8 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook *cb, uint64_t seed, int32_t head_
  * stride_h = head_dim, stride_t = hidden with batch 1.
  *   codes, norms: device, SoA layout above (T_max = t_max, Hkv = n_kv_heads).
  *   out: device, 16-byte aligned; strides non-negative multiples of 8 elements.
- * flags: 0, FA_TQ_TWO_SIGNS or FA_TQ_WHOLE_VECTOR (how the cache was encoded).
+ * flags: 0, FA_TQ_TWO_SIGNS or FA_TQ_WHOLE_VECTOR (how the cache was encoded; in
+ * the last, codes hold d'/128 blocks per vector and head_dim elements are written).
  * batch, n_kv_heads or n_tokens == 0 is an OK no-op; n_tokens <= t_max.
  */
 fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, uint32_t flags,

@@ -183,13 +183,21 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def cache_buffers(batch, n_kv_heads, t_max, head_dim, bits, device="cuda"):
-    """Allocate (codes, norms) for the packed SoA cache layout."""
+def whole_length(head_dim: int) -> int:
+    """Transform length of the whole-vector mode: head_dim zero-padded to 128 or 256."""
+    return QK if head_dim <= QK else 2 * QK
+
+
+def cache_buffers(batch, n_kv_heads, t_max, head_dim, bits, device="cuda", flags: int = 0):
+    """Allocate (codes, norms) for the packed SoA cache layout (with WHOLE_VECTOR:
+    whole_length(head_dim) / 128 code blocks and one norm per vector)."""
     import torch
-    nblk = head_dim // QK
+    whole = bool(flags & WHOLE_VECTOR)
+    nblk = (whole_length(head_dim) if whole else head_dim) // QK
     codes = torch.empty((batch, n_kv_heads, t_max, nblk, code_bytes(bits)), dtype=torch.uint8,
                         device=device)
-    norms = torch.empty((batch, n_kv_heads, t_max, nblk), dtype=torch.int16, device=device)
+    norms = torch.empty((batch, n_kv_heads, t_max, 1 if whole else nblk), dtype=torch.int16,
+                        device=device)
     return codes, norms
 
 
@@ -199,9 +207,7 @@ def encode(cb: Codebook, seed: int, x, t_max: int | None = None, t0=None, codes=
     B, H, T, d = x.shape
     t_max = T if t_max is None else t_max
     if codes is None or norms is None:
-        codes, norms = cache_buffers(B, H, t_max, d, cb.bits, x.device)
-        if flags & WHOLE_VECTOR:        # one norm per vector
-            norms = norms[..., :1].contiguous()
+        codes, norms = cache_buffers(B, H, t_max, d, cb.bits, x.device, flags)
     encode_call(cb, seed, x, codes, norms, t_max, t0, stream, flags)()
     return codes, norms
 
@@ -220,15 +226,23 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
     return out
 
 
+def _expect_blocks(nblk, head_dim, flags):
+    want = (whole_length(head_dim) if flags & WHOLE_VECTOR else head_dim) // QK
+    if nblk != want:
+        raise ValueError(f"a cache of {nblk} blocks per vector for head_dim {head_dim}")
+
+
 def decode_kv(cb: Codebook, seed: int, codes, norms, n_tokens: int | None = None, out=None,
-              out_dtype=None, stream=None, flags: int = 0):
+              out_dtype=None, stream=None, flags: int = 0, head_dim: int | None = None):
     """Restore a packed cache [B, Hkv, T_max, nblk, cb] to a K or V tensor: tokens
     [0, n_tokens) of every row into out [B, Hkv, n_tokens, head_dim] (any strides
-    with channel stride 1, bf16 or float32; bf16 by default)."""
+    with channel stride 1, bf16 or float32; bf16 by default).  head_dim defaults to
+    out's last size, else nblk * 128 (a padded whole-vector cache needs it)."""
     import torch
     lib = load()
     B, H, t_max, nblk, cbytes = codes.shape
-    d = nblk * QK
+    d = head_dim or (out.shape[3] if out is not None else nblk * QK)
+    _expect_blocks(nblk, d, flags)
     n_tokens = t_max if n_tokens is None else n_tokens
     if cbytes != code_bytes(cb.bits):
         raise ValueError(f"code rows of {cbytes} bytes for {cb.bits}-bit codes")
@@ -253,7 +267,8 @@ def decode_kv_call(cb: Codebook, seed: int, codes, norms, out, n_tokens: int | N
     """``decode_kv`` with its arguments marshalled once (see ``encode_call``)."""
     lib = load()
     B, H, t_max, nblk, cbytes = codes.shape
-    d = nblk * QK
+    d = out.shape[3]
+    _expect_blocks(nblk, d, flags)
     n_tokens = t_max if n_tokens is None else n_tokens
     if tuple(out.shape) != (B, H, n_tokens, d) or out.stride(3) != 1:
         raise ValueError(f"out {tuple(out.shape)} for a cache of {tuple(codes.shape)}")

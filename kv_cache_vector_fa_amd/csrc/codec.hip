@@ -306,20 +306,24 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // One block's input in the quad layout from byte offset `off` of resource r.
+// dead[k] is 0, or kOOB for a chunk that lies in the zero padding of a vector: or-ed
+// into its offset (every in-range offset is below 2^31) it makes the load return
+// zeros without reading past the vector.
 template <bool BF16>
-__device__ __forceinline__ void load_raw(Rsrc r, uint32_t off, int q, RawBlock<BF16>& b) {
+__device__ __forceinline__ void load_raw(Rsrc r, uint32_t off, int q, const uint32_t (&dead)[4],
+                                         RawBlock<BF16>& b) {
   if constexpr (BF16) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       b.w[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             r, off + 16 * (q + 4 * k), 0, 0));
+                                             r, (off + 16 * (q + 4 * k)) | dead[k], 0, 0));
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      b.w[2 * k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 r, off + 32 * (q + 4 * k), 0, 0));
-      b.w[2 * k + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     r, off + 32 * (q + 4 * k) + 16, 0, 0));
+      const uint32_t o = (off + 32 * (q + 4 * k)) | dead[k];
+      b.w[2 * k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+      b.w[2 * k + 1] =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o + 16, 0, 0));
     }
   }
 }
@@ -392,10 +396,12 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
 // WV: whole-vector mode for head_dim 256 ([Spec] "Step 1", one 256-point transform;
 // nblk = 2): the two quads of a vector also run the last butterfly stage between
 // them, share one norm (and store it once) and scale by RN32(1/16).
-template <int BITS, bool BF16, bool NC, bool WV>
+// PAD: a.dim < QK * nblk; the chunks at or past a.dim load as zeros.
+template <int BITS, bool BF16, bool NC, bool WV, bool PAD>
 __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
                                                           SignWords sw) {
   static_assert(!WV || (BITS != 8 && !NC), "whole-vector mode: 2-4 bit codebooks");
+  static_assert(!PAD || (BITS != 8 && !NC), "padding: whole-vector mode only");
   constexpr int CB = code_bytes_of<BITS>();
   typedef typename std::conditional<NC, uint4, uint2>::type Cell;
   __shared__ Cell cells[BITS == 8 ? 1 : kCells];
@@ -408,7 +414,7 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   const int t_step = a.t_step;   // gridDim.x * quads per workgroup / nblk
   const int rows = a.batch * a.heads;
   constexpr uint32_t ES = BF16 ? 2 : 4;   // input element bytes
-  const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + QK * a.nblk) * ES);
+  const uint32_t xbytes = static_cast<uint32_t>(((a.tokens - 1) * a.st + a.dim) * ES);
   const uint32_t cbytes = static_cast<uint32_t>(a.t_max) * a.nblk * CB;
   const uint32_t nbytes = static_cast<uint32_t>(a.t_max) * a.nblk * 2;
   struct Row {
@@ -440,10 +446,15 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   if (row >= rows) return;   // uniform over the workgroup
   const uint32_t sbits = sw.w[j][q];
   const uint32_t s2bits = sw.two ? sw.w2[j][q] : 0u;
+  uint32_t dead[4] = {0u, 0u, 0u, 0u};
+  if constexpr (PAD) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dead[k] = QK * j + 8 * (q + 4 * k) >= a.dim ? kOOB : 0u;
+  }
   Row R = open_row(row);
   int t = t_first;
   RawBlock<BF16> ba, bb;
-  load_raw<BF16>(R.rx, xoff(t), q, ba);
+  load_raw<BF16>(R.rx, xoff(t), q, dead, ba);
   if constexpr (BITS != 8) {
     fill_cells(cells, tab);
     lds_barrier();
@@ -606,12 +617,12 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   for (;;) {
     dummy_stores<BITS>(R.rc, R.rn);
     while (__builtin_amdgcn_readfirstlane(t) < a.tokens) {
-      load_raw<BF16>(R.rx, xoff(t + t_step), q, bb);
+      load_raw<BF16>(R.rx, xoff(t + t_step), q, dead, bb);
       __builtin_amdgcn_sched_barrier(0);
       process(ba, t);
       t += t_step;
       if (__builtin_amdgcn_readfirstlane(t) >= a.tokens) break;
-      load_raw<BF16>(R.rx, xoff(t + t_step), q, ba);
+      load_raw<BF16>(R.rx, xoff(t + t_step), q, dead, ba);
       __builtin_amdgcn_sched_barrier(0);
       process(bb, t);
       t += t_step;
@@ -620,7 +631,7 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
     if (row >= rows) break;
     R = open_row(row);
     t = t_first;
-    load_raw<BF16>(R.rx, xoff(t), q, ba);
+    load_raw<BF16>(R.rx, xoff(t), q, dead, ba);
   }
 }
 
@@ -632,10 +643,12 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
 // difference, a sign folded into the final scale.  WV: whole vectors of head_dim 256
 // (nblk = 2): one norm per vector, the second quad's chunks in reversed lane order and
 // the stage between the vector's two blocks by row_half_mirror, scale 1/16.
-template <int BITS, bool BF16_OUT, bool WV>
+// PAD: d.dim < QK * nblk; the chunks at or past d.dim (the padding) are not stored.
+template <int BITS, bool BF16_OUT, bool WV, bool PAD>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
                                                           SignWords sw) {
   static_assert(!WV || BITS != 8, "whole-vector mode: 2-4 bit codebooks");
+  static_assert(!PAD || BITS != 8, "padding: whole-vector mode only");
   constexpr int CB = code_bytes_of<BITS>();
   __shared__ float cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
@@ -714,6 +727,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = flip_sign(v[k][i] * scale, (sbits >> (8 * k + i)) & 1u);
         const int c = q + 4 * k;
+        if (PAD && QK * j + 8 * c >= d.dim) continue;
         if constexpr (BF16_OUT) {
           // v_cvt_pk_bf16_f32: two fp32 to bf16, round to nearest even
           uint32_t w[4];
@@ -768,29 +782,38 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
   const dim3 grid = encode_grid(a), block(kEncThreads);
   EncodeLaunch la = a;
   la.t_step = static_cast<int32_t>(grid.x * (kEncThreads / 4) / a.nblk);
-#define FATQ_ENC(B, F, N, W) \
-  hipLaunchKernelGGL((encode_kernel<B, F, N, W>), grid, block, 0, stream, la, tab, sw)
-#define FATQ_ENC_BITS(F, N)                     \
-  switch (tab.bits) {                           \
-    case 2: FATQ_ENC(2, F, N, false); break;    \
-    case 3: FATQ_ENC(3, F, N, false); break;    \
-    case 4: FATQ_ENC(4, F, N, false); break;    \
-    default: FATQ_ENC(8, F, false, false); break; \
+#define FATQ_ENC(B, F, N, W, P) \
+  hipLaunchKernelGGL((encode_kernel<B, F, N, W, P>), grid, block, 0, stream, la, tab, sw)
+#define FATQ_ENC_BITS(F, N)                            \
+  switch (tab.bits) {                                  \
+    case 2: FATQ_ENC(2, F, N, false, false); break;    \
+    case 3: FATQ_ENC(3, F, N, false, false); break;    \
+    case 4: FATQ_ENC(4, F, N, false, false); break;    \
+    default: FATQ_ENC(8, F, false, false, false); break; \
   }
-#define FATQ_ENC_WV(F)                          \
-  switch (tab.bits) {                           \
-    case 2: FATQ_ENC(2, F, false, true); break; \
-    case 3: FATQ_ENC(3, F, false, true); break; \
-    default: FATQ_ENC(4, F, false, true); break; \
+#define FATQ_ENC_WV(F, W, P)                        \
+  switch (tab.bits) {                               \
+    case 2: FATQ_ENC(2, F, false, W, P); break;     \
+    case 3: FATQ_ENC(3, F, false, W, P); break;     \
+    default: FATQ_ENC(4, F, false, W, P); break;    \
   }
-  // head_dim 128 in the whole-vector mode is the blocked encode itself
-  if (whole && a.nblk == 2) {
-    if (a.x_is_bf16) { FATQ_ENC_WV(true) } else { FATQ_ENC_WV(false) }
+#define FATQ_ENC_WHOLE(F)                                          \
+  if (a.nblk == 2) {                                               \
+    if (pad) { FATQ_ENC_WV(F, true, true) } else { FATQ_ENC_WV(F, true, false) } \
+  } else {                                                         \
+    FATQ_ENC_WV(F, false, true)                                    \
+  }
+  // unpadded head_dim 128 in the whole-vector mode is the blocked encode itself
+  const bool pad = a.dim != QK * a.nblk;
+  if (pad && !whole) return hipErrorInvalidValue;
+  if (whole && (a.nblk == 2 || pad)) {
+    if (a.x_is_bf16) { FATQ_ENC_WHOLE(true) } else { FATQ_ENC_WHOLE(false) }
   } else if (a.x_is_bf16) {
     if (norm_correct) { FATQ_ENC_BITS(true, true) } else { FATQ_ENC_BITS(true, false) }
   } else {
     if (norm_correct) { FATQ_ENC_BITS(false, true) } else { FATQ_ENC_BITS(false, false) }
   }
+#undef FATQ_ENC_WHOLE
 #undef FATQ_ENC_WV
 #undef FATQ_ENC_BITS
 #undef FATQ_ENC
@@ -820,28 +843,37 @@ dim3 decode_grid(const DecodeLaunch& d) {
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          bool whole, hipStream_t stream) {
   const dim3 grid = decode_grid(d), block(kThreads);
-#define FATQ_DEC(B, F, W) \
-  hipLaunchKernelGGL((decode_kernel<B, F, W>), grid, block, 0, stream, d, tab, sw)
-#define FATQ_DEC_BITS(F)                 \
-  switch (tab.bits) {                    \
-    case 2: FATQ_DEC(2, F, false); break; \
-    case 3: FATQ_DEC(3, F, false); break; \
-    case 4: FATQ_DEC(4, F, false); break; \
-    default: FATQ_DEC(8, F, false); break; \
+#define FATQ_DEC(B, F, W, P) \
+  hipLaunchKernelGGL((decode_kernel<B, F, W, P>), grid, block, 0, stream, d, tab, sw)
+#define FATQ_DEC_BITS(F)                        \
+  switch (tab.bits) {                           \
+    case 2: FATQ_DEC(2, F, false, false); break; \
+    case 3: FATQ_DEC(3, F, false, false); break; \
+    case 4: FATQ_DEC(4, F, false, false); break; \
+    default: FATQ_DEC(8, F, false, false); break; \
   }
-#define FATQ_DEC_WV(F)                   \
-  switch (tab.bits) {                    \
-    case 2: FATQ_DEC(2, F, true); break;  \
-    case 3: FATQ_DEC(3, F, true); break;  \
-    default: FATQ_DEC(4, F, true); break; \
+#define FATQ_DEC_WV(F, W, P)                \
+  switch (tab.bits) {                       \
+    case 2: FATQ_DEC(2, F, W, P); break;    \
+    case 3: FATQ_DEC(3, F, W, P); break;    \
+    default: FATQ_DEC(4, F, W, P); break;   \
   }
-  if (whole && d.nblk == 2) {
-    if (d.out_bf16) { FATQ_DEC_WV(true) } else { FATQ_DEC_WV(false) }
+#define FATQ_DEC_WHOLE(F)                                          \
+  if (d.nblk == 2) {                                               \
+    if (pad) { FATQ_DEC_WV(F, true, true) } else { FATQ_DEC_WV(F, true, false) } \
+  } else {                                                         \
+    FATQ_DEC_WV(F, false, true)                                    \
+  }
+  const bool pad = d.dim != QK * d.nblk;
+  if (pad && !whole) return hipErrorInvalidValue;
+  if (whole && (d.nblk == 2 || pad)) {
+    if (d.out_bf16) { FATQ_DEC_WHOLE(true) } else { FATQ_DEC_WHOLE(false) }
   } else if (d.out_bf16) {
     FATQ_DEC_BITS(true)
   } else {
     FATQ_DEC_BITS(false)
   }
+#undef FATQ_DEC_WHOLE
 #undef FATQ_DEC_WV
 #undef FATQ_DEC_BITS
 #undef FATQ_DEC

@@ -159,11 +159,18 @@ fatq::SignWords make_sign_words(uint64_t seed, int head_dim, bool two = false) {
   return sw;
 }
 
-// Whole-vector mode: head_dim 128 or 256, a 2-4 bit codebook of that dimension.
+// Whole-vector mode: transform length of a head_dim-d vector, d itself for 128 and
+// 256, else the next of the two ([Spec] "Hadamard Transform Detail": a head_dim that
+// is not a power of two is zero-padded to the next one).
+int32_t whole_length(int32_t head_dim) { return head_dim <= 128 ? 128 : 256; }
+
+// Whole-vector mode: 64 < head_dim <= 256, a multiple of 8 (one 16-byte bf16 chunk),
+// and a 2-4 bit codebook.
 fa_tq_status check_whole(const fa_tq_codebook* cb, int32_t head_dim, const char* who) {
-  if (head_dim != 128 && head_dim != 256)
-    return fail(FA_TQ_EUNSUPPORTED, "%s: whole-vector mode for head_dim 128 or 256 (got %d)",
-                who, head_dim);
+  if (head_dim <= 64 || head_dim > 256 || head_dim % 8 != 0)
+    return fail(FA_TQ_EUNSUPPORTED,
+                "%s: whole-vector mode for head_dim in (64, 256], a multiple of 8 (got %d)", who,
+                head_dim);
   if (cb && cb->bits == 8)
     return fail(FA_TQ_EUNSUPPORTED, "%s: whole-vector mode needs a 2-4 bit codebook", who);
   return ok();
@@ -305,9 +312,11 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
       flags, FA_TQ_TWO_SIGNS | FA_TQ_NORM_CORRECT | (ring ? 0u : FA_TQ_WHOLE_VECTOR), cb, who);
   if (st != FA_TQ_OK) return st;
   if (whole && (st = check_whole(cb, head_dim, who)) != FA_TQ_OK) return st;
-  if ((st = check_codebook(cb, who, true, &tab, whole ? head_dim : fatq::QK)) != FA_TQ_OK)
+  // transform length: head_dim, or its zero-padded length in the whole-vector mode
+  const int32_t dt = whole ? whole_length(head_dim) : head_dim;
+  if ((st = check_codebook(cb, who, true, &tab, whole ? dt : fatq::QK)) != FA_TQ_OK)
     return st;
-  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (!whole && (st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
   if (x_dtype != FA_TQ_F32 && x_dtype != FA_TQ_BF16)
@@ -326,7 +335,7 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   // byte offsets below 2^31.
   const int64_t esize = x_dtype == FA_TQ_BF16 ? 2 : 4;
   const int64_t xrow = ((static_cast<int64_t>(n_tokens) - 1) * x_layout.stride_t + head_dim) * esize;
-  const int64_t crow = static_cast<int64_t>(t_max) * (head_dim / fatq::QK) * fa_tq_code_bytes(cb->bits);
+  const int64_t crow = static_cast<int64_t>(t_max) * (dt / fatq::QK) * fa_tq_code_bytes(cb->bits);
   if (xrow >= (int64_t{1} << 31) || crow >= (int64_t{1} << 31))
     return fail(FA_TQ_EUNSUPPORTED, "%s: one (batch, head) row spans 2 GiB or more", who);
   if (check_only) return ok();
@@ -338,14 +347,15 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   a.batch = batch;
   a.heads = n_kv_heads;
   a.tokens = n_tokens;
-  a.nblk = head_dim / fatq::QK;
+  a.nblk = dt / fatq::QK;
+  a.dim = head_dim;
   a.t_max = t_max;
   a.t0 = t0;
   a.ring = ring ? 1 : 0;
   a.codes = codes;
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
+  const fatq::SignWords sw = make_sign_words(seed, dt, flags & FA_TQ_TWO_SIGNS);
   return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0, whole,
                                       static_cast<hipStream_t>(stream)),
                   who);
@@ -527,6 +537,7 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
   d.sh = 0;
   d.st = head_dim;
   d.out_bf16 = 0;
+  d.dim = head_dim;
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
   return launched(fatq::launch_decode(d, tab, sw, false, static_cast<hipStream_t>(stream)),
                   "fa_tq_decode");
@@ -543,9 +554,10 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
   fa_tq_status st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_WHOLE_VECTOR, nullptr, who);
   if (st != FA_TQ_OK) return st;
   if (whole && (st = check_whole(cb, head_dim, who)) != FA_TQ_OK) return st;
-  if ((st = check_codebook(cb, who, true, &tab, whole ? head_dim : fatq::QK)) != FA_TQ_OK)
+  const int32_t dt = whole ? whole_length(head_dim) : head_dim;   // transform length
+  if ((st = check_codebook(cb, who, true, &tab, whole ? dt : fatq::QK)) != FA_TQ_OK)
     return st;
-  if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
+  if (!whole && (st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
   if (n_tokens > t_max)
@@ -566,13 +578,14 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
   d.tokens = n_tokens;
   d.t_max = t_max;
   d.heads = n_kv_heads;
-  d.nblk = head_dim / fatq::QK;
+  d.nblk = dt / fatq::QK;
   d.out = out;
   d.sb = out_layout.stride_b;
   d.sh = out_layout.stride_h;
   d.st = out_layout.stride_t;
   d.out_bf16 = out_dtype == FA_TQ_BF16;
-  const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
+  d.dim = head_dim;
+  const fatq::SignWords sw = make_sign_words(seed, dt, flags & FA_TQ_TWO_SIGNS);
   return launched(fatq::launch_decode(d, tab, sw, whole, static_cast<hipStream_t>(stream)),
                   who);
 }

@@ -53,11 +53,15 @@ struct EncodeLaunch {
   uint16_t* norms;
   int32_t x_is_bf16;
   int32_t t_step;        // token stride of one quad (set by the launcher from its grid)
+  int32_t dim;           // input elements per vector (head_dim); below QK * nblk, the
+                         // rest of the transform's input is zero padding
 };
 
 // norm_correct: store n / ||c[codes]|| ([turboq] "Encode pipeline" step 4; bits 2-4).
-// whole: whole-vector mode ([Spec] "Step 1": one rotation over head_dim = 128 or 256,
-// one norm per vector, norms[rows][t_max]; codes as the blocked layout).
+// whole: whole-vector mode ([Spec] "Step 1": one rotation over the transform length
+// QK * nblk = 128 or 256, one norm per vector, norms[rows][t_max]; codes as the
+// blocked layout).  dim < QK * nblk (whole mode only): the vector is zero-padded to
+// the transform length ([Spec] "Hadamard Transform Detail").
 hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWords& sw,
                          bool norm_correct, bool whole, hipStream_t stream);
 // Decode of tokens [0, tokens) of `rows` cache rows of t_max slots each (row =
@@ -70,6 +74,8 @@ struct DecodeLaunch {
   void* out;
   int64_t sb, sh, st;
   int32_t out_bf16;
+  int32_t dim;   // output elements per vector; below QK * nblk (whole mode only) the
+                 // transform's last outputs are the padding, not stored
 };
 
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,

@@ -22,19 +22,23 @@ def _torch():
 
 
 def _check(fa, x, bits, where, t_max=None, t0=None):
+    """Encode x [B, H, T, d] in the whole-vector mode (d zero-padded to the transform
+    length d' when it is not 128 or 256), compare codes and norms with the oracle,
+    then decode back (fp32, the first d outputs) against the fp64 oracle decode."""
     torch = _torch()
     B, H, T, d = x.shape
-    cb = fa.codebook_init(d, bits)
+    dp = fa.whole_length(d)
+    cb = fa.codebook_init(dp, bits)
     t_max = T if t_max is None else t_max
-    codes, norms = fa.cache_buffers(B, H, t_max, d, bits, x.device)
-    norms = norms[..., :1].contiguous()
+    codes, norms = fa.cache_buffers(B, H, t_max, d, bits, x.device, flags=fa.WHOLE_VECTOR)
+    assert codes.shape[3] == dp // 128 and norms.shape[3] == 1
     codes.fill_(0xAB)
     t0d = None if t0 is None else torch.tensor(t0, dtype=torch.int32, device=x.device)
     fa.encode(cb, SEED, x, t_max=t_max, t0=t0d, codes=codes, norms=norms, flags=fa.WHOLE_VECTOR)
     torch.cuda.synchronize()
     x32 = np.ascontiguousarray(bf16_to_f32(x) if x.dtype == torch.bfloat16 else x.cpu().numpy())
-    b, c = o_cb.codebook(bits, d)
-    oc, on, _ = codec.encode_mse_whole(x32, o_signs.signs(SEED, d), b)
+    b, c = o_cb.codebook(bits, dp)
+    oc, on, _ = codec.encode_mse_whole(x32, o_signs.signs(SEED, dp), b)
     gc, gn = codes.cpu().numpy(), norms.cpu().numpy()
     offs = [0] * B if t0 is None else t0
     flips = 0
@@ -47,13 +51,15 @@ def _check(fa, x, bits, where, t_max=None, t0=None):
         rest[sl] = False
         assert np.all(gc[bb, :, rest] == 0xAB), where
     # decode back (fp32) against the fp64 oracle decode of the oracle's codes
-    out = fa.decode_kv(cb, SEED, codes, norms, out_dtype=torch.float32, flags=fa.WHOLE_VECTOR)
+    out = fa.decode_kv(cb, SEED, codes, norms, out_dtype=torch.float32, flags=fa.WHOLE_VECTOR,
+                       head_dim=d)
     torch.cuda.synchronize()
+    assert out.shape[-1] == d
     g = out.cpu().numpy().astype(np.float64)
     for bb in range(B):
         sl = slice(offs[bb], offs[bb] + T)
         ref = codec.decode_mse_whole(codec.unpack(gc[bb, :, sl], bits), gn[bb, :, sl, 0].view(np.float16),
-                                     o_signs.signs(SEED, d), c)
+                                     o_signs.signs(SEED, dp), c, head_dim=d)
         rel = np.linalg.norm(g[bb, :, sl] - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
         assert rel.max() <= DECODE_REL_L2, (where, rel.max())
     say(f"{where}: {flips} adjacent flips")
@@ -68,6 +74,45 @@ def test_whole_encode_decode(gpu_lib, bits, dtype, d):
     x = torch.randn((2, 3, 257, d), generator=g, device="cuda")
     x = x.to(torch.bfloat16) if dtype == "bf16" else x
     _check(gpu_lib, x, bits, f"whole bits={bits} {dtype} d={d}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [72, 96, 120, 136, 192, 248])
+def test_whole_padded_encode_decode(gpu_lib, bits, dtype, d):
+    """head_dim not a power of two: zero-padded to 128 or 256 for the transform."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(bits * 13 + d)
+    x = torch.randn((2, 3, 131, d), generator=g, device="cuda")
+    x = x.to(torch.bfloat16) if dtype == "bf16" else x
+    _check(gpu_lib, x, bits, f"whole padded bits={bits} {dtype} d={d}")
+
+
+@pytest.mark.parametrize("d", [96, 192])
+def test_whole_padded_reads_and_writes_only_head_dim(gpu_lib, d):
+    """The padding is zeros, not the memory after the vector: an input that is the
+    first d channels of a wider tensor whose other channels hold NaN encodes as the
+    contiguous copy does, and decoding into the first d channels of a wider output
+    leaves the other channels untouched (bf16 and fp32 outputs)."""
+    torch = _torch()
+    fa = gpu_lib
+    dp = fa.whole_length(d)
+    wide = torch.full((2, 3, 70, 320), float("nan"), device="cuda", dtype=torch.bfloat16)
+    wide[..., :d] = torch.randn((2, 3, 70, d), device="cuda").to(torch.bfloat16)
+    x = wide[..., :d]
+    cb = fa.codebook_init(dp, 4)
+    c1, n1 = fa.encode(cb, SEED, x, flags=fa.WHOLE_VECTOR)
+    c2, n2 = fa.encode(cb, SEED, x.contiguous(), flags=fa.WHOLE_VECTOR)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(n1, n2)
+    assert not torch.isnan(n1.view(torch.float16)).any()
+    for dt in (torch.bfloat16, torch.float32):
+        ref = fa.decode_kv(cb, SEED, c1, n1, out_dtype=dt, flags=fa.WHOLE_VECTOR, head_dim=d)
+        big = torch.full((2, 3, 70, 328), 7.0, device="cuda", dtype=dt)
+        fa.decode_kv(cb, SEED, c1, n1, out=big[..., 8:8 + d], flags=fa.WHOLE_VECTOR)
+        torch.cuda.synchronize()
+        assert torch.equal(big[..., 8:8 + d], ref)
+        assert torch.all(big[..., :8] == 7) and torch.all(big[..., 8 + d:] == 7)
 
 
 def test_whole_positions_and_strides(gpu_lib):

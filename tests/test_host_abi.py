@@ -135,11 +135,11 @@ def test_attn_validation_before_launch(lib):
     assert _attn_raw(lib, ck, cv, 128, 0, 32, 8, 64, big) == fa.FA_TQ_OK
 
 
-def _encode_ex_raw(lib, cb, flags, B=1, ptr=1 << 20):
+def _encode_ex_raw(lib, cb, flags, B=1, ptr=1 << 20, head_dim=128):
     P = ctypes.c_void_p(ptr)
-    lay = fa.Layout(128, 128, 128)
-    return lib.fa_tq_encode_ex(ctypes.byref(cb), 42, flags, 128, P, fa.FA_TQ_BF16, lay, B, 1, 1,
-                               None, 1, P, P, None)
+    lay = fa.Layout(256, 256, 256)
+    return lib.fa_tq_encode_ex(ctypes.byref(cb), 42, flags, head_dim, P, fa.FA_TQ_BF16, lay, B,
+                               1, 1, None, 1, P, P, None)
 
 
 def test_variant_flags_validated_before_launch(lib):
@@ -177,3 +177,45 @@ def test_variant_flags_validated_before_launch(lib):
     assert lib.fa_tq_attn_decode_ex(ctypes.byref(c4), ctypes.byref(c2), 42, fa.NORM_CORRECT, 128,
                                     P, 1, P, P, P, P, P, 1, 32, 8, 64, 0.088, P, P, 1 << 40,
                                     None) == fa.FA_TQ_EINVAL
+
+
+def test_whole_vector_head_dims_validated(lib):
+    """Whole-vector mode: head_dim in (64, 256] and a multiple of 8, padded to 128 or
+    256 with the codebook of that length; other head_dims, or a padded head_dim
+    without the flag, are rejected before any launch (batch 0: an OK no-op)."""
+    W = fa.WHOLE_VECTOR
+    c128, c256, c192 = (fa.codebook_init(n, 4) for n in (128, 256, 192))
+    for d, cb in ((72, c128), (96, c128), (120, c128), (136, c256), (192, c256), (248, c256)):
+        assert _encode_ex_raw(lib, cb, W, B=0, head_dim=d) == fa.FA_TQ_OK, d
+    assert _encode_ex_raw(lib, c192, W, B=0, head_dim=192) == fa.FA_TQ_EINVAL   # dim 192 table
+    assert "256" in lib.fa_tq_last_error().decode()
+    assert _encode_ex_raw(lib, c256, W, B=0, head_dim=96) == fa.FA_TQ_EINVAL    # 96 pads to 128
+    for d in (64, 100, 260, 384):
+        assert _encode_ex_raw(lib, c256, W, B=0, head_dim=d) == fa.FA_TQ_EUNSUPPORTED, d
+    assert _encode_ex_raw(lib, c128, 0, B=0, head_dim=192) == fa.FA_TQ_EINVAL
+    P = ctypes.c_void_p(1 << 20)
+    lay = fa.Layout(0, 256, 256)
+    assert lib.fa_tq_decode_kv(ctypes.byref(c256), 42, W, 200, P, P, 0, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay, None) == fa.FA_TQ_OK
+    assert lib.fa_tq_decode_kv(ctypes.byref(c128), 42, W, 200, P, P, 0, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay, None) == fa.FA_TQ_EINVAL
+    assert lib.fa_tq_decode_kv(ctypes.byref(c256), 42, 0, 200, P, P, 0, 1, 1, 1, P,
+                               fa.FA_TQ_BF16, lay, None) == fa.FA_TQ_EINVAL
+
+
+def test_padded_cache_shapes_in_the_binding(lib):
+    """cache_buffers sizes a padded whole-vector cache by the transform length, and
+    decode_kv refuses a cache whose block count does not fit head_dim (no device)."""
+    import torch
+    codes, norms = fa.cache_buffers(2, 3, 5, 192, 4, device="cpu", flags=fa.WHOLE_VECTOR)
+    assert tuple(codes.shape) == (2, 3, 5, 2, 64) and tuple(norms.shape) == (2, 3, 5, 1)
+    codes, norms = fa.cache_buffers(2, 3, 5, 96, 2, device="cpu", flags=fa.WHOLE_VECTOR)
+    assert tuple(codes.shape) == (2, 3, 5, 1, 32) and tuple(norms.shape) == (2, 3, 5, 1)
+    cb = fa.codebook_init(128, 2)
+    with pytest.raises(ValueError):
+        fa.decode_kv(cb, 42, codes, norms, flags=fa.WHOLE_VECTOR, head_dim=192)
+    with pytest.raises(ValueError):
+        fa.decode_kv(cb, 42, codes, norms, head_dim=96)   # blocked mode: 96 is no block count
+    out = torch.empty((2, 3, 5, 200), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.decode_kv_call(cb, 42, codes, norms, out, flags=fa.WHOLE_VECTOR)

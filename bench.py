@@ -33,7 +33,8 @@ Other modes:
 After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv restoring
 the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
 second sign vector and corrected norm, ``prefill_encode_d256`` a head_dim-256 encode in
-the whole-vector and blocked modes, and ``append_decode`` reports the decode-loop call
+the whole-vector and blocked modes (and head_dim 192 zero-padded to 256 in the
+whole-vector mode), and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
 positions are captured in one HIP graph and replayed, so the figure is GPU time per
@@ -252,7 +253,9 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     """Encode of a prefill-shaped K slice (8 x 8 KV heads x 16384 tokens, head_dim 256,
     bf16 AR(1) rho 0.9, 512 MiB: larger than the last-level cache) with 4-bit codes,
     in the whole-vector mode (one 256-point rotation, the d = 256 codebook, one norm
-    per vector) and in the blocked mode (two 128-blocks), for comparison."""
+    per vector) and in the blocked mode (two 128-blocks), for comparison; and the
+    first 192 channels of the same vectors (a contiguous head_dim-192 tensor) in the
+    whole-vector mode, zero-padded to 256."""
     import torch
     import workloads
     w = workloads.WORKLOADS["prefill"]
@@ -260,11 +263,15 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     del v
     B, H, T, d = k.shape
     out = {}
-    for mode, cb, flags, nnorm in (("whole", fa.codebook_init(256, 4), fa.WHOLE_VECTOR, 1),
-                                   ("blocked", fa.codebook_init(128, 4), 0, 2)):
-        codes, norms = fa.cache_buffers(B, H, T, d, 4)
-        norms = norms[..., :nnorm].contiguous()
-        call = fa.encode_call(cb, seed, k, codes, norms, flags=flags)
+    cb256 = fa.codebook_init(256, 4)
+    for mode, cb, flags in (("whole", cb256, fa.WHOLE_VECTOR),
+                            ("blocked", fa.codebook_init(128, 4), 0),
+                            ("whole_padded_d192", cb256, fa.WHOLE_VECTOR)):
+        x = k[..., :192].contiguous() if mode == "whole_padded_d192" else k
+        d = x.shape[-1]
+        codes, norms = fa.cache_buffers(B, H, T, d, 4, flags=flags)
+        nnorm = norms.shape[-1]
+        call = fa.encode_call(cb, seed, x, codes, norms, flags=flags)
         call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -275,12 +282,12 @@ def prefill_whole(fa, seed, reps=10) -> dict:
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         nvec = B * H * T
-        nbytes = nvec * (2 * d + 2 * 64 + 2 * nnorm)
+        nbytes = nvec * (2 * d + codes.shape[-2] * 64 + 2 * nnorm)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[mode] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
                      "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        del codes, norms
+        del codes, norms, x
     del k
     return out
 

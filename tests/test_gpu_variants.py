@@ -63,14 +63,23 @@ def _flags(fa, two, nc):
 @pytest.mark.parametrize("two,nc", [(True, False), (False, True), (True, True)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_encode_variants(gpu_lib, bits, two, nc, dtype):
-    if bits == 8 and nc:
-        pytest.skip("the corrected norm is defined for the 2-4 bit codebooks")
     torch = _torch()
     fa = gpu_lib
     g = torch.Generator(device="cuda").manual_seed(bits * 7 + two * 3 + nc)
     x = torch.randn((2, 3, 301, 256), generator=g, device="cuda")
     x = x.to(torch.bfloat16) if dtype == "bf16" else x
     cb = fa.codebook_init(128, bits)
+    if bits == 8 and nc:
+        # the corrected norm is defined for the 2-4 bit codebooks: rejected before
+        # any launch, the cache left as it was
+        codes, norms = fa.cache_buffers(2, 3, 301, 256, 8, x.device)
+        codes.fill_(0x5A)
+        with pytest.raises(fa.FaTqError) as err:
+            fa.encode(cb, SEED, x, codes=codes, norms=norms, flags=_flags(fa, two, nc))
+        torch.cuda.synchronize()
+        assert err.value.status == fa.FA_TQ_EUNSUPPORTED
+        assert torch.all(codes == 0x5A)
+        return
     codes, norms = fa.encode(cb, SEED, x, flags=_flags(fa, two, nc))
     torch.cuda.synchronize()
     x32 = bf16_to_f32(x) if dtype == "bf16" else x.cpu().numpy()

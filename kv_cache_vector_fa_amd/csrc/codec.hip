@@ -48,34 +48,6 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
   b = u - v;
 }
 
-// The 8 codes of chunk c (elements 8c .. 8c + 7) of one packed block row ([Spec]
-// "Step 3: Packing", least-significant field first; 3 bits as the split planes of
-// [turboq] block_turboq3_0).
-template <int BITS>
-__device__ __forceinline__ void load_chunk(const uint8_t* row, int c, uint32_t (&code)[8]) {
-  if constexpr (BITS == 4) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[c];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = (w >> (4 * i)) & 15u;
-  } else if constexpr (BITS == 2) {
-    const uint32_t w = reinterpret_cast<const uint16_t*>(row)[c];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = (w >> (2 * i)) & 3u;
-  } else if constexpr (BITS == 3) {
-    const uint32_t lo = reinterpret_cast<const uint16_t*>(row)[c];
-    const uint32_t hi = row[32 + c];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = ((lo >> (2 * i)) & 3u) | (((hi >> i) & 1u) << 2);
-  } else {
-    const uint2 w = reinterpret_cast<const uint2*>(row)[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      code[i] = (w.x >> (8 * i)) & 255u;
-      code[4 + i] = (w.y >> (8 * i)) & 255u;
-    }
-  }
-}
-
 template <int BITS>
 constexpr int code_bytes_of() {
   return BITS == 2 ? 32 : BITS == 3 ? 48 : BITS == 4 ? 64 : 128;
@@ -635,14 +607,89 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   }
 }
 
+// Raw code words of one block for the lane's chunks q + 4k, and its norm, as loaded:
+// a[k] the chunk's codes (4-bit: 4 bytes, 2/3-bit: the 2-bit plane's 2 bytes, 8-bit:
+// the first 4 bytes), b[k] the 3-bit high plane byte or the second 4 bytes of an
+// 8-bit chunk; n the fp16 norm bits.
+template <int BITS>
+struct RawCodes {
+  uint32_t a[4];
+  uint32_t b[BITS == 3 || BITS == 8 ? 4 : 1];
+  uint32_t n;
+};
+
+// Loads of one block (byte offset co of its code row in rc, norm byte offset no in
+// rn; kOOB for slots without work: zeros, nothing read).
+template <int BITS>
+__device__ __forceinline__ void load_codes(Rsrc rc, Rsrc rn, uint32_t co, uint32_t no, int q,
+                                           RawCodes<BITS>& r) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t c = static_cast<uint32_t>(q + 4 * k);
+    if constexpr (BITS == 4) {
+      r.a[k] = __builtin_amdgcn_raw_buffer_load_b32(rc, co + 4 * c, 0, 0);
+    } else if constexpr (BITS == 2) {
+      r.a[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, co + 2 * c, 0, 0);
+    } else if constexpr (BITS == 3) {
+      r.a[k] = __builtin_amdgcn_raw_buffer_load_b16(rc, co + 2 * c, 0, 0);
+      r.b[k] = __builtin_amdgcn_raw_buffer_load_b8(rc, co + 32 + c, 0, 0);
+    } else {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rc, co + 8 * c, 0, 0);
+      r.a[k] = w[0];
+      r.b[k] = w[1];
+    }
+  }
+  r.n = __builtin_amdgcn_raw_buffer_load_b16(rn, no, 0, 0);
+}
+
+// The 8 codes of the lane's chunk k ([Spec] "Step 3: Packing", least-significant
+// field first; 3 bits as the split planes of [turboq] block_turboq3_0).
+template <int BITS>
+__device__ __forceinline__ void chunk_codes(const RawCodes<BITS>& r, int k, uint32_t (&code)[8]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = (r.a[k] >> (4 * i)) & 15u;
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = (r.a[k] >> (2 * i)) & 3u;
+  } else if constexpr (BITS == 3) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      code[i] = ((r.a[k] >> (2 * i)) & 3u) | (((r.b[k] >> i) & 1u) << 2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      code[i] = (r.a[k] >> (8 * i)) & 255u;
+      code[4 + i] = (r.b[k] >> (8 * i)) & 255u;
+    }
+  }
+}
+
+// Stores of one decoded block (same count and kinds as the decoder's), all to
+// offset kOOB, so they are dropped.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16_OUT>
+__device__ __forceinline__ void dummy_out_stores(Rsrc ro) {
+#pragma unroll
+  for (int k = 0; k < (BF16_OUT ? 4 : 8); ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ro, kOOB + 16 * k, 0, 0);
+}
+
 // Decode: x_hat = s * (H (n * c[code])) / sqrt(128), one quad per block, in the
 // encoder's layout: grid (gx, gy), blockIdx.y over the (batch, head) rows and block
 // slots f = (token, block j) of a row strided by gridDim.x * 64 (a multiple of nblk, so
-// a quad keeps its j and its sign words).  The two cross-lane stages are DPP
-// multiply-adds as in the encoder: the upper lane of a pair keeps the negated
-// difference, a sign folded into the final scale.  WV: whole vectors of head_dim 256
-// (nblk = 2): one norm per vector, the second quad's chunks in reversed lane order and
-// the stage between the vector's two blocks by row_half_mirror, scale 1/16.
+// a quad keeps its j and its sign words).  Ping-pong register sets: the next block's
+// codes and norm load while the current block is transformed and stored.  Memory
+// operations go through buffer resources; slots past the row's last token (and, with
+// PAD, the padding chunks) use offset kOOB: they load zeros and store nothing,
+// without divergent control flow, and every iteration leaves the same pattern of
+// outstanding loads and stores, so the wait before a block covers only its own
+// loads.  The two cross-lane stages are DPP multiply-adds as in the encoder: the
+// upper lane of a pair keeps the negated difference, a sign folded into the final
+// scale.  WV: whole vectors of head_dim 256 (nblk = 2): one norm per vector, the
+// second quad's chunks in reversed lane order and the stage between the vector's two
+// blocks by row_half_mirror, scale 1/16.
 // PAD: d.dim < QK * nblk; the chunks at or past d.dim (the padding) are not stored.
 template <int BITS, bool BF16_OUT, bool WV, bool PAD>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
@@ -650,9 +697,13 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   static_assert(!WV || BITS != 8, "whole-vector mode: 2-4 bit codebooks");
   static_assert(!PAD || BITS != 8, "padding: whole-vector mode only");
   constexpr int CB = code_bytes_of<BITS>();
+  constexpr uint32_t OES = BF16_OUT ? 2 : 4;   // output element bytes
   __shared__ float cent[16];
   if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
   __syncthreads();
+  const int64_t rows = d.rows;
+  int64_t row = blockIdx.y;
+  if (row >= rows) return;   // uniform over the workgroup
   const uint32_t nblk = static_cast<uint32_t>(d.nblk);
   const uint32_t f0 = blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2);
   const uint32_t fstep = gridDim.x * (kThreads / 4);
@@ -666,84 +717,138 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   const uint32_t carried = (((q ^ (q >> 1)) & 1u) ^ (WV ? (j & 1) : 0)) << 31;
   constexpr float c_scale = WV ? 0.0625f : kInvSqrtQK;   // RN32(1/sqrt(d))
   const float scale = __uint_as_float(__float_as_uint(c_scale) ^ carried);
-  const uint32_t per_row = static_cast<uint32_t>(d.tokens) * nblk;
-  for (int64_t row = blockIdx.y; row < d.rows; row += gridDim.y) {
-    const uint8_t* crows = d.codes + row * d.t_max * nblk * CB;
-    const uint16_t* nrows = d.norms + row * d.t_max * (WV ? 1 : nblk);
-    const int64_t b = row / d.heads, h = row - b * d.heads;
-    const int64_t obase = b * d.sb + h * d.sh + static_cast<int64_t>(QK) * j;
-    for (uint32_t f = f0; f < per_row; f += fstep) {
-      const uint32_t t = f / nblk;
-      const uint8_t* crow = crows + static_cast<int64_t>(f) * CB;
-      const float n = __half2float(__ushort_as_half(nrows[WV ? t : f]));
-      float v[4][8];
+  // store offset of the lane's chunk k relative to its block (or kOOB in the padding)
+  uint32_t cofs[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t code[8];
-        load_chunk<BITS>(crow, q + 4 * k, code);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t e = QK * j + 8 * (q + 4 * k);
+    cofs[k] = PAD && static_cast<int>(e) >= d.dim ? kOOB : e * OES;
+  }
+  // The host keeps a row's decoded codes, its norms and its output span below 2^31
+  // bytes, so every offset below is a 32-bit value and kOOB lies past every range.
+  const uint32_t tokens = static_cast<uint32_t>(d.tokens);
+  const uint32_t per_row = tokens * nblk;
+  const uint32_t nnorm = WV ? tokens : per_row;
+  const uint32_t obytes =
+      static_cast<uint32_t>(((d.tokens - 1) * d.st + static_cast<int64_t>(d.dim)) * OES);
+  const uint32_t st_bytes = static_cast<uint32_t>(d.st) * OES;   // token stride of out
+  // the quad's slots are f = t * nblk + j for its tokens t = t_first, + t_step, ...
+  const uint32_t t_first = f0 / nblk, t_step = fstep / nblk;
+  struct Row {
+    Rsrc rc, rn, ro;
+  };
+  auto open_row = [&](int64_t r) {
+    const int64_t b = r / d.heads, h = r - b * d.heads;
+    Row R;
+    R.rc = make_rsrc(d.codes + r * d.t_max * nblk * CB, per_row * CB);
+    R.rn = make_rsrc(d.norms + r * d.t_max * (WV ? 1 : nblk), 2 * nnorm);
+    R.ro = make_rsrc(static_cast<char*>(d.out) + (b * d.sb + h * d.sh) * OES, obytes);
+    return R;
+  };
+  auto load = [&](const Row& R, uint32_t t, RawCodes<BITS>& raw) {
+    const bool live = t < tokens;
+    const uint32_t f = t * nblk + j;
+    load_codes<BITS>(R.rc, R.rn, live ? f * CB : kOOB, live ? 2 * (WV ? t : f) : kOOB, q, raw);
+  };
+  auto process = [&](const Row& R, const RawCodes<BITS>& raw, uint32_t t) {
+    const float n = __half2float(__ushort_as_half(static_cast<uint16_t>(raw.n)));
+    float v[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float r;
-          if constexpr (BITS == 8)
-            r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
-          else
-            r = n * cent[code[i]];
-          v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
-        }
-      }
-      // butterflies: stages 1, 2, 4 in-chunk, 8, 16 across the quad, 32, 64 across
-      // chunks, and 128 across a whole vector's two quads
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        bfly(v[k][0], v[k][1]); bfly(v[k][2], v[k][3]);
-        bfly(v[k][4], v[k][5]); bfly(v[k][6], v[k][7]);
-        bfly(v[k][0], v[k][2]); bfly(v[k][1], v[k][3]);
-        bfly(v[k][4], v[k][6]); bfly(v[k][5], v[k][7]);
-        bfly(v[k][0], v[k][4]); bfly(v[k][1], v[k][5]);
-        bfly(v[k][2], v[k][6]); bfly(v[k][3], v[k][7]);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) xstage<0xB1>(v[k], mu1);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) xstage<0x4E>(v[k], mu2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bfly(v[0][i], v[1][i]);
-        bfly(v[2][i], v[3][i]);
-      }
+    for (int k = 0; k < 4; ++k) {
+      uint32_t code[8];
+      chunk_codes<BITS>(raw, k, code);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        bfly(v[0][i], v[2][i]);
-        bfly(v[1][i], v[3][i]);
-      }
-      if constexpr (WV) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) xstage_mirror(v[k], mu3);
-      }
-      const int64_t eo = obase + static_cast<int64_t>(t) * d.st;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float r[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = flip_sign(v[k][i] * scale, (sbits >> (8 * k + i)) & 1u);
-        const int c = q + 4 * k;
-        if (PAD && QK * j + 8 * c >= d.dim) continue;
-        if constexpr (BF16_OUT) {
-          // v_cvt_pk_bf16_f32: two fp32 to bf16, round to nearest even
-          uint32_t w[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            w[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                    f2{r[2 * m], r[2 * m + 1]}, bf16x2));
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(d.out) + eo + 8 * c) =
-              make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-          float4* o = reinterpret_cast<float4*>(static_cast<float*>(d.out) + eo + 8 * c);
-          o[0] = make_float4(r[0], r[1], r[2], r[3]);
-          o[1] = make_float4(r[4], r[5], r[6], r[7]);
-        }
+        float r;
+        if constexpr (BITS == 8)
+          r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
+        else
+          r = n * cent[code[i]];
+        v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
       }
     }
+    // butterflies: stages 1, 2, 4 in-chunk, 8, 16 across the quad, 32, 64 across
+    // chunks, and 128 across a whole vector's two quads
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bfly(v[k][0], v[k][1]); bfly(v[k][2], v[k][3]);
+      bfly(v[k][4], v[k][5]); bfly(v[k][6], v[k][7]);
+      bfly(v[k][0], v[k][2]); bfly(v[k][1], v[k][3]);
+      bfly(v[k][4], v[k][6]); bfly(v[k][5], v[k][7]);
+      bfly(v[k][0], v[k][4]); bfly(v[k][1], v[k][5]);
+      bfly(v[k][2], v[k][6]); bfly(v[k][3], v[k][7]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xstage<0xB1>(v[k], mu1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xstage<0x4E>(v[k], mu2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bfly(v[0][i], v[1][i]);
+      bfly(v[2][i], v[3][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bfly(v[0][i], v[2][i]);
+      bfly(v[1][i], v[3][i]);
+    }
+    if constexpr (WV) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xstage_mirror(v[k], mu3);
+    }
+    // byte offset of the block's token row; kOOB for a slot past the row
+    const uint32_t tb = t < tokens ? t * st_bytes : kOOB;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = flip_sign(v[k][i] * scale, (sbits >> (8 * k + i)) & 1u);
+      // past every range when either part is kOOB (the sum alone may wrap)
+      const uint32_t o = (tb + cofs[k]) | ((tb | cofs[k]) & kOOB);
+      if constexpr (BF16_OUT) {
+        // v_cvt_pk_bf16_f32: two fp32 to bf16, round to nearest even
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          w[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                  f2{r[2 * m], r[2 * m + 1]}, bf16x2));
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, R.ro, o, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]), __float_as_uint(r[2]),
+                  __float_as_uint(r[3])}, R.ro, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(r[4]), __float_as_uint(r[5]), __float_as_uint(r[6]),
+                  __float_as_uint(r[7])}, R.ro, o + 16, 0, 0);
+      }
+    }
+  };
+  Row R = open_row(row);
+  uint32_t t = t_first;
+  RawCodes<BITS> ra, rb;
+  load(R, t, ra);
+  // Ping-pong over the row's slots (lane 0 holds the wavefront's smallest slot, so
+  // the trip count is uniform); the stores of a block placed before the first one
+  // (dropped) give the loop entry the same outstanding-memory pattern as later
+  // iterations.
+  for (;;) {
+    dummy_out_stores<BF16_OUT>(R.ro);
+    while (__builtin_amdgcn_readfirstlane(t) < tokens) {
+      load(R, t + t_step, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      process(R, ra, t);
+      t += t_step;
+      if (__builtin_amdgcn_readfirstlane(t) >= tokens) break;
+      load(R, t + t_step, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      process(R, rb, t);
+      t += t_step;
+    }
+    row += gridDim.y;
+    if (row >= rows) break;
+    R = open_row(row);
+    t = t_first;
+    load(R, t, ra);
   }
 }
 
@@ -820,13 +925,19 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
   return hipGetLastError();
 }
 
-// Decode grid: y over the rows, x over the block slots of a row (about 8192
-// workgroups in total), x a multiple of what keeps 64 * x divisible by nblk.
+// Decode grid: y over the rows, x over the block slots of a row (about kDecodeWGs
+// workgroups in total, so that a quad loops over several blocks and its loads run
+// one block ahead), x a multiple of what keeps 64 * x divisible by nblk.
+#ifndef FATQ_DECODE_WGS
+#define FATQ_DECODE_WGS 2048
+#endif
+constexpr int64_t kDecodeWGs = FATQ_DECODE_WGS;
+
 dim3 decode_grid(const DecodeLaunch& d) {
   const int64_t gy = d.rows < 65535 ? d.rows : 65535;
   const int64_t per_row = d.tokens * d.nblk;
   const int64_t wg_row = (per_row + kThreads / 4 - 1) / (kThreads / 4);
-  int64_t gx = 8192 / gy;
+  int64_t gx = kDecodeWGs / gy;
   if (gx > wg_row) gx = wg_row;
   if (gx < 1) gx = 1;
   int64_t g = kThreads / 4, n = d.nblk;

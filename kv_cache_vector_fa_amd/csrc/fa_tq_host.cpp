@@ -4,6 +4,7 @@
 // Pages cited: [Spec] "TurboQuant KV Cache Compression -- Spec";
 //              [turboq] "TurboQuant KV Cache (turboq2 / turboq3 / turboq4)".
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -524,23 +525,35 @@ fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_
   if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "fa_tq_decode: NULL device pointer");
   if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 1u))
     return fail(FA_TQ_EINVAL, "fa_tq_decode: codes and out must be 16-byte aligned");
-  fatq::DecodeLaunch d;
-  d.codes = codes;
-  d.norms = norms;
-  d.rows = 1;
-  d.tokens = n_vec;
-  d.t_max = n_vec;
-  d.heads = 1;
-  d.nblk = head_dim / fatq::QK;
-  d.out = out;
-  d.sb = 0;
-  d.sh = 0;
-  d.st = head_dim;
-  d.out_bf16 = 0;
-  d.dim = head_dim;
+  // The kernel addresses one row of codes and of output with 32-bit byte offsets
+  // below 2^31: the vectors go as rows of R vectors each, then one row of the rest.
+  const int32_t nblk = head_dim / fatq::QK;
+  const int64_t vec_bytes = static_cast<int64_t>(nblk) * fa_tq_code_bytes(cb->bits);
+  const int64_t out_bytes = static_cast<int64_t>(head_dim) * sizeof(float);
+  const int64_t R = ((int64_t{1} << 31) - 1) / std::max(vec_bytes, out_bytes);
   const fatq::SignWords sw = make_sign_words(seed, head_dim);
-  return launched(fatq::launch_decode(d, tab, sw, false, static_cast<hipStream_t>(stream)),
-                  "fa_tq_decode");
+  auto launch_rows = [&](int64_t first, int64_t rows, int64_t per) {
+    fatq::DecodeLaunch d;
+    d.codes = codes + first * vec_bytes;
+    d.norms = norms + first * nblk;
+    d.rows = rows;
+    d.tokens = per;
+    d.t_max = per;
+    d.heads = 1;
+    d.nblk = nblk;
+    d.out = out + first * head_dim;
+    d.sb = per * head_dim;   // row b starts at vector first + b * per
+    d.sh = 0;
+    d.st = head_dim;
+    d.out_bf16 = 0;
+    d.dim = head_dim;
+    return launched(fatq::launch_decode(d, tab, sw, false, static_cast<hipStream_t>(stream)),
+                    "fa_tq_decode");
+  };
+  if (n_vec <= R) return launch_rows(0, 1, n_vec);
+  const int64_t full = n_vec / R, rem = n_vec - full * R;
+  if ((st = launch_rows(0, full, R)) != FA_TQ_OK) return st;
+  return rem ? launch_rows(full * R, 1, rem) : ok();
 }
 
 fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t flags,
@@ -571,6 +584,14 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
   if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
   if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 1u))
     return fail(FA_TQ_EINVAL, "%s: codes and out must be 16-byte aligned, norms 2-byte", who);
+  // The kernel addresses the decoded codes and the output of one (batch, head) row
+  // with 32-bit byte offsets below 2^31.
+  const int64_t oes = out_dtype == FA_TQ_BF16 ? 2 : 4;
+  if (static_cast<int64_t>(n_tokens) * (dt / fatq::QK) * fa_tq_code_bytes(cb->bits) >=
+          (int64_t{1} << 31) ||
+      ((n_tokens - 1) * out_layout.stride_t + head_dim) * oes >= (int64_t{1} << 31))
+    return fail(FA_TQ_EUNSUPPORTED,
+                "%s: one (batch, head) row of codes or of output spans 2 GiB or more", who);
   fatq::DecodeLaunch d;
   d.codes = codes;
   d.norms = norms;

@@ -140,3 +140,36 @@ def test_decode_kv_llama_layer_sampled(gpu_lib):
     x64 = _oracle_decode(c, n, w.k_bits, 128)
     got = bf16_to_f32(out[:, heads][:, :, toks]).astype(np.float64)
     _check_bf16(got, x64, "llama K4 bf16 restore")
+
+
+def test_flat_decode_beyond_one_row(gpu_lib):
+    """fa_tq_decode of more vectors than one launch row holds (its fp32 output spans
+    more than 2 GiB at head_dim 128: 2^31 / 512 B = 4194303 vectors per row): the
+    vectors around the row boundary, the first and the last decode as the oracle
+    does; a second, shorter call into the same output leaves the rest untouched."""
+    torch = _torch()
+    fa = gpu_lib
+    bits, d = 4, 128
+    per_row = ((1 << 31) - 1) // (d * 4)
+    n = per_row + 1001
+    rng = np.random.default_rng(77)
+    gc = torch.randint(0, 256, (n, 1, 64), dtype=torch.uint8, device="cuda")
+    n16 = (11.3 * np.exp(0.3 * rng.standard_normal((n, 1)))).astype(np.float16)
+    gn = torch.from_numpy(n16.view(np.int16)).cuda()
+    cb = fa.codebook_init(128, bits)
+    out = fa.decode(cb, SEED, gc, gn, d)
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, per_row - 2, per_row - 1, per_row, per_row + 1, n - 2, n - 1])
+    ti = torch.from_numpy(idx).cuda()
+    codes = gc[ti].cpu().numpy()
+    x64 = _oracle_decode(codes.reshape(1, 1, -1, 1, 64), n16[idx].reshape(1, 1, -1, 1), bits, d)
+    g = out[ti].cpu().numpy().astype(np.float64).reshape(x64.shape)
+    rel = np.linalg.norm(g - x64, axis=-1) / np.linalg.norm(x64, axis=-1)
+    assert rel.max() <= DECODE_REL_L2, rel
+    # a shorter call (one row) rewrites only its own vectors
+    ref_tail = out[per_row:].clone()
+    out2 = fa.decode(cb, SEED, gc[:1000], gn[:1000], d, out=out[:1000])
+    torch.cuda.synchronize()
+    assert out2.data_ptr() == out.data_ptr()
+    assert torch.equal(out[per_row:], ref_tail)
+    say(f"flat decode of {n} vectors: max rel L2 {rel.max():.2e} at the sampled vectors")

@@ -219,3 +219,15 @@ def test_padded_cache_shapes_in_the_binding(lib):
     out = torch.empty((2, 3, 5, 200), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.decode_kv_call(cb, 42, codes, norms, out, flags=fa.WHOLE_VECTOR)
+
+
+def test_decode_kv_rejects_an_output_row_of_2_gib(lib):
+    """fa_tq_decode_kv addresses one (batch, head) row of output with 32-bit byte
+    offsets: an output whose token stride makes one row span 2 GiB or more is
+    rejected before any launch (no device needed)."""
+    cb = fa.codebook_init(128, 4)
+    P = ctypes.c_void_p(1 << 20)
+    big = fa.Layout(0, 128, 1 << 29)   # 3 tokens of bf16 at 1 GiB apart
+    assert lib.fa_tq_decode_kv(ctypes.byref(cb), 42, 0, 128, P, P, 1, 1, 3, 3, P,
+                               fa.FA_TQ_BF16, big, None) == fa.FA_TQ_EUNSUPPORTED
+    assert "2 GiB" in lib.fa_tq_last_error().decode()

@@ -698,8 +698,19 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   static_assert(!PAD || BITS != 8, "padding: whole-vector mode only");
   constexpr int CB = code_bytes_of<BITS>();
   constexpr uint32_t OES = BF16_OUT ? 2 : 4;   // output element bytes
-  __shared__ float cent[16];
-  if (threadIdx.x < 16) cent[threadIdx.x] = tab.c[threadIdx.x];
+  // Centroid table in LDS.  4-bit codes: entry r (one code byte) holds the two
+  // centroids (c[r & 15], c[r >> 4]); 2-bit: entry r holds the four centroids of the
+  // byte's fields; 3-bit: the 16 centroids (one look-up per code).
+  constexpr int TW = BITS == 4 ? 2 : BITS == 2 ? 4 : 1;   // floats per entry
+  __shared__ __attribute__((aligned(16))) float ctab[BITS == 8 ? 1 : (BITS == 3 ? 16 : 256 * TW)];
+  static_assert(kThreads == 256, "one table entry per thread");
+  if constexpr (BITS == 4 || BITS == 2) {
+    const uint32_t r = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < TW; ++m) ctab[TW * r + m] = tab.c[(r >> (8 / TW * m)) & ((1u << BITS) - 1)];
+  } else if constexpr (BITS == 3) {
+    if (threadIdx.x < 16) ctab[threadIdx.x] = tab.c[threadIdx.x];
+  }
   __syncthreads();
   const int64_t rows = d.rows;
   int64_t row = blockIdx.y;
@@ -755,15 +766,37 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
     float v[4][8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t code[8];
-      chunk_codes<BITS>(raw, k, code);
+      float cv[8];   // centroid values of the chunk's 8 codes
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float2 e = reinterpret_cast<const float2*>(ctab)[(raw.a[k] >> (8 * m)) & 255u];
+          cv[2 * m] = e.x;
+          cv[2 * m + 1] = e.y;
+        }
+      } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float4 e = reinterpret_cast<const float4*>(ctab)[(raw.a[k] >> (8 * m)) & 255u];
+          cv[4 * m] = e.x;
+          cv[4 * m + 1] = e.y;
+          cv[4 * m + 2] = e.z;
+          cv[4 * m + 3] = e.w;
+        }
+      } else {
+        uint32_t code[8];
+        chunk_codes<BITS>(raw, k, code);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if constexpr (BITS == 8)
+            cv[i] = static_cast<float>(code[i]) - 127.5f;
+          else
+            cv[i] = ctab[code[i]];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float r;
-        if constexpr (BITS == 8)
-          r = (static_cast<float>(code[i]) - 127.5f) * (n / 127.5f);
-        else
-          r = n * cent[code[i]];
+        const float r = BITS == 8 ? cv[i] * (n / 127.5f) : n * cv[i];
         v[k][i] = flip_sign(r, (s2bits >> (8 * k + i)) & 1u);
       }
     }

@@ -34,7 +34,8 @@ After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv res
 the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
 second sign vector and corrected norm, ``prefill_encode_d256`` a head_dim-256 encode in
 the whole-vector and blocked modes (and head_dim 192 zero-padded to 256 in the
-whole-vector mode), and ``append_decode`` reports the decode-loop call
+whole-vector mode), ``attention_other_workloads`` decode attention on the batched
+and long-context workloads, and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
 positions are captured in one HIP graph and replayed, so the figure is GPU time per
@@ -292,6 +293,52 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     return out
 
 
+def other_attention(fa, seed, reps=20) -> dict:
+    """GPU time of fa_tq_attn_decode on the batched workload (16 sequences x 8 KV heads,
+    8192 slots, lengths 4096..8192, K3/V3) and the long-context one (4 x 8 x 131072,
+    K4/V4): caches encoded from the seeded inputs, calls rotating over enough cache
+    copies (at least 768 MB of attention bytes) that the working set exceeds the
+    256 MB last-level cache."""
+    import torch
+    import workloads
+    out = {}
+    for name in ("batched", "long_context"):
+        w = workloads.WORKLOADS[name]
+        B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim
+        k, v = workloads.make_kv(w, "cuda")
+        q = workloads.make_q(w, "cuda")
+        lens_np = workloads.make_seq_lens(w)
+        lens = torch.from_numpy(lens_np).cuda()
+        cbk, cbv = fa.codebook_init(128, w.k_bits), fa.codebook_init(128, w.v_bits)
+        kc, kn = fa.encode(cbk, seed, k)
+        vc, vn = fa.encode(cbv, seed, v)
+        del k, v
+        nbytes = attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits)
+        copies = max(1, -(-768_000_000 // nbytes))
+        caches = [(kc, kn, vc, vn)] + [tuple(t.clone() for t in (kc, kn, vc, vn))
+                                       for _ in range(copies - 1)]
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        ws = fa.attn_workspace(B, Hq, Hkv, T, d)
+        calls = [fa.attn_decode_call(cbk, cbv, seed, q, *c, lens, 1 / np.sqrt(d), o, ws)
+                 for c in caches]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 1), "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "cache_copies": copies,
+                     "shape": f"{B}x{Hkv}x{T} K{w.k_bits}/V{w.v_bits}, {Hq} query heads"}
+        del caches, kc, kn, vc, vn, ws, o
+    return out
+
+
 def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
     """The oracle as it stands, on ``n_slices`` (batch, KV head) slices of the workload
     (default: all of them): encode their K and V blocks in canonical fp32 and run fp64
@@ -460,6 +507,7 @@ def main():
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)
         rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks, caches)
         rec["prefill_encode_d256"] = prefill_whole(fa, seed)
+        rec["attention_other_workloads"] = other_attention(fa, seed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(rec), flush=True)

@@ -691,11 +691,13 @@ __device__ __forceinline__ void dummy_out_stores(Rsrc ro) {
 // second quad's chunks in reversed lane order and the stage between the vector's two
 // blocks by row_half_mirror, scale 1/16.
 // PAD: d.dim < QK * nblk; the chunks at or past d.dim (the padding) are not stored.
-template <int BITS, bool BF16_OUT, bool WV, bool PAD>
+// TWO: the two-sign rotation (otherwise s2 = +1 and its flips are compiled out).
+template <int BITS, bool BF16_OUT, bool WV, bool PAD, bool TWO>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable tab,
                                                           SignWords sw) {
   static_assert(!WV || BITS != 8, "whole-vector mode: 2-4 bit codebooks");
   static_assert(!PAD || BITS != 8, "padding: whole-vector mode only");
+  static_assert(!TWO || (!WV && !PAD), "the whole-vector mode has one sign vector");
   constexpr int CB = code_bytes_of<BITS>();
   constexpr uint32_t OES = BF16_OUT ? 2 : 4;   // output element bytes
   // Centroid table in LDS.  4-bit codes: entry r (one code byte) holds the two
@@ -721,7 +723,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   const int j = static_cast<int>(f0 % nblk);
   const int q = WV && (j & 1) ? 3 - static_cast<int>(threadIdx.x & 3) : threadIdx.x & 3;
   const uint32_t sbits = sw.w[j][q];
-  const uint32_t s2bits = sw.w2[j][q];   // R^T = D1 H D2 / sqrt(128); zero without it
+  const uint32_t s2bits = TWO ? sw.w2[j][q] : 0u;   // R^T = D1 H D2 / sqrt(128)
   const float mu1 = (q & 1) ? -1.0f : 1.0f;
   const float mu2 = (q & 2) ? -1.0f : 1.0f;
   const float mu3 = (j & 1) ? -1.0f : 1.0f;
@@ -987,20 +989,20 @@ dim3 decode_grid(const DecodeLaunch& d) {
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          bool whole, hipStream_t stream) {
   const dim3 grid = decode_grid(d), block(kThreads);
-#define FATQ_DEC(B, F, W, P) \
-  hipLaunchKernelGGL((decode_kernel<B, F, W, P>), grid, block, 0, stream, d, tab, sw)
-#define FATQ_DEC_BITS(F)                        \
-  switch (tab.bits) {                           \
-    case 2: FATQ_DEC(2, F, false, false); break; \
-    case 3: FATQ_DEC(3, F, false, false); break; \
-    case 4: FATQ_DEC(4, F, false, false); break; \
-    default: FATQ_DEC(8, F, false, false); break; \
+#define FATQ_DEC(B, F, W, P, T) \
+  hipLaunchKernelGGL((decode_kernel<B, F, W, P, T>), grid, block, 0, stream, d, tab, sw)
+#define FATQ_DEC_BITS(F, T)                            \
+  switch (tab.bits) {                                  \
+    case 2: FATQ_DEC(2, F, false, false, T); break;    \
+    case 3: FATQ_DEC(3, F, false, false, T); break;    \
+    case 4: FATQ_DEC(4, F, false, false, T); break;    \
+    default: FATQ_DEC(8, F, false, false, T); break;   \
   }
-#define FATQ_DEC_WV(F, W, P)                \
-  switch (tab.bits) {                       \
-    case 2: FATQ_DEC(2, F, W, P); break;    \
-    case 3: FATQ_DEC(3, F, W, P); break;    \
-    default: FATQ_DEC(4, F, W, P); break;   \
+#define FATQ_DEC_WV(F, W, P)                       \
+  switch (tab.bits) {                              \
+    case 2: FATQ_DEC(2, F, W, P, false); break;    \
+    case 3: FATQ_DEC(3, F, W, P, false); break;    \
+    default: FATQ_DEC(4, F, W, P, false); break;   \
   }
 #define FATQ_DEC_WHOLE(F)                                          \
   if (d.nblk == 2) {                                               \
@@ -1010,12 +1012,13 @@ hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWor
   }
   const bool pad = d.dim != QK * d.nblk;
   if (pad && !whole) return hipErrorInvalidValue;
+  if (whole && sw.two) return hipErrorInvalidValue;
   if (whole && (d.nblk == 2 || pad)) {
     if (d.out_bf16) { FATQ_DEC_WHOLE(true) } else { FATQ_DEC_WHOLE(false) }
-  } else if (d.out_bf16) {
-    FATQ_DEC_BITS(true)
+  } else if (sw.two) {
+    if (d.out_bf16) { FATQ_DEC_BITS(true, true) } else { FATQ_DEC_BITS(false, true) }
   } else {
-    FATQ_DEC_BITS(false)
+    if (d.out_bf16) { FATQ_DEC_BITS(true, false) } else { FATQ_DEC_BITS(false, false) }
   }
 #undef FATQ_DEC_WHOLE
 #undef FATQ_DEC_WV

@@ -195,8 +195,10 @@ __device__ __forceinline__ void issue_loads(const Rows& r, Codes<KB, VB>& c, int
           static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r.vn, ov, 0, 0));
 }
 
-// The key words of one tile as four words of 4-bit fields (byte i of the 16: elements
-// 32 qq + 2i (low nibble) and 32 qq + 2i + 1).
+// The key words of one tile as four words of table index bytes (byte i of the 16:
+// elements e = 32 qq + 2i and e + 1).  2/4-bit: 4-bit fields, code(e) in the low
+// nibble.  3-bit: lo(e) | lo(e + 1) << 2 | hi(e) << 4 | hi(e + 1) << 5 from the
+// low-bit plane (lo) and the high-bit plane (hi), the layout of the 3-bit key rows.
 template <int KB>
 __device__ __forceinline__ void key_fields(const uint32_t (&w)[KB == 4 ? 4 : 3], uint32_t (&f)[4]) {
   if constexpr (KB == 4) {
@@ -206,10 +208,20 @@ __device__ __forceinline__ void key_fields(const uint32_t (&w)[KB == 4 ? 4 : 3],
     f[2] = spread2(w[1] & 0xFFFFu); f[3] = spread2(w[1] >> 16);
   } else {
     const uint32_t h = w[2];
-    f[0] = spread2(w[0] & 0xFFFFu) | (spread1(h & 0xFFu) << 2);
-    f[1] = spread2(w[0] >> 16) | (spread1((h >> 8) & 0xFFu) << 2);
-    f[2] = spread2(w[1] & 0xFFFFu) | (spread1((h >> 16) & 0xFFu) << 2);
-    f[3] = spread2(w[1] >> 16) | (spread1(h >> 24) << 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // the pair (e, e + 1)'s low bits are a nibble of the low plane: bytes 2(m & 1)
+      // and 2(m & 1) + 1 of its word go to bytes 0 and 2, then a nibble to a byte
+      const uint32_t b0 = 2u * (m & 1);
+      const uint32_t y = __builtin_amdgcn_perm(0u, m < 2 ? w[0] : w[1],
+                                               0x0C000C00u | ((b0 + 1) << 16) | b0);
+      const uint32_t z = (y | (y << 4)) & 0x0F0F0F0Fu;
+      // their high bits, a 2-bit field of byte m of the high plane, to bits 4-5
+      const uint32_t a = (h >> (8 * m)) & 0xFFu;
+      const uint32_t b = (a | (a << 12)) & 0x000F000Fu;
+      const uint32_t c = (b | (b << 6)) & 0x03030303u;
+      f[m] = z | (c << 4);
+    }
   }
 }
 
@@ -376,7 +388,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   if (tid < 256) {
     const int r = tid;
     uint8_t* row = tab + r * kRow;
-    const uint32_t a0 = sp[0][r & 15], a1 = sp[0][r >> 4];
+    // key row r: the codes of its two elements (3-bit rows: see key_fields)
+    const uint32_t a0 = sp[0][KB == 3 ? (r & 3) | ((r >> 2) & 4) : r & 15];
+    const uint32_t a1 = sp[0][KB == 3 ? ((r >> 2) & 3) | ((r >> 3) & 4) : r >> 4];
     const uint32_t kh = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // hi(c_lo4), hi(c_hi4)
     const uint32_t kl = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // lo(c_lo4), lo(c_hi4)
     const uint4 ke = make_uint4(kh, kl, kh, kl);
@@ -783,9 +797,9 @@ void launch_g(const AttnLaunch& a, const KTable& tk, const KTable& tv, const Sig
   hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT>), g1, b1, 0, stream, a, tk, tv, sw)
 #define FATQ_ATS(K) \
   hipLaunchKernelGGL((attn_mfma_kernel<K, K, true, GT>), g1, b1, 0, stream, a, tk, tv, sw)
-  if (same) {
-    if (tk.bits == 3) FATQ_ATS(3);
-    else FATQ_ATS(4);
+  // shared key/value entries for 4-bit tables (3-bit key rows have their own layout)
+  if (same && tk.bits == 4) {
+    FATQ_ATS(4);
     return;
   }
   switch (tk.bits * 10 + tv.bits) {

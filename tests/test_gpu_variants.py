@@ -112,6 +112,12 @@ def test_decode_two_signs(gpu_lib, bits):
     rel = np.linalg.norm(g - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
     say(f"decode two-sign bits={bits}: max rel L2 {rel.max():.2e}")
     assert rel.max() <= DECODE_REL_L2
+    # bf16 restore: the round-to-nearest-even of the same fp32 decode
+    ob = fa.decode_kv(cb, SEED, torch.from_numpy(packed).cuda(),
+                      torch.from_numpy(on.view(np.int16)).cuda(), out_dtype=torch.bfloat16,
+                      flags=fa.TWO_SIGNS)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_to_f32(ob), codec.round_bf16(g).astype(np.float32))
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 2)])

@@ -642,17 +642,13 @@ __device__ __forceinline__ void load_codes(Rsrc rc, Rsrc rn, uint32_t co, uint32
   r.n = __builtin_amdgcn_raw_buffer_load_b16(rn, no, 0, 0);
 }
 
-// The 8 codes of the lane's chunk k ([Spec] "Step 3: Packing", least-significant
-// field first; 3 bits as the split planes of [turboq] block_turboq3_0).
+// The 8 codes of the lane's chunk k for 3-bit and 8-bit rows ([Spec] "Step 3:
+// Packing", least-significant field first; 3 bits as the split planes of [turboq]
+// block_turboq3_0).  2- and 4-bit code bytes index the decoder's table directly.
 template <int BITS>
 __device__ __forceinline__ void chunk_codes(const RawCodes<BITS>& r, int k, uint32_t (&code)[8]) {
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = (r.a[k] >> (4 * i)) & 15u;
-  } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = (r.a[k] >> (2 * i)) & 3u;
-  } else if constexpr (BITS == 3) {
+  static_assert(BITS == 3 || BITS == 8, "2/4-bit codes are looked up by byte");
+  if constexpr (BITS == 3) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       code[i] = ((r.a[k] >> (2 * i)) & 3u) | (((r.b[k] >> i) & 1u) << 2);
@@ -665,10 +661,10 @@ __device__ __forceinline__ void chunk_codes(const RawCodes<BITS>& r, int k, uint
   }
 }
 
-// Stores of one decoded block (same count and kinds as the decoder's), all to
-// offset kOOB, so they are dropped.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Stores of one decoded block (same count and kinds as the decoder's), all to
+// offset kOOB, so they are dropped.
 template <bool BF16_OUT>
 __device__ __forceinline__ void dummy_out_stores(Rsrc ro) {
 #pragma unroll

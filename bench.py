@@ -254,9 +254,9 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     """Encode of a prefill-shaped K slice (8 x 8 KV heads x 16384 tokens, head_dim 256,
     bf16 AR(1) rho 0.9, 512 MiB: larger than the last-level cache) with 4-bit codes,
     in the whole-vector mode (one 256-point rotation, the d = 256 codebook, one norm
-    per vector) and in the blocked mode (two 128-blocks), for comparison; and the
-    first 192 channels of the same vectors (a contiguous head_dim-192 tensor) in the
-    whole-vector mode, zero-padded to 256."""
+    per vector) and in the blocked mode (two 128-blocks), for comparison; the blocked
+    8-bit uniform grid (turboq8); and the first 192 channels of the same vectors (a
+    contiguous head_dim-192 tensor) in the whole-vector mode, zero-padded to 256."""
     import torch
     import workloads
     w = workloads.WORKLOADS["prefill"]
@@ -267,10 +267,11 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     cb256 = fa.codebook_init(256, 4)
     for mode, cb, flags in (("whole", cb256, fa.WHOLE_VECTOR),
                             ("blocked", fa.codebook_init(128, 4), 0),
+                            ("blocked_8bit", fa.codebook_init(128, 8), 0),
                             ("whole_padded_d192", cb256, fa.WHOLE_VECTOR)):
         x = k[..., :192].contiguous() if mode == "whole_padded_d192" else k
         d = x.shape[-1]
-        codes, norms = fa.cache_buffers(B, H, T, d, 4, flags=flags)
+        codes, norms = fa.cache_buffers(B, H, T, d, cb.bits, flags=flags)
         nnorm = norms.shape[-1]
         call = fa.encode_call(cb, seed, x, codes, norms, flags=flags)
         call()
@@ -283,7 +284,7 @@ def prefill_whole(fa, seed, reps=10) -> dict:
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         nvec = B * H * T
-        nbytes = nvec * (2 * d + codes.shape[-2] * 64 + 2 * nnorm)
+        nbytes = nvec * (2 * d + codes.shape[-2] * fa.code_bytes(cb.bits) + 2 * nnorm)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[mode] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
                      "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),

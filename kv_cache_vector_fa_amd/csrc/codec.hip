@@ -370,8 +370,8 @@ __device__ __forceinline__ void widen(const RawBlock<BF16>& r, const uint32_t (&
 // them, share one norm (and store it once) and scale by RN32(1/16).
 // PAD: a.dim < QK * nblk; the chunks at or past a.dim load as zeros.
 template <int BITS, bool BF16, bool NC, bool WV, bool PAD>
-__global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
-                                                          SignWords sw) {
+__device__ __forceinline__ void encode_body(const EncodeLaunch& a, const KTable& tab,
+                                            const SignWords& sw) {
   static_assert(!WV || (BITS != 8 && !NC), "whole-vector mode: 2-4 bit codebooks");
   static_assert(!PAD || (BITS != 8 && !NC), "padding: whole-vector mode only");
   constexpr int CB = code_bytes_of<BITS>();
@@ -605,6 +605,24 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
     t = t_first;
     load_raw<BF16>(R.rx, xoff(t), q, dead, ba);
   }
+}
+
+template <int BITS, bool BF16, bool NC, bool WV, bool PAD>
+__global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTable tab,
+                                                          SignWords sw) {
+  encode_body<BITS, BF16, NC, WV, PAD>(a, tab, sw);
+}
+
+// The keys and the values of one append in one launch (the same grid over the same
+// shape): blockIdx.z = 0 encodes the keys, 1 the values.
+template <int KB, int VB, bool BF16, bool NC>
+__global__ void __launch_bounds__(kEncThreads) encode_pair_kernel(EncodeLaunch ak, KTable tk,
+                                                               EncodeLaunch av, KTable tv,
+                                                               SignWords sw) {
+  if (blockIdx.z == 0)
+    encode_body<KB, BF16, NC, false, false>(ak, tk, sw);
+  else
+    encode_body<VB, BF16, NC, false, false>(av, tv, sw);
 }
 
 // Raw code words of one block for the lane's chunks q + 4k, and its norm, as loaded:
@@ -953,6 +971,41 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
 #undef FATQ_ENC_WV
 #undef FATQ_ENC_BITS
 #undef FATQ_ENC
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_pair(const EncodeLaunch& ak, const KTable& tk, const EncodeLaunch& av,
+                              const KTable& tv, const SignWords& sw, bool norm_correct,
+                              hipStream_t stream) {
+  if (ak.batch != av.batch || ak.heads != av.heads || ak.tokens != av.tokens ||
+      ak.nblk != av.nblk || ak.x_is_bf16 != av.x_is_bf16 || ak.dim != QK * ak.nblk ||
+      av.dim != QK * av.nblk || tk.bits == 8 || tv.bits == 8)
+    return hipErrorInvalidValue;
+  const dim3 g2 = encode_grid(ak), grid(g2.x, g2.y, 2), block(kEncThreads);
+  EncodeLaunch lk = ak, lv = av;
+  lk.t_step = lv.t_step = static_cast<int32_t>(grid.x * (kEncThreads / 4) / ak.nblk);
+#define FATQ_PAIR(K, V, F, N) \
+  hipLaunchKernelGGL((encode_pair_kernel<K, V, F, N>), grid, block, 0, stream, lk, tk, lv, tv, sw)
+#define FATQ_PAIR_V(K, F, N)                     \
+  switch (tv.bits) {                             \
+    case 2: FATQ_PAIR(K, 2, F, N); break;        \
+    case 3: FATQ_PAIR(K, 3, F, N); break;        \
+    default: FATQ_PAIR(K, 4, F, N); break;       \
+  }
+#define FATQ_PAIR_KV(F, N)                       \
+  switch (tk.bits) {                             \
+    case 2: FATQ_PAIR_V(2, F, N) break;          \
+    case 3: FATQ_PAIR_V(3, F, N) break;          \
+    default: FATQ_PAIR_V(4, F, N) break;         \
+  }
+  if (ak.x_is_bf16) {
+    if (norm_correct) { FATQ_PAIR_KV(true, true) } else { FATQ_PAIR_KV(true, false) }
+  } else {
+    if (norm_correct) { FATQ_PAIR_KV(false, true) } else { FATQ_PAIR_KV(false, false) }
+  }
+#undef FATQ_PAIR_KV
+#undef FATQ_PAIR_V
+#undef FATQ_PAIR
   return hipGetLastError();
 }
 

@@ -306,7 +306,9 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
                           const void* x, fa_tq_dtype x_dtype, fa_tq_layout x_layout,
                           int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
                           const int32_t* t0, int32_t t_max, uint8_t* codes, uint16_t* norms,
-                          void* stream, bool ring, bool check_only = false) {
+                          void* stream, bool ring, bool check_only = false,
+                          fatq::EncodeLaunch* prep = nullptr, fatq::KTable* prep_tab = nullptr,
+                          fatq::SignWords* prep_sw = nullptr) {
   fatq::KTable tab;
   const bool whole = (flags & FA_TQ_WHOLE_VECTOR) != 0;
   fa_tq_status st = check_flags(
@@ -357,6 +359,12 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
   const fatq::SignWords sw = make_sign_words(seed, dt, flags & FA_TQ_TWO_SIGNS);
+  if (prep) {   // the caller launches (the keys and values of an append together)
+    *prep = a;
+    *prep_tab = tab;
+    *prep_sw = sw;
+    return ok();
+  }
   return launched(fatq::launch_encode(a, tab, sw, (flags & FA_TQ_NORM_CORRECT) != 0, whole,
                                       static_cast<hipStream_t>(stream)),
                   who);
@@ -672,15 +680,26 @@ fa_tq_status fa_tq_attn_append_ex(const fa_tq_codebook* cb_k, const fa_tq_codebo
   if (!pos) return fail(FA_TQ_EINVAL, "%s: pos is NULL", who);
   // Every argument of the three steps is checked before the first launch, so a
   // rejected call leaves the cache untouched.
+  // The keys and values of the new tokens are encoded by one launch (blockIdx.z
+  // selects K or V), then the attention kernels run.
   fa_tq_status st;
+  fatq::EncodeLaunch ak, av;
+  fatq::KTable tk, tv;
+  fatq::SignWords sw;
   for (bool check_only : {true, false}) {
     if ((st = encode_impl(who, cb_k, seed, flags, head_dim, k_new, kv_dtype, k_layout, batch,
                           n_kv_heads, n_new, pos, t_max, k_codes, k_norms, stream, true,
-                          check_only)) != FA_TQ_OK)
+                          check_only, &ak, &tk, &sw)) != FA_TQ_OK)
       return st;
     if ((st = encode_impl(who, cb_v, seed, flags, head_dim, v_new, kv_dtype, v_layout, batch,
                           n_kv_heads, n_new, pos, t_max, v_codes, v_norms, stream, true,
-                          check_only)) != FA_TQ_OK)
+                          check_only, &av, &tv, &sw)) != FA_TQ_OK)
+      return st;
+    if (!check_only &&
+        (st = launched(fatq::launch_encode_pair(ak, tk, av, tv, sw,
+                                                (flags & FA_TQ_NORM_CORRECT) != 0,
+                                                static_cast<hipStream_t>(stream)),
+                       who)) != FA_TQ_OK)
       return st;
     if ((st = attn_impl(who, cb_k, cb_v, seed, flags & FA_TQ_TWO_SIGNS, head_dim, q, q_dtype,
                         k_codes, k_norms, v_codes, v_norms, nullptr, pos, n_new, batch,

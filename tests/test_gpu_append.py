@@ -66,7 +66,7 @@ def _device(fa, kp, kn, vp, vn):
             torch.from_numpy(vp.copy()).cuda(), torch.from_numpy(vn.view(np.int16).copy()).cuda())
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4), (2, 4), (3, 2)])
 @pytest.mark.parametrize("n_new", [1, 3])
 def test_append_positions_and_wrap(gpu_lib, kb, vb, n_new):
     """Three sequences: one early in the cache, one ending on the last slot, one that

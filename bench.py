@@ -397,7 +397,7 @@ def main():
         summarize_rocprof(args.summarize_rocprof)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
     import torch
 

@@ -16,7 +16,7 @@
  * Errors: arguments are checked on the host before any launch.  A non-OK status
  * launches nothing and leaves a message readable with fa_tq_last_error() (per host
  * thread).  FA_TQ_EINVAL: a bad size, pointer, alignment or table; FA_TQ_EUNSUPPORTED:
- * a valid combination this build has no kernel for; FA_TQ_EHIP: the HIP runtime
+ * a valid combination the library has no kernel for; FA_TQ_EHIP: the HIP runtime
  * reported an error at launch.  Faults inside a kernel surface at the caller's next
  * synchronization, as for any HIP kernel.
  *
@@ -213,7 +213,7 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, uint32_t f
  *   holds per-split partial results (m, l and the unnormalized rotated output per
  *   split of the sequence); its contents on entry do not matter.  Calls that run
  *   concurrently must not share a workspace; calls in order on one stream may.
- * This build supports head_dim == 128, key/value bits in {2, 3, 4} and
+ * The library supports head_dim == 128, key/value bits in {2, 3, 4} and
  * n_q_heads / n_kv_heads <= 16, and t_max < 33554432 (one cache row below 2 GiB).
  */
 fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
@@ -250,7 +250,7 @@ fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook *cb_k, const fa_tq_codebo
  *      the element strides of k_layout / v_layout (channel stride 1), 16-byte aligned.
  *   pos: device int32[batch], positions >= 0 (a negative position stores nothing and
  *      clamps the attended length at 0).
- *   codebooks: bits 2, 3 or 4 for keys and values; head_dim 128 (this build).
+ *   codebooks: bits 2, 3 or 4 for keys and values; head_dim 128.
  *   1 <= n_new <= t_max (two new tokens never share a slot); every argument is
  *   checked before anything is written to the cache.
  */

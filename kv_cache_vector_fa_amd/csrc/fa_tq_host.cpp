@@ -387,7 +387,7 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   if ((st = check_flags(flags, FA_TQ_TWO_SIGNS, nullptr, who)) != FA_TQ_OK) return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (head_dim != fatq::QK)
-    return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (this build: 128)", who,
+    return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (the attention kernels take 128)", who,
                 head_dim);
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0)
     return fail(FA_TQ_EINVAL, "%s: bad sizes", who);

@@ -660,22 +660,15 @@ __device__ __forceinline__ void load_codes(Rsrc rc, Rsrc rn, uint32_t co, uint32
   r.n = __builtin_amdgcn_raw_buffer_load_b16(rn, no, 0, 0);
 }
 
-// The 8 codes of the lane's chunk k for 3-bit and 8-bit rows ([Spec] "Step 3:
-// Packing", least-significant field first; 3 bits as the split planes of [turboq]
-// block_turboq3_0).  2- and 4-bit code bytes index the decoder's table directly.
+// The 8 codes of the lane's chunk k of an 8-bit row (one byte per code); 2-, 3- and
+// 4-bit codes index the decoder's centroid table by byte or element pair.
 template <int BITS>
 __device__ __forceinline__ void chunk_codes(const RawCodes<BITS>& r, int k, uint32_t (&code)[8]) {
-  static_assert(BITS == 3 || BITS == 8, "2/4-bit codes are looked up by byte");
-  if constexpr (BITS == 3) {
+  static_assert(BITS == 8, "2-4 bit codes are looked up by byte or pair");
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      code[i] = ((r.a[k] >> (2 * i)) & 3u) | (((r.b[k] >> i) & 1u) << 2);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      code[i] = (r.a[k] >> (8 * i)) & 255u;
-      code[4 + i] = (r.b[k] >> (8 * i)) & 255u;
-    }
+  for (int i = 0; i < 4; ++i) {
+    code[i] = (r.a[k] >> (8 * i)) & 255u;
+    code[4 + i] = (r.b[k] >> (8 * i)) & 255u;
   }
 }
 
@@ -716,16 +709,22 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
   constexpr uint32_t OES = BF16_OUT ? 2 : 4;   // output element bytes
   // Centroid table in LDS.  4-bit codes: entry r (one code byte) holds the two
   // centroids (c[r & 15], c[r >> 4]); 2-bit: entry r holds the four centroids of the
-  // byte's fields; 3-bit: the 16 centroids (one look-up per code).
-  constexpr int TW = BITS == 4 ? 2 : BITS == 2 ? 4 : 1;   // floats per entry
-  __shared__ __attribute__((aligned(16))) float ctab[BITS == 8 ? 1 : (BITS == 3 ? 16 : 256 * TW)];
+  // byte's fields; 3-bit: entry r of 64 holds the centroids of an element pair whose
+  // low bits are r & 15 (two 2-bit fields) and high bits r >> 4 (two 1-bit fields).
+  constexpr int TW = BITS == 2 ? 4 : 2;   // floats per entry
+  constexpr int TN = BITS == 3 ? 64 : 256;   // entries
+  __shared__ __attribute__((aligned(16))) float ctab[BITS == 8 ? 1 : TN * TW];
   static_assert(kThreads == 256, "one table entry per thread");
   if constexpr (BITS == 4 || BITS == 2) {
     const uint32_t r = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < TW; ++m) ctab[TW * r + m] = tab.c[(r >> (8 / TW * m)) & ((1u << BITS) - 1)];
   } else if constexpr (BITS == 3) {
-    if (threadIdx.x < 16) ctab[threadIdx.x] = tab.c[threadIdx.x];
+    const uint32_t r = threadIdx.x;
+    if (r < 64) {
+      ctab[2 * r] = tab.c[(r & 3) | ((r >> 2) & 4)];
+      ctab[2 * r + 1] = tab.c[((r >> 2) & 3) | ((r >> 3) & 4)];
+    }
   }
   __syncthreads();
   const int64_t rows = d.rows;
@@ -799,16 +798,21 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
           cv[4 * m + 2] = e.z;
           cv[4 * m + 3] = e.w;
         }
+      } else if constexpr (BITS == 3) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // elements 2m, 2m + 1: low bits from the 2-bit plane, high bits from the
+          // 1-bit plane ([turboq] block_turboq3_0)
+          const uint32_t r = ((raw.a[k] >> (4 * m)) & 15u) | (((raw.b[k] >> (2 * m)) & 3u) << 4);
+          const float2 e = reinterpret_cast<const float2*>(ctab)[r];
+          cv[2 * m] = e.x;
+          cv[2 * m + 1] = e.y;
+        }
       } else {
         uint32_t code[8];
         chunk_codes<BITS>(raw, k, code);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if constexpr (BITS == 8)
-            cv[i] = static_cast<float>(code[i]) - 127.5f;
-          else
-            cv[i] = ctab[code[i]];
-        }
+        for (int i = 0; i < 8; ++i) cv[i] = static_cast<float>(code[i]) - 127.5f;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {

@@ -111,8 +111,8 @@ typedef struct {
  * [Spec] "Step 1"/"Step 2", with [Spec] "As-Built Notes" L2 normalization),
  * built as in [Spec] "Codebook Generation": uniform start, centroids = conditional
  * means, boundaries = midpoints, iterated to convergence (|change| < 1e-12) in fp64
- * and stored as fp32.  dim in [4, 65536]; bits in {2, 3, 4, 8} (8: grid, arrays
- * zeroed).  Host only: pure, deterministic, touches no device.
+ * and stored as fp32.  dim in [4, 512] (FA_TQ_EINVAL outside); bits in {2, 3, 4, 8}
+ * (8: grid, arrays zeroed).  Host only: pure, deterministic, touches no device.
  */
 fa_tq_status fa_tq_codebook_init(int32_t dim, int32_t bits, fa_tq_codebook *out);
 

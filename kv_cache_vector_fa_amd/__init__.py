@@ -217,10 +217,22 @@ def decode(cb: Codebook, seed: int, codes, norms, head_dim: int, out=None, strea
     import torch
     lib = load()
     nblk = head_dim // QK
-    n_vec = codes.numel() // (nblk * code_bytes(cb.bits))
+    cbytes = code_bytes(cb.bits)
+    if head_dim % QK or codes.dim() < 2 or tuple(codes.shape[-2:]) != (nblk, cbytes) or \
+            codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError(f"codes: expected contiguous uint8 [..., {nblk}, {cbytes}], got "
+                         f"{codes.dtype} {tuple(codes.shape)}")
+    n_vec = codes.numel() // (nblk * cbytes)
+    if norms.dtype != torch.int16 or not norms.is_contiguous() or norms.numel() != n_vec * nblk:
+        raise ValueError(f"norms: expected {n_vec * nblk} contiguous int16 (fp16 bits), got "
+                         f"{norms.dtype} {tuple(norms.shape)}")
     if out is None:
         out = torch.empty(tuple(codes.shape[:-2]) + (head_dim,), dtype=torch.float32,
                           device=codes.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n_vec * head_dim:
+        raise ValueError(f"out: expected {n_vec * head_dim} contiguous float32, got "
+                         f"{out.dtype} {tuple(out.shape)}")
+    _same_device(codes, norms, out)
     _check(lib.fa_tq_decode(ctypes.byref(cb), seed, head_dim, _ptr(codes), _ptr(norms), n_vec,
                             _ptr(out), _stream(stream)))
     return out
@@ -310,6 +322,13 @@ def attn_decode(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, 
     return out
 
 
+def _same_device(*ts):
+    """Every tensor on one GPU (the kernels take raw device addresses)."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError(f"tensors must share one GPU device, got {sorted(map(str, devs))}")
+
+
 def _expect(t, shape, dtype, name):
     """Shape/dtype/contiguity check of a device buffer the kernels index densely."""
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
@@ -348,11 +367,21 @@ def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = No
     """``encode`` with its arguments marshalled once: returns a callable that launches
     fa_tq_encode on the same tensors (for tight loops where per-call Python work
     would dominate the kernel)."""
+    import torch
     lib = load()
     B, H, T, d = x.shape
     if x.stride(3) != 1:
         raise ValueError("channel stride must be 1")
     t_max = T if t_max is None else t_max
+    whole = bool(flags & WHOLE_VECTOR)
+    nblk = (whole_length(d) if whole else d) // QK
+    if not whole and d % QK:
+        raise ValueError(f"head_dim {d} is not a multiple of {QK}")
+    _expect(codes, (B, H, t_max, nblk, code_bytes(cb.bits)), torch.uint8, "codes")
+    _expect(norms, (B, H, t_max, 1 if whole else nblk), torch.int16, "norms")
+    if t0 is not None:
+        _expect(t0, (B,), torch.int32, "t0")
+    _same_device(x, codes, norms, t0)
     args = (ctypes.byref(cb), ctypes.c_uint64(seed), ctypes.c_int32(d), _ptr(x),
             ctypes.c_int(_dtype_code(x)), Layout(x.stride(0), x.stride(1), x.stride(2)),
             ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(T), _ptr(t0),
@@ -370,9 +399,19 @@ def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_no
                      v_norms, seq_lens, scale: float, out, workspace, stream=None,
                      flags: int = 0):
     """``attn_decode`` with its arguments marshalled once (see ``encode_call``)."""
+    import torch
     lib = load()
     B, Hq, d = q.shape
     Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _expect(seq_lens, (B,), torch.int32, "seq_lens")
+    _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
+    _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
+    _expect(out, (B, Hq, d), torch.float32, "out")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_device(q, seq_lens, k_codes, k_norms, v_codes, v_norms, out, workspace)
     args = (ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_int32(d),
             _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_codes), _ptr(k_norms),
             _ptr(v_codes), _ptr(v_norms), _ptr(seq_lens), ctypes.c_int32(B),
@@ -409,6 +448,9 @@ def attn_append_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new,
     _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
     _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
     _expect(out, (B, Hq, d), torch.float32, "out")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_device(q, k_new, v_new, pos, k_codes, k_norms, v_codes, v_norms, out, workspace)
     args = (ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_int32(d),
             _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_new), _ptr(v_new),
             ctypes.c_int(_dtype_code(k_new)),

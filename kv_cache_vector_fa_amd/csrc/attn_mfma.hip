@@ -10,16 +10,26 @@
 // scores K~ (16 x 128) . Q'^T (128 x G) and values P (G x 16) . V~ (16 x 128).
 // Both run on v_mfma_f32_16x16x32_f16 (8 k-steps of 32 slots per product).
 //
-// Accuracy (fp32 level from fp16 operands, all splits exact in fp32):
-//  * every centroid value is split as 4c = hi + lo (fp16 each; the factor 4 is exact
-//    and keeps lo in the fp16 normal range).  Four k-slots hold two elements:
-//    A = [hi(c_e0), hi(c_e1), lo(c_e0), lo(c_e1)], B = [q_e0, q_e1, q_e0, q_e1];
+// Accuracy (about 22 significant bits per product, every fp16 product exact in the
+// fp32 accumulator, every fp16 half rounded to nearest):
+//  * every centroid value is split as 64c = hi + lo (fp16 each; the factor 64 is exact
+//    and keeps lo in the fp16 normal range for every 2-4 bit table of dimension 128).
+//    Four k-slots hold two elements: A = [hi(c_e0), hi(c_e1), lo(c_e0), lo(c_e1)],
+//    B = [q_e0, q_e1, q_e0, q_e1];
 //  * queries: B columns 0..G-1 hold hi(q'), columns G..2G-1 hold lo(q'); the two
-//    score columns of a head are added (q' is scaled by a power of two so |q'| < 1);
+//    score columns of a head are added (q' is scaled by a power of two so that
+//    2^13 <= max |q'| < 2^14);
 //  * values: B = [hi(v_ta), hi(v_tb), lo(v_ta), lo(v_tb)] for two tokens, and the
-//    probabilities A = [p_ta, p_tb, p_ta, p_tb] with rows 0..G-1 = hi(p'), rows
-//    G..2G-1 = lo(p'); the two output rows of a head are added at the end.
-// Every fp16 product is exact in the fp32 accumulator.
+//    weights A = [w_ta, w_tb, w_ta, w_tb] with rows 0..G-1 = hi(w), rows G..2G-1 =
+//    lo(w), w = p * n_V * vs; the two output rows of a head are added at the end.
+//    p <= 1, and vs is a power of two per wave, lowered (the accumulator rescaled
+//    with it) whenever a super tile holds a value norm n with n * vs > 2^15, so the
+//    weights of a wave's stream stay below 2^15 and lo(w) is an fp16 normal number
+//    unless w < 2^-3.  The rounding error of one token's weight is then at most
+//    2^-22 w + 2^-25 (absolute floor of the fp16 subnormals), i.e. relative to the
+//    largest value norm of the stream at most 2^-22 + 2^-40 per token, with no sign
+//    bias (round to nearest), and the fp32 normaliser l carries exact p.
+// Scores and weights therefore carry fp32-level rounding, not fp16-level.
 //
 // Dequantization is a table look-up in LDS returning a ready MFMA operand.  One
 // 64 KB table has a 256-byte row per index byte r:
@@ -68,7 +78,8 @@ constexpr int kMaxG = 8;         // query heads per KV head on this path
 constexpr int kRow = 256;        // table bytes per index byte
 constexpr int kMaxSplit = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kCScale = 4.0f;  // centroid pre-scale (exact)
+constexpr float kCScale = 64.0f;  // centroid pre-scale (exact)
+constexpr float kWMax = 32768.0f;  // bound of the value weights w = p n_V vs
 // Raw buffer resources: an access at or beyond the range returns zeros, so loads
 // past the sequence need no clamp and lanes without work use offset kOOB.
 constexpr int32_t kRsrcWord3 = 0x00020000;
@@ -113,6 +124,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Maximum over each row of 16 lanes (every lane of the row gets it).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
+  return x;
 }
 
 // Spread 8 two-bit fields (bits 2i..2i+1) to nibbles (bits 4i..4i+1).
@@ -448,9 +473,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   lds_barrier();   // tables and per-head maxima complete
   float qmax = 0.0f;
   for (int h = 0; h < G; ++h) qmax = fmaxf(qmax, qmx[h]);
+  // qscale = 2^e with 2^13 <= max |q'| / qscale < 2^14 (e >= -110: a query that
+  // small gives scores of 0 either way, and 1 / qscale stays finite)
   int qex = 0;
   frexpf(qmax * kInvSqrtQK, &qex);
-  const float qscale = qmax > 0.0f ? ldexpf(1.0f, qex) : 1.0f;
+  const float qscale = qmax > 0.0f ? ldexpf(1.0f, max(qex - 14, -110)) : 1.0f;
   {
     const float inv = kInvSqrtQK / qscale;
 #pragma unroll
@@ -487,21 +514,41 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
                      ((VSH ? ((lane & 15) << 3) : V2 ? 128 + ((lane & 7) << 4) : 128 + ((lane & 15) << 3)) << 8);
 
   float m_run = -INFINITY, l_run = 0.0f;
+  // value weight scale of this wave's stream; above any value a norm needs, so the
+  // first super tile with a nonzero value norm sets it
+  float vs = 18446744073709551616.0f;   // 2^64
   f4 o[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   auto process = [&](const Codes<KB, VB>& cur, int s0) {
     // per-token factors through LDS: key scale (0 when masked), key bias (-inf when
-    // masked), value scale
+    // masked), value weight factor n_V * vs
     {
       const int t = s0 + (lane & 31);
       const float nf = __half2float(__ushort_as_half(static_cast<uint16_t>(cur.nrm)));
+      // the largest value norm of the super tile (lanes 32..63; past the sequence the
+      // loads return 0) bounds every weight p n_V (p <= 1): lower vs, and rescale the
+      // accumulator by the same power of two, when it would push a weight past kWMax
+      const float rm = row_max16(nf);
+      const float vmax = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                   __builtin_bit_cast(int, rm), 32)),
+                               __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                   __builtin_bit_cast(int, rm), 48)));
+      if (vmax * vs > kWMax) {
+        int e = 0;
+        frexpf(vmax, &e);                       // vmax < 2^e
+        const float vs_new = ldexpf(kWMax, -e);  // vmax * vs_new < 2^15
+        const float r = vs_new / vs;            // a power of two
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] *= r;
+        vs = vs_new;
+      }
       if (lane < 32) {
         nrm[wave][0][lane] = t < c1 ? nf * sc2 : 0.0f;
         nrm[wave][1][lane] = t < c1 ? 0.0f : -INFINITY;
       } else {
-        nrm[wave][2][lane - 32] = nf * (1.0f / kCScale);
+        nrm[wave][2][lane - 32] = nf * vs;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -574,13 +621,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
       const float4 fv = *reinterpret_cast<const float4*>(&nrm[wave][2][16 * t4 + 4 * qq]);
       const float pa = p[t4][0] * fv.x, pb = p[t4][1] * fv.y;
       const float pc = p[t4][2] * fv.z, pd = p[t4][3] * fv.w;
-      // hi = fp16 pair rounded toward zero, lo = the exact fp32 remainder in fp16
-      const auto hab = __builtin_amdgcn_cvt_pkrtz(pa, pb);
-      const auto hcd = __builtin_amdgcn_cvt_pkrtz(pc, pd);
-      const auto lab2 = __builtin_amdgcn_cvt_pkrtz(pa - static_cast<float>(hab[0]),
-                                                   pb - static_cast<float>(hab[1]));
-      const auto lcd2 = __builtin_amdgcn_cvt_pkrtz(pc - static_cast<float>(hcd[0]),
-                                                   pd - static_cast<float>(hcd[1]));
+      // hi = nearest fp16, lo = nearest fp16 of the exact fp32 remainder
+      _Float16 ha, la, hb, lb, hc, lc, hd, ld;
+      split_h(pa, ha, la);
+      split_h(pb, hb, lb);
+      split_h(pc, hc, lc);
+      split_h(pd, hd, ld);
+      const h2 hab = {ha, hb}, hcd = {hc, hd}, lab2 = {la, lb}, lcd2 = {lc, ld};
       const uint32_t lab = row_up<GT>(__builtin_bit_cast(uint32_t, lab2), G);
       const uint32_t lcd = row_up<GT>(__builtin_bit_cast(uint32_t, lcd2), G);
       const uint32_t pab = n < G ? __builtin_bit_cast(uint32_t, hab) : (n < 2 * G ? lab : 0u);
@@ -642,12 +689,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   // split's partial (m, l, o') per head
   __syncthreads();
   float* comb_o = reinterpret_cast<float*>(tab);
+  const float ovs = 1.0f / (kCScale * vs);   // a power of two: o' = o / (64 vs)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * qq + j;
     if (r < 2 * G) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) comb_o[(wave * 2 * kMaxG + r) * QK + 8 * n + m] = o[m][j];
+      for (int m = 0; m < 8; ++m)
+        comb_o[(wave * 2 * kMaxG + r) * QK + 8 * n + m] = o[m][j] * ovs;
     }
   }
   if (qq == 0 && n < G) {

@@ -87,6 +87,45 @@ def attend_fused(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits
     return out
 
 
+def attend_fused_counted(q, k_codes, k_norms, v_codes, v_norms, counts, k_bits, v_bits,
+                         k_centroids, v_centroids, s, scale, s2=None):
+    """fp64 fused attention of one sequence and KV head over a cache given as distinct
+    tokens with multiplicities (test infrastructure for caches too long to unpack).
+
+    A cache in which token j occurs counts[j] times has the softmax of [Spec]
+    "Optimization: Fused dequant-dot" over all its slots, so token j's weight is
+    counts[j] * exp(s_j - m) / sum_i counts[i] * exp(s_i - m): the same steps as
+    ``attend_fused`` with each exponential multiplied by its count.
+
+    q: [G, d] (the query heads of the KV head); k_codes/v_codes: [n, nblk, cb] uint8;
+    k_norms/v_norms: [n, nblk] float16; counts: [n] non-negative integers.
+    Returns out [G, d] float64.
+    """
+    q = np.asarray(q, np.float64)
+    G, d = q.shape
+    nblk = d // QK
+    n = k_codes.shape[0]
+    w = np.asarray(counts, np.float64)
+    kc = np.asarray(k_centroids, np.float32).astype(np.float64)[unpack(k_codes, k_bits)]
+    vc = np.asarray(v_centroids, np.float32).astype(np.float64)[unpack(v_codes, v_bits)]
+    kc, vc = kc.reshape(n, nblk, QK), vc.reshape(n, nblk, QK)
+    kn = np.asarray(k_norms, np.float16).astype(np.float64).reshape(n, nblk)
+    vn = np.asarray(v_norms, np.float16).astype(np.float64).reshape(n, nblk)
+    out = np.zeros((G, d), np.float64)
+    live = w > 0
+    if not np.any(live):
+        return out
+    for h in range(G):
+        qr = forward64(q[h], s, s2).reshape(nblk, QK)
+        scores = scale * np.sum(kn * np.einsum("tjc,jc->tj", kc, qr), axis=-1)
+        m = np.max(scores[live])
+        e = np.where(live, w * np.exp(np.where(live, scores - m, 0.0)), 0.0)
+        p = e / np.sum(e)
+        o_rot = np.einsum("t,tj,tjc->jc", p, vn, vc)
+        out[h] = inverse64(o_rot.reshape(d), s, s2)
+    return out
+
+
 def attend_bruteforce(q, k_codes, k_norms, v_codes, v_norms, seq_lens, k_bits, v_bits,
                       k_centroids, v_centroids, s, scale, s2=None):
     """softmax(scale * q K_hat^T) V_hat on the decoded cache, fp64 (tiny inputs)."""

@@ -159,7 +159,7 @@ def test_attn_long_context_full_sampled(gpu_lib):
     vp, vn = _random_cache(w.batch, w.n_kv_heads, w.tokens, w.v_bits, 42)
     lens = workloads.make_seq_lens(w)
     q = workloads.make_q(w, "cuda")
-    heads = [(0, 0), (1, 9), (3, 31)]
+    heads = [(0, 0), (1, 9), (2, 20), (3, 31)]   # four (sequence, KV head) slices
     _run(gpu_lib, q, kp, kn, vp, vn, lens, w.k_bits, w.v_bits, 1 / np.sqrt(128), heads=heads,
          where="long_context")
 
@@ -203,3 +203,62 @@ def test_attn_largest_t_max(gpu_lib):
     err = float(np.max(np.abs(out.cpu().numpy() - ref)))
     say(f"largest t_max: max abs err {err:.3e}")
     assert err <= ATTN_MAX_ABS
+
+
+def test_attn_sink_and_faint_tail(gpu_lib):
+    """Value weights far below one next to a dominant token, over a long stream.
+
+    t_max = 2^25 - 1 slots of one KV head with 4 query heads (K4/V2).  Slot 0 is a
+    sink (the highest score); slots 1 .. 65535 hold keys whose softmax weights
+    relative to the sink are log-spread over [1e-7, 1e-5] (61 distinct key norms
+    in turn), all with the same value codes (the largest centroid in every
+    element, a sign-coherent value row) and value norm 1, so rounding of their
+    weights cannot cancel; every later slot has a key pointing away from the query
+    (weight 0 in fp32, below 1e-120 in fp64).  Each wave of the first split streams
+    thousands of these faint tokens after the sink, the case where a one-signed
+    rounding of small weights would add up.  The reference is the oracle's fused
+    attention over the distinct tokens with their multiplicities."""
+    from oracle import rotation
+    torch = _torch()
+    fa = gpu_lib
+    T, C, P = (1 << 25) - 1, 1 << 16, 61
+    scale = 1 / np.sqrt(128)
+    ck4, cv2 = o_cb.codebook(4)[1], o_cb.codebook(2)[1]
+    a = np.array([0.1, 0.1, 0.08, 0.12])          # q'_h = a_h * (1, ..., 1)
+    kfac = scale * 128 * float(ck4[15])           # score per unit key norm and unit a
+    n_sink = 100.0
+    p_want = np.exp(np.linspace(np.log(1e-7), np.log(1e-5), P))
+    n_cold = (n_sink + np.log(p_want) / (kfac * a[0])).astype(np.float16)
+    say(f"attn sink + faint tail: t_max={T}, {C - 1} faint slots, key norms "
+        f"{float(n_cold.min()):.2f}..{float(n_cold.max()):.2f}")
+    dev = "cuda"
+    kp = torch.full((1, 1, T, 1, 64), 0xFF, dtype=torch.uint8, device=dev)
+    kp[0, 0, C:] = 0
+    kn = torch.full((1, 1, T, 1), 1000.0, dtype=torch.float16, device=dev)
+    kn[0, 0, 0, 0] = n_sink
+    reps = -(-(C - 1) // P)
+    kn[0, 0, 1:C, 0] = torch.from_numpy(np.tile(n_cold, reps)[:C - 1]).to(dev)
+    vp = torch.full((1, 1, T, 1, 32), 0xFF, dtype=torch.uint8, device=dev)
+    vn = torch.full((1, 1, T, 1), 1.0, dtype=torch.float16, device=dev)
+    vn[0, 0, 0, 0] = 8.0
+    s = o_signs.signs(SEED, 128)
+    q = rotation.inverse64(a[:, None] * np.ones((4, 128)), s).astype(np.float32)[None]
+    ck, cv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    out = fa.attn_decode(ck, cv, SEED, torch.from_numpy(q).to(dev), kp, kn.view(torch.int16),
+                         vp, vn.view(torch.int16),
+                         torch.tensor([T], dtype=torch.int32, device=dev), scale)
+    torch.cuda.synchronize()
+    del kp, kn, vp, vn
+    # distinct tokens: sink, the P faint keys, the far key
+    counts = np.concatenate([[1], np.bincount(np.arange(C - 1) % P, minlength=P), [T - C]])
+    dk = np.full((P + 2, 1, 64), 0xFF, np.uint8)
+    dk[-1] = 0
+    dkn = np.concatenate([[n_sink], n_cold, [1000.0]]).astype(np.float16).reshape(-1, 1)
+    dv = np.full((P + 2, 1, 32), 0xFF, np.uint8)
+    dvn = np.ones((P + 2, 1), np.float16)
+    dvn[0] = 8.0
+    ref = o_att.attend_fused_counted(q[0], dk, dkn, dv, dvn, counts, 4, 2, ck4, cv2, s, scale)
+    err = float(np.max(np.abs(out.cpu().numpy()[0] - ref)))
+    say(f"sink + faint tail: max abs err {err:.3e} (|out| max {np.max(np.abs(ref)):.2f})")
+    assert err <= ATTN_MAX_ABS, err
+    assert err <= ATTN_MAX_ABS / 10, f"no margin left: {err}"

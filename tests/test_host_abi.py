@@ -231,3 +231,69 @@ def test_decode_kv_rejects_an_output_row_of_2_gib(lib):
     assert lib.fa_tq_decode_kv(ctypes.byref(cb), 42, 0, 128, P, P, 1, 1, 3, 3, P,
                                fa.FA_TQ_BF16, big, None) == fa.FA_TQ_EUNSUPPORTED
     assert "2 GiB" in lib.fa_tq_last_error().decode()
+
+
+def _attn_args(B=2, Hq=8, Hkv=2, T=64, kb=4, vb=2):
+    """CPU tensors with the shapes attn_decode_call expects (no device is touched:
+    every check runs before the library call)."""
+    import torch
+    t = dict(
+        q=torch.zeros((B, Hq, 128), dtype=torch.bfloat16),
+        k_codes=torch.zeros((B, Hkv, T, 1, fa.code_bytes(kb)), dtype=torch.uint8),
+        k_norms=torch.zeros((B, Hkv, T, 1), dtype=torch.int16),
+        v_codes=torch.zeros((B, Hkv, T, 1, fa.code_bytes(vb)), dtype=torch.uint8),
+        v_norms=torch.zeros((B, Hkv, T, 1), dtype=torch.int16),
+        seq_lens=torch.full((B,), T, dtype=torch.int32),
+        out=torch.zeros((B, Hq, 128), dtype=torch.float32),
+        workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    return t
+
+
+def _call_attn(t, kb=4, vb=2):
+    cbk, cbv = fa.codebook_init(128, kb), fa.codebook_init(128, vb)
+    return fa.attn_decode_call(cbk, cbv, 42, t["q"], t["k_codes"], t["k_norms"], t["v_codes"],
+                               t["v_norms"], t["seq_lens"], 0.1, t["out"], t["workspace"])
+
+
+@pytest.mark.parametrize("case", ["int64_lens", "short_v_cache", "v_heads", "q_strided",
+                                  "out_dtype", "k_norms_f32", "cpu_tensors"])
+def test_attn_binding_rejects_bad_tensors(lib, case):
+    """The binding checks dtype, shape and contiguity of every tensor before any
+    launch (an int64 length array would be read as int32 pairs; a smaller value
+    cache would be addressed with the key cache's sizes)."""
+    import torch
+    t = _attn_args()
+    if case == "int64_lens":
+        t["seq_lens"] = t["seq_lens"].to(torch.int64)
+    elif case == "short_v_cache":
+        t["v_codes"], t["v_norms"] = t["v_codes"][:, :, :32], t["v_norms"][:, :, :32]
+    elif case == "v_heads":
+        t["v_codes"], t["v_norms"] = t["v_codes"][:, :1].contiguous(), t["v_norms"][:, :1].contiguous()
+    elif case == "q_strided":
+        t["q"] = torch.zeros((2, 16, 128), dtype=torch.bfloat16)[:, ::2]
+    elif case == "out_dtype":
+        t["out"] = t["out"].to(torch.bfloat16)
+    elif case == "k_norms_f32":
+        t["k_norms"] = t["k_norms"].to(torch.float32)
+    with pytest.raises(ValueError):
+        _call_attn(t)
+
+
+def test_encode_and_decode_binding_reject_bad_buffers(lib):
+    import torch
+    cb = fa.codebook_init(128, 4)
+    x = torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16)
+    codes = torch.zeros((1, 2, 16, 1, 64), dtype=torch.uint8)
+    norms = torch.zeros((1, 2, 16, 1), dtype=torch.int16)
+    with pytest.raises(ValueError):   # codes sized for 2-bit rows
+        fa.encode_call(cb, 42, x, codes[..., :32].contiguous(), norms)
+    with pytest.raises(ValueError):   # fewer cache slots than tokens x t_max claims
+        fa.encode_call(cb, 42, x, codes, norms, t_max=32)
+    with pytest.raises(ValueError):   # t0 of the wrong dtype
+        fa.encode_call(cb, 42, x, codes, norms, t0=torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError):   # CPU tensors never reach the library
+        fa.encode_call(cb, 42, x, codes, norms)
+    with pytest.raises(ValueError):   # norms for fewer vectors than codes
+        fa.decode(cb, 42, codes, norms[:, :, :8].contiguous(), 128)
+    with pytest.raises(ValueError):   # an output of the wrong dtype
+        fa.decode(cb, 42, codes, norms, 128, out=torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16))

@@ -208,3 +208,26 @@ def test_append_per_sequence_positions():
         c = _cache(kk, vv, s, 4, 2)
         ref = att.attend_bruteforce(q[b:b + 1], *c, [L], 4, 2, ck, cv, s, 0.09)
         np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3)])
+def test_counted_equals_repeated_cache(kb, vb):
+    """The multiset form equals attend_fused on the cache with every distinct token
+    written out counts[j] times (in any slot order), and zero counts drop a token."""
+    rng = np.random.default_rng(7)
+    d, n, G = 128, 6, 4
+    s = sg.signs(42, d)
+    kx = (rng.standard_normal((1, 1, n, d)) * rng.uniform(0.5, 4.0, (1, 1, n, 1))).astype(np.float32)
+    vx = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    q = rng.standard_normal((1, G, d)).astype(np.float32)
+    kc, kn, vc, vn = _cache(kx, vx, s, kb, vb)
+    ck, cv = cbm.codebook(kb)[1], cbm.codebook(vb)[1]
+    counts = np.array([3, 1, 0, 7, 2, 5])
+    idx = rng.permutation(np.repeat(np.arange(n), counts))
+    full = att.attend_fused(q, kc[:, :, idx], kn[:, :, idx], vc[:, :, idx], vn[:, :, idx],
+                            [idx.size], kb, vb, ck, cv, s, 0.3)
+    got = att.attend_fused_counted(q[0], kc[0, 0], kn[0, 0], vc[0, 0], vn[0, 0], counts, kb, vb,
+                                   ck, cv, s, 0.3)
+    np.testing.assert_allclose(got, full[0], rtol=0, atol=1e-12)
+    assert np.all(att.attend_fused_counted(q[0], kc[0, 0], kn[0, 0], vc[0, 0], vn[0, 0],
+                                           np.zeros(n), kb, vb, ck, cv, s, 0.3) == 0)

@@ -217,7 +217,14 @@ def test_attn_sink_and_faint_tail(gpu_lib):
     (weight 0 in fp32, below 1e-120 in fp64).  Each wave of the first split streams
     thousands of these faint tokens after the sink, the case where a one-signed
     rounding of small weights would add up.  The reference is the oracle's fused
-    attention over the distinct tokens with their multiplicities."""
+    attention over the distinct tokens with their multiplicities.
+
+    A weight rounding biased toward zero (fp16 halves of p * n_V cut to the fp16
+    subnormal step) loses about 2.5e-3 here (CPU emulation); round-to-nearest halves
+    in the normal range leave the fp32 accumulation of ~1024 MFMA tile sums per wave
+    onto a sink-sized accumulator (at most ~2^-24 of it per addition, 6e-5 relative
+    in all, 7e-4 on these outputs of magnitude 12).  The test asks for half the
+    contract's tolerance."""
     from oracle import rotation
     torch = _torch()
     fa = gpu_lib
@@ -261,4 +268,4 @@ def test_attn_sink_and_faint_tail(gpu_lib):
     err = float(np.max(np.abs(out.cpu().numpy()[0] - ref)))
     say(f"sink + faint tail: max abs err {err:.3e} (|out| max {np.max(np.abs(ref)):.2f})")
     assert err <= ATTN_MAX_ABS, err
-    assert err <= ATTN_MAX_ABS / 10, f"no margin left: {err}"
+    assert err <= ATTN_MAX_ABS / 2, f"no margin left: {err}"

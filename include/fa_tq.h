@@ -236,6 +236,35 @@ fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook *cb_k, const fa_tq_codebo
                                   int32_t n_kv_heads, int32_t t_max, float scale, float *out,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the per-GPU scratch array of fa_tq_attn_decode_noalloc (8 MiB). */
+#define FA_TQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * fa_tq_attn_decode_ex without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus workspace and
+ * workspace_bytes), same kernels and results as fa_tq_attn_decode_ex; the per-split
+ * partial results go to a scratch array of FA_TQ_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds in the memory of each GPU it runs on until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Sizes whose partials (fa_tq_attn_workspace_bytes) exceed the array are rejected
+ *   with FA_TQ_EUNSUPPORTED, before anything is launched.
+ *   The array of the current device is used; its device address is looked up once
+ *   per device, on the first call on that device (make that first call outside
+ *   graph capture).
+ *   Every call on one GPU shares its array, which keeps the last call's contents:
+ *   calls that can overlap on one GPU (several streams or host threads) race and
+ *   give wrong results; calls in order on one stream are safe.
+ */
+fa_tq_status fa_tq_attn_decode_noalloc(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                                       uint64_t seed, uint32_t flags, int32_t head_dim,
+                                       const void *q, fa_tq_dtype q_dtype,
+                                       const uint8_t *k_codes, const uint16_t *k_norms,
+                                       const uint8_t *v_codes, const uint16_t *v_norms,
+                                       const int32_t *seq_lens, int32_t batch,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t t_max,
+                                       float scale, float *out, void *stream);
+
 /*
  * Append, then attend ([Spec] "Attention with TurboQuant cache": the cached-attention
  * call quantizes the current K and V into the cache, then attends with the full-

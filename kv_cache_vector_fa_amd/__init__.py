@@ -80,6 +80,13 @@ _SIGS = {
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P,
                                          _P, ctypes.c_size_t, _P]),
 }
+# fa_tq_attn_decode_ex without the workspace pointer and size.
+_SIGS["fa_tq_attn_decode_noalloc"] = (
+    ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook), ctypes.c_uint64,
+                   ctypes.c_uint32, ctypes.c_int32, _P, ctypes.c_int, _P, _P, _P, _P, _P,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_float, _P, _P])
+NOALLOC_SCRATCH_BYTES = 8 << 20   # FA_TQ_NOALLOC_SCRATCH_BYTES
 # The _ex entry points take the variant flags right after the seed.
 for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
     _r, _a = _SIGS[_name]
@@ -327,6 +334,32 @@ def _same_device(*ts):
     devs = {t.device for t in ts if t is not None}
     if len(devs) != 1 or next(iter(devs)).type != "cuda":
         raise ValueError(f"tensors must share one GPU device, got {sorted(map(str, devs))}")
+
+
+def attn_decode_noalloc(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms,
+                        v_codes, v_norms, seq_lens, scale: float, out, stream=None,
+                        flags: int = 0):
+    """``attn_decode`` through fa_tq_attn_decode_noalloc: no workspace, the split
+    partials go to the library's per-GPU scratch array (calls that overlap on one
+    GPU race).  ``out`` [B, Hq, d] float32 must be given (nothing is allocated)."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _expect(seq_lens, (B,), torch.int32, "seq_lens")
+    _expect_cache(k_codes, k_norms, B, Hkv, t_max, d, cb_k.bits, "k cache")
+    _expect_cache(v_codes, v_norms, B, Hkv, t_max, d, cb_v.bits, "v cache")
+    _expect(out, (B, Hq, d), torch.float32, "out")
+    _same_device(q, seq_lens, k_codes, k_norms, v_codes, v_norms, out)
+    _check(lib.fa_tq_attn_decode_noalloc(
+        ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_uint32(flags),
+        ctypes.c_int32(d), _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_codes),
+        _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(seq_lens), ctypes.c_int32(B),
+        ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max), ctypes.c_float(scale),
+        _ptr(out), _stream(stream)))
+    return out
 
 
 def _expect(t, shape, dtype, name):

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -370,6 +371,35 @@ fa_tq_status encode_impl(const char* who, const fa_tq_codebook* cb, uint64_t see
                   who);
 }
 
+// Split partials of fa_tq_attn_decode_noalloc: one array per GPU the library runs on,
+// held until the process ends.  Host code never passes `scratch` itself to a kernel
+// (in host code it names a host-side stand-in): it passes the device address that
+// hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) uint8_t scratch[FA_TQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, resolved once per device.
+fa_tq_status scratch_of_current_device(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_TQ_EHIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: device index %d >= %d", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FA_TQ_EHIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
                        const fa_tq_codebook* cb_v, uint64_t seed, uint32_t flags,
                        int32_t head_dim,
@@ -644,6 +674,40 @@ fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook* cb_k, const fa_tq_codebo
   return attn_impl("fa_tq_attn_decode", cb_k, cb_v, seed, flags, head_dim, q, q_dtype,
                    k_codes, k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
                    n_kv_heads, t_max, scale, out, workspace, workspace_bytes, stream);
+}
+
+fa_tq_status fa_tq_attn_decode_noalloc(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                                       uint64_t seed, uint32_t flags, int32_t head_dim,
+                                       const void* q, fa_tq_dtype q_dtype,
+                                       const uint8_t* k_codes, const uint16_t* k_norms,
+                                       const uint8_t* v_codes, const uint16_t* v_norms,
+                                       const int32_t* seq_lens, int32_t batch,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t t_max,
+                                       float scale, float* out, void* stream) {
+  static const char* who = "fa_tq_attn_decode_noalloc";
+  if (batch > 0 && !seq_lens) return fail(FA_TQ_EINVAL, "%s: seq_lens is NULL", who);
+  // every argument checked (with a stand-in workspace address) before the scratch
+  // array is looked up or anything is launched
+  void* const probe = reinterpret_cast<void*>(uintptr_t{256});
+  fa_tq_status st = attn_impl(who, cb_k, cb_v, seed, flags, head_dim, q, q_dtype, k_codes,
+                              k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
+                              n_kv_heads, t_max, scale, out, probe,
+                              FA_TQ_NOALLOC_SCRATCH_BYTES, stream, true);
+  if (st != FA_TQ_OK) {
+    const size_t need = fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, head_dim);
+    if (need > FA_TQ_NOALLOC_SCRATCH_BYTES)
+      return fail(FA_TQ_EUNSUPPORTED,
+                  "%s: these sizes need %zu bytes of split partials, more than the %u-byte "
+                  "scratch array; use fa_tq_attn_decode with a workspace", who, need,
+                  static_cast<unsigned>(FA_TQ_NOALLOC_SCRATCH_BYTES));
+    return st;
+  }
+  if (batch == 0) return ok();
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(who, &ws)) != FA_TQ_OK) return st;
+  return attn_impl(who, cb_k, cb_v, seed, flags, head_dim, q, q_dtype, k_codes, k_norms,
+                   v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads, n_kv_heads, t_max,
+                   scale, out, ws, FA_TQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 fa_tq_status fa_tq_attn_append(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,

@@ -297,3 +297,17 @@ def test_encode_and_decode_binding_reject_bad_buffers(lib):
         fa.decode(cb, 42, codes, norms[:, :, :8].contiguous(), 128)
     with pytest.raises(ValueError):   # an output of the wrong dtype
         fa.decode(cb, 42, codes, norms, 128, out=torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16))
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Partials larger than the scratch array are refused before any device call
+    (the pointers below are never dereferenced)."""
+    B, Hq, Hkv, T = 512, 32, 8, 128
+    assert fa.attn_workspace_bytes(B, Hq, Hkv, T) > fa.NOALLOC_SCRATCH_BYTES
+    cb = fa.codebook_init(128, 4)
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.fa_tq_attn_decode_noalloc(ctypes.byref(cb), ctypes.byref(cb), 42, 0, 128, fake,
+                                       fa.FA_TQ_BF16, fake, fake, fake, fake, fake, B, Hq, Hkv,
+                                       T, 0.1, fake, None)
+    assert st == fa.FA_TQ_EUNSUPPORTED
+    assert "scratch" in lib.fa_tq_last_error().decode()

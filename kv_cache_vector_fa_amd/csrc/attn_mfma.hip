@@ -16,50 +16,65 @@
 //    and keeps lo in the fp16 normal range for every 2-4 bit table of dimension 128).
 //    Four k-slots hold two elements: A = [hi(c_e0), hi(c_e1), lo(c_e0), lo(c_e1)],
 //    B = [q_e0, q_e1, q_e0, q_e1];
-//  * queries: B columns 0..G-1 hold hi(q'), columns G..2G-1 hold lo(q'); the two
-//    score columns of a head are added (q' is scaled by a power of two so that
-//    2^13 <= max |q'| < 2^14);
+//  * queries: B column h < G holds hi(q'_h), column 15 - h holds lo(q'_h) (q' is
+//    scaled by a power of two so that 2^13 <= max |q'| < 2^14).  One DPP add of the
+//    mirrored lane (row_mirror) gives both lanes h and 15 - h the full score of head h;
 //  * values: B = [hi(v_ta), hi(v_tb), lo(v_ta), lo(v_tb)] for two tokens, and the
-//    weights A = [w_ta, w_tb, w_ta, w_tb] with rows 0..G-1 = hi(w), rows G..2G-1 =
-//    lo(w), w = p * n_V * vs; the two output rows of a head are added at the end.
-//    p <= 1, and vs is a power of two per wave, lowered (the accumulator rescaled
-//    with it) whenever a super tile holds a value norm n with n * vs > 2^15, so the
-//    weights of a wave's stream stay below 2^15 and lo(w) is an fp16 normal number
-//    unless w < 2^-3.  The rounding error of one token's weight is then at most
-//    2^-22 w + 2^-25 (absolute floor of the fp16 subnormals), i.e. relative to the
-//    largest value norm of the stream at most 2^-22 + 2^-40 per token, with no sign
-//    bias (round to nearest), and the fp32 normaliser l carries exact p.
-// Scores and weights therefore carry fp32-level rounding, not fp16-level.
+//    weights A = [w_ta, w_tb, w_ta, w_tb] with row h = hi(w) and row 15 - h = lo(w)
+//    of head h, each lane taking the half of its own row (no lane moves); the two
+//    output rows of a head are added at the end.  w = p * n_V * vs with p <= 2^8 (see
+//    the softmax below) and vs a power of two per wave, lowered (the accumulator
+//    rescaled with it) whenever a super tile holds a value norm n with n * vs > 2^7,
+//    so every weight stays below 2^15 and lo(w) is an fp16 normal number unless
+//    w < 2^-3: a token's weight is off by at most 2^-22 w + 2^-25 (the fp16 subnormal
+//    step), relative to the stream's largest weight 2^-22 + 2^-40, with no sign bias.
+// The fp32 normaliser l carries the exact p.  What remains is fp32 accumulation.
 //
-// Dequantization is a table look-up in LDS returning a ready MFMA operand.  One
-// 64 KB table has a 256-byte row per index byte r:
-//  * bytes [0, 128): key entry r (two 4-bit key codes: low nibble first element),
-//    8 bytes replicated 16 times;
-//  * bytes [128, 256): value entry r.  2-bit values: r holds the codes of one
-//    element in the four tokens of a lane's operand, and the 16-byte entry is that
-//    whole operand, replicated 8 times; 3/4-bit values: r holds the codes of one
-//    element in two tokens (8 bytes, 16 replicas).  When keys and values share a codebook the value
-//    look-ups use the key half.
-// A look-up address is one v_perm: (index byte << 8) | replica offset of the lane.
-// Lane L reads replica L % 16 (8-byte entries) or L % 8 (16-byte entries), so the
-// lanes an LDS cycle serves hit distinct banks.
+// Online softmax with a lazy reference (base 2): p = 2^(s - m) against a per-head
+// reference m that only moves when a super tile holds a score above m + 8 (or on the
+// first tile); then m becomes the tile's true maximum and l and the accumulator are
+// rescaled.  So p <= 2^8, and the usual path needs no cross-lane maximum or sum:
+// each lane keeps the partial l of its own tokens, added across lanes at the end.
+//
+// Dequantization is a table look-up in LDS returning a ready MFMA operand; the rows
+// are laid out so that a wave's look-ups never share an LDS bank (gfx950: 64 banks,
+// a ds_read_b64 serves 32 lanes per cycle, a ds_read_b128 16 lanes):
+//  * key rows (bytes [0, 64 KB)): one 256-byte row per index byte r, the 8-byte key
+//    entry (two 4-bit key codes of r: low nibble first element) replicated 32 times;
+//    lane L reads replica L % 32;
+//  * value rows (bytes [64 KB, 128 KB)), unless keys and values share a 4-bit
+//    codebook (then the key rows serve both): 2-bit values: r holds the codes of one
+//    element in the four tokens of a lane's operand and the 16-byte entry is that
+//    whole operand, replicated 16 times (lane L reads replica L % 16); 3/4-bit
+//    values: r holds the codes of one element in two tokens, an 8-byte entry
+//    replicated 32 times.
+// A look-up address is one v_perm of the index byte and the lane's replica offset
+// (and, for value rows, the 64 KB base held in a byte of the same lane word).
 //
 // Token order inside a 16-token tile is the identity: score row r = 4 qq + j is
-// token r, which is the token pair (4qq + j, j = 0..3) lane group qq needs for its
-// probability operand, so no cross-lane exchange is needed between the products.
+// token r, which is the token the lane group qq needs for its weight operand, so no
+// cross-lane exchange is needed between the products.
 //
-// Work layout: grid (n_split, Hkv, B), 4 waves per workgroup; the workgroup owns
-// tokens [split*chunk, min(len, (split+1)*chunk)) and wave w takes 32-token super
-// tiles w, w+4, ... with the next super tile's codes loaded while the current one
-// is processed.  Waves merge in LDS and each workgroup writes one partial
-// (m, l, o') per head to the workspace; a second kernel merges the splits by
-// log-sum-exp, divides by l and applies R^T = D H / sqrt(128).  Scores are in
-// base 2.
+// Work layout: grid (n_split, Hkv, B), 8 waves per workgroup (one workgroup per
+// compute unit: the table takes 128 KB of LDS); the workgroup owns tokens
+// [split*chunk, min(len, (split+1)*chunk)) and wave w takes 32-token super tiles
+// w, w+8, ... with the codes of the next three super tiles (one for 3-bit values) in
+// flight while one is processed.  Within a super tile all key look-ups go out before
+// the score products, and all value look-ups (they need only the codes) before the
+// softmax, so the LDS latency is paid once per phase rather than at every MFMA.
+// Waves merge in LDS and each workgroup stores one partial (m, l, o') per head to the
+// workspace; a second kernel, one workgroup per (sequence, KV head), merges the splits
+// by log-sum-exp, divides by l, applies R^T = D H / sqrt(128) and writes the output.
+// (Merging in the split kernel instead, by the last workgroup of a sequence to arrive
+// on a counter, measured slower: the device-scope stores, the counter and the loads
+// each cost a full memory round trip inside the kernel.)
 //
 // MFMA 16x16x32 f16 operand layout (wave64): A[i][k]: lane i%16 + 16*(k/8), slot
 // k%8; B[k][j]: lane j + 16*(k/8), slot k%8; D[i][j]: lane j + 16*(i/4), slot i%4.
 
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 #include "fa_tq_internal.h"
 
@@ -71,26 +86,25 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-constexpr int kWaves = 4;
+#ifndef FATQ_ATTN_WANT_WG
+#define FATQ_ATTN_WANT_WG 256
+#endif
+
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kST = 32;          // tokens per super tile (2 MFMA tiles)
-constexpr int kMaxG = 8;         // query heads per KV head on this path
-constexpr int kRow = 256;        // table bytes per index byte
-constexpr int kMaxSplit = 1024;
+constexpr int kST = 32;           // tokens per super tile (2 MFMA tiles)
+constexpr int kMaxG = 8;          // query heads per KV head on this path
+constexpr int kRow = 256;         // table bytes per index byte
+constexpr int kVBase = 65536;     // byte offset of the value rows
+constexpr int kMaxSplit = 1024;   // splits per (sequence, KV head)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kCScale = 64.0f;  // centroid pre-scale (exact)
-constexpr float kWMax = 32768.0f;  // bound of the value weights w = p n_V vs
+constexpr float kTau = 8.0f;      // a score may pass the reference by this (log2) before a rescale
+constexpr float kVMax = 128.0f;   // bound of n_V * vs: weights p n_V vs <= 2^8 * 2^7 = 2^15
 // Raw buffer resources: an access at or beyond the range returns zeros, so loads
 // past the sequence need no clamp and lanes without work use offset kOOB.
 constexpr int32_t kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOOB = 0x80000000u;   // every range is below 2^31 (host check)
-
-#ifndef FATQ_ATTN_WANT_WG
-#define FATQ_ATTN_WANT_WG 512
-#endif
-#ifndef FATQ_ATTN_MIN_CHUNK
-#define FATQ_ATTN_MIN_CHUNK 512
-#endif
 
 template <int B>
 constexpr int cbytes() { return B == 2 ? 32 : B == 3 ? 48 : 64; }
@@ -109,6 +123,7 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 x, _Float16 y) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// x = hi + lo, hi the nearest fp16, lo the nearest fp16 of the exact fp32 remainder.
 __device__ __forceinline__ void split_h(float x, _Float16& hi, _Float16& lo) {
   hi = static_cast<_Float16>(x);
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
@@ -126,18 +141,24 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Maximum over each row of 16 lanes (every lane of the row gets it).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                CTRL, 0xF, 0xF, false));
 }
+
+// Maximum over each row of 16 lanes (every lane of the row gets it).
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1, 0, 3, 2]
   x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2, 3, 0, 1]
   x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
   x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
   return x;
+}
+
+__device__ __forceinline__ float max8(const float (&x)[2][4]) {
+  return fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+               fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
 }
 
 // Spread 8 two-bit fields (bits 2i..2i+1) to nibbles (bits 4i..4i+1).
@@ -156,19 +177,29 @@ __device__ __forceinline__ uint32_t spread1(uint32_t x) {
   return x;
 }
 
-// Raw code words of one super tile as loaded (widened to 4-bit fields at use).
+// Raw code words of one super tile as loaded.  Every load is a plain 32- or 128-bit
+// word and nothing is computed from it here: the words are only read when the super
+// tile is processed, so the compiler's wait for them comes there, not at the load.
 //  k[t4]: the key codes of elements 32 qq .. 32 qq + 31 of token 16 t4 + n;
-//  v[t4][j]: the value codes of elements 8 n .. 8 n + 7 of token 16 t4 + 4 qq + j;
-//  nrm: lanes < 32 the key norm, lanes >= 32 the value norm of token lane % 32.
+//  v[t4][j]: value codes of token 16 t4 + 4 qq + j holding elements 8 n .. 8 n + 7:
+//    2-bit: the 32-bit word with the lane's 16 bits in half n & 1; 3-bit: that word of
+//    the low-bit plane, then the word of the high-bit plane with the lane's 8 bits in
+//    byte n & 3; 4-bit: the lane's own 32 bits;
+//  nk / nv: the 32-bit word holding, in half (t + sh) & 1, the key norm (lanes < 32;
+//    nk) or the value norm (lanes >= 32; nv) of token t = s0 + lane % 32 (norm rows are
+//    read in aligned words from the row start rounded down to 4 bytes; sh = 1 when
+//    the row starts 2 bytes past a word).
 template <int KB, int VB>
 struct Codes {
   uint32_t k[2][KB == 4 ? 4 : 3];
   uint32_t v[2][4][VB == 3 ? 2 : 1];
-  uint32_t nrm;
+  uint32_t nk, nv;
 };
 
 struct Rows {
   Rsrc kc, vc, kn, vn;
+  int ksh, vsh;   // norm rows: tokens of the half-word offset of their start
+  int nsh;        // this lane's (ksh for lanes < 32, vsh for lanes >= 32)
 };
 
 template <int KB, int VB>
@@ -204,20 +235,22 @@ __device__ __forceinline__ void issue_loads(const Rows& r, Codes<KB, VB>& c, int
         const uint32_t o = live ? tv * VCB + 4 * n : kOOB;
         c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o + d, 0, 0);
       } else {
-        const uint32_t o = live ? tv * VCB + 2 * n : kOOB;
-        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b16(r.vc, o + d, 0, 0);
+        const uint32_t o = live ? tv * VCB + 4 * (n >> 1) : kOOB;
+        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o + d, 0, 0);
         if constexpr (VB == 3) {
-          const uint32_t oh = live ? tv * VCB + 32 + n : kOOB;
-          c.v[t4][j][1] = __builtin_amdgcn_raw_buffer_load_b8(r.vc, oh + d, 0, 0);
+          const uint32_t oh = live ? tv * VCB + 32 + 4 * (n >> 2) : kOOB;
+          c.v[t4][j][1] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, oh + d, 0, 0);
         }
       }
     }
   }
-  const uint32_t on = static_cast<uint32_t>(s0 + (lane & 31)) * 2;
-  const uint32_t ok = live && lane < 32 ? on : kOOB;
-  const uint32_t ov = live && lane >= 32 ? on : kOOB;
-  c.nrm = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r.kn, ok, 0, 0)) |
-          static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r.vn, ov, 0, 0));
+  // (two loads with uniform resources, each lane using one: lanes < 32 the key norm
+  // word, lanes >= 32 the value norm word)
+  const uint32_t ok = live && lane < 32 ? static_cast<uint32_t>(s0 + lane + r.ksh) / 2 * 4 : kOOB;
+  const uint32_t ov =
+      live && lane >= 32 ? static_cast<uint32_t>(s0 + lane - 32 + r.vsh) / 2 * 4 : kOOB;
+  c.nk = __builtin_amdgcn_raw_buffer_load_b32(r.kn, ok, 0, 0);
+  c.nv = __builtin_amdgcn_raw_buffer_load_b32(r.vn, ov, 0, 0);
 }
 
 // The key words of one tile as four words of table index bytes (byte i of the 16:
@@ -250,22 +283,27 @@ __device__ __forceinline__ void key_fields(const uint32_t (&w)[KB == 4 ? 4 : 3],
   }
 }
 
-// Value word of elements 8 n .. 8 n + 7 as 4-bit fields (3/4-bit values).
+// Value word of elements 8 n .. 8 n + 7 as 4-bit fields (3/4-bit values; n = lane % 16).
 template <int VB>
-__device__ __forceinline__ uint32_t value_fields(const uint32_t (&w)[VB == 3 ? 2 : 1]) {
+__device__ __forceinline__ uint32_t value_fields(const uint32_t (&w)[VB == 3 ? 2 : 1], int n) {
   if constexpr (VB == 4) return w[0];
-  else return spread2(w[0] & 0xFFFFu) | (spread1(w[1] & 0xFFu) << 2);
+  else
+    return spread2(__builtin_amdgcn_ubfe(w[0], 16 * (n & 1), 16)) |
+           (spread1(__builtin_amdgcn_ubfe(w[1], 8 * (n & 3), 8)) << 2);
 }
 
-// Four 16-bit words of 2-bit value codes (tokens a, b, c, d; field i = element
+// Four 16-bit groups of 2-bit value codes (tokens a, b, c, d; field i = element
 // 8n + i) -> index bytes: byte k of e = element 2k, of o = element 2k + 1, each
 // (code of a) | (b) << 2 | (c) << 4 | (d) << 6.
+// The words hold the lane's 16 bits in the half that `sel` picks: 0x05010400 (low
+// halves) or 0x07030602 (high halves).
 __device__ __forceinline__ void quad_index2(uint32_t wa, uint32_t wb, uint32_t wc, uint32_t wd,
-                                            uint32_t& e, uint32_t& o) {
-  auto pair = [](uint32_t x, uint32_t y) {
-    // bytes [x.b0, y.b0, x.b1, y.b1], then nibble k = (x nibble k) | (y nibble k) << 4,
-    // then fields reordered within each byte to (x_2k, y_2k, x_2k+1, y_2k+1)
-    uint32_t z = __builtin_amdgcn_perm(y, x, 0x05010400u);
+                                            uint32_t sel, uint32_t& e, uint32_t& o) {
+  auto pair = [sel](uint32_t x, uint32_t y) {
+    // bytes [x.b0, y.b0, x.b1, y.b1] of the lane's halves, then nibble k = (x nibble k)
+    // | (y nibble k) << 4, then fields reordered within each byte to (x_2k, y_2k,
+    // x_2k+1, y_2k+1)
+    uint32_t z = __builtin_amdgcn_perm(y, x, sel);
     uint32_t t = ((z >> 4) ^ z) & 0x00F000F0u;
     z ^= t ^ (t << 4);
     t = ((z >> 2) ^ z) & 0x0C0C0C0Cu;
@@ -276,27 +314,38 @@ __device__ __forceinline__ void quad_index2(uint32_t wa, uint32_t wb, uint32_t w
   o = ((ab >> 4) & 0x0F0F0F0Fu) | (cd & 0xF0F0F0F0u);
 }
 
-// Table address of index byte k of word z: (byte << 8) | byte `rsel` of lane word R.
-template <int K, int RSEL>
-__device__ __forceinline__ uint32_t taddr(uint32_t z, uint32_t R) {
-  return __builtin_amdgcn_perm(z, R, 0x0C0C0000u | ((4u + K) << 8) | RSEL);
+// Key-row address of index byte K of word z: (byte << 8) | lane's key replica offset
+// (byte 0 of the lane word R).
+template <int K>
+__device__ __forceinline__ uint32_t kaddr(uint32_t z, uint32_t R) {
+  return __builtin_amdgcn_perm(z, R, 0x0C0C0000u | ((4u + K) << 8));
+}
+// Value-row address: kVBase (byte 2 of R) | (byte << 8) | value replica offset (byte 1).
+template <int K>
+__device__ __forceinline__ uint32_t vaddr(uint32_t z, uint32_t R) {
+  return __builtin_amdgcn_perm(z, R, 0x0C020001u | ((4u + K) << 8));
 }
 
-template <int D>
-__device__ __forceinline__ float row_down(float x, int d) {
-  if constexpr (D > 0)
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), 0x100 + D, 0xF, 0xF, false));
-  else
-    return __shfl_down(x, d, 16);
+// Workspace: the split partials, o' rows [B][Hq][n_split][QK] then (m, l) pairs
+// [B][Hq][n_split][2]; for one (sequence, KV head) the pairs j = h * n_split + split of
+// its G heads are contiguous in both.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store4(Rsrc r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
-template <int D>
-__device__ __forceinline__ uint32_t row_up(uint32_t x, int d) {
-  if constexpr (D > 0)
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-        0, static_cast<int>(x), 0x110 + D, 0xF, 0xF, false));
-  else
-    return __shfl_up(x, d, 16);
+__device__ __forceinline__ void store2(Rsrc r, uint32_t off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+struct Partials {
+  Rsrc o, ml;
+};
+__device__ __forceinline__ Partials unit_partials(const AttnLaunch& a, int b, int g, int G) {
+  const int ns = a.n_split, np = G * ns;
+  const int64_t rbase = (static_cast<int64_t>(b) * a.hq + g * G) * ns;
+  float* const ws_o = static_cast<float*>(a.workspace);
+  float* const ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * ns * QK;
+  return {make_rsrc(ws_o + rbase * QK, np * QK * 4), make_rsrc(ws_ml + 2 * rbase, np * 8)};
 }
 
 // Sign of element e of the first 128-block (SignWords quad layout), of s1 and of the
@@ -333,69 +382,96 @@ __device__ __forceinline__ void rotate_out(float2 o, const SignWords& sw, int la
       make_float2(sign_bit(sw, 2 * lane) ? -r0 : r0, sign_bit(sw, 2 * lane + 1) ? -r1 : r1);
 }
 
-// VSH: key and value codebooks are identical, so the key entries serve both.
+// Buffer resources of one (sequence, KV head) row covering tokens [0, ntok): codes, and
+// norm rows read as aligned words (the start rounded down to 4 bytes, 1 token earlier
+// when it is 2 bytes past a word, and the range rounded up to whole words; a word
+// never crosses a page, so the last one is always readable).
+template <int KB, int VB>
+__device__ __forceinline__ Rows make_rows(const AttnLaunch& a, int64_t kvb, int ntok, int lane) {
+  const uint32_t u = static_cast<uint32_t>(ntok);
+  Rows r;
+  r.kc = make_rsrc(a.k_codes + kvb * cbytes<KB>(), u * cbytes<KB>());
+  r.vc = make_rsrc(a.v_codes + kvb * cbytes<VB>(), u * cbytes<VB>());
+  const uintptr_t ka = reinterpret_cast<uintptr_t>(a.k_norms + kvb);
+  const uintptr_t va = reinterpret_cast<uintptr_t>(a.v_norms + kvb);
+  const int ksh = static_cast<int>((ka >> 1) & 1), vsh = static_cast<int>((va >> 1) & 1);
+  r.kn = make_rsrc(reinterpret_cast<const void*>(ka & ~uintptr_t{3}), (u + ksh + 1) / 2 * 4);
+  r.vn = make_rsrc(reinterpret_cast<const void*>(va & ~uintptr_t{3}), (u + vsh + 1) / 2 * 4);
+  r.ksh = ksh;
+  r.vsh = vsh;
+  r.nsh = lane < 32 ? ksh : vsh;
+  return r;
+}
+
+// VSH: key and value codebooks are identical 4-bit tables, so the key rows serve both.
 // GT: the group size G as a compile-time constant (1, 2, 4, 8), or 0 (runtime).
 template <int KB, int VB, bool VSH, int GT>
-__global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KTable tk,
+__global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KTable tk,
                                                                 KTable tv, SignWords sw) {
   constexpr bool V2 = VB == 2;
-  __shared__ __attribute__((aligned(16))) uint8_t tab[256 * kRow];   // 64 KB
-  __shared__ __attribute__((aligned(16))) uint16_t qhl[17][QK];      // hi, lo, zero rows
-  __shared__ __attribute__((aligned(16))) float nrm[kWaves][3][kST];
+  // super tiles of codes in flight beyond the one processed (3-bit values: their larger
+  // register sets leave room for one)
+  constexpr int kDepth = VB == 3 ? 1 : 3;
+  // the rows, and afterwards the waves' partial outputs for the merge in LDS
+  constexpr int kMergeBytes = sizeof(float) * kWaves * 2 * kMaxG * QK;
+  constexpr int kTab = (VSH ? kVBase : 2 * kVBase) > kMergeBytes ? (VSH ? kVBase : 2 * kVBase)
+                                                                  : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t tab[kTab];
+  __shared__ __attribute__((aligned(16))) uint16_t qhl[2 * kMaxG + 1][QK];   // hi, lo, zero rows
+  __shared__ __attribute__((aligned(16))) float nrm[kWaves][2][kST];
   __shared__ uint32_t sp[2][16];
   __shared__ float qmx[kMaxG];
   __shared__ float comb_ml[kWaves][kMaxG][2];
-  static_assert(sizeof(tab) >= sizeof(float) * kWaves * 2 * kMaxG * QK, "merge buffer");
   static_assert(!(VSH && V2), "2-bit values have their own entries");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qq = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = GT > 0 ? GT : a.hq / a.hkv;
-  constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
+  // lanes of column h < G carry hi(q'_h) and row h of the weights (hi), lanes of
+  // column 15 - h the lo halves; the other columns are zero (scores) or unused rows
+  const bool hi_lane = n < G;
+  const bool use = hi_lane || n >= 16 - G;
 
-  // ---- loads that need only the kernel arguments go out first (query elements, sign
-  // words and centroids, all indexed per lane), so that waiting for them later
-  // leaves the code loads in flight: wave w rotates heads w and w + 4; lane holds
-  // elements lane and lane + 64 of each
-  // (raw bits here; widened after the loads are waited for)
-  uint32_t qraw[2][2];
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const int h = wave + kWaves * hs;
-    const int hc = h < G ? h : 0;
+  // ---- loads that need only the kernel arguments go out first: wave w < G rotates
+  // head w, lane holding elements lane and lane + 64 (raw bits, widened later)
+  uint32_t qraw[2];
+  {
+    const int hc = wave < G ? wave : 0;
     const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + hc) * QK;
     if (a.q_is_bf16) {
       const uint16_t* qb = static_cast<const uint16_t*>(a.q) + qo;
-      qraw[hs][0] = qb[lane];
-      qraw[hs][1] = qb[lane + 64];
+      qraw[0] = qb[lane];
+      qraw[1] = qb[lane + 64];
     } else {
       const uint32_t* qf = static_cast<const uint32_t*>(a.q) + qo;
-      qraw[hs][0] = qf[lane];
-      qraw[hs][1] = qf[lane + 64];
+      qraw[0] = qf[lane];
+      qraw[1] = qf[lane + 64];
     }
   }
   // sign words of elements lane and lane + 64 (the same word; see sign_bit)
   const uint32_t sw1 = sw.w[0][(lane >> 3) & 3], sw2 = sw.w2[0][(lane >> 3) & 3];
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the sequence range, then the first super tile's loads (in flight during setup)
-  const int64_t len64 = static_cast<int64_t>(a.lens[b]) + a.len_add;
-  const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
+  // ---- the first super tiles' loads go out at once, bounded by the split's chunk
+  // (tokens past the sequence are masked when processed), so they need not wait for
+  // the sequence length, which arrives while the table is built
+  const int len_raw = a.lens[b];
   const int c0 = split * a.chunk;
-  const int c1 = min(len, c0 + a.chunk);
+  const int ce = min(a.t_max, c0 + a.chunk);
   const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g) * a.t_max;
-  const uint32_t ulen = static_cast<uint32_t>(len);
-  Rows rows;
-  rows.kc = make_rsrc(a.k_codes + kvb * KCB, ulen * KCB);
-  rows.vc = make_rsrc(a.v_codes + kvb * VCB, ulen * VCB);
-  rows.kn = make_rsrc(a.k_norms + kvb, ulen * 2);
-  rows.vn = make_rsrc(a.v_norms + kvb, ulen * 2);
+  Rows rows = make_rows<KB, VB>(a, kvb, ce > 0 ? ce : 0, lane);
   int st = c0 + wave * kST;
-  Codes<KB, VB> buf0, buf1;
-  issue_loads<KB, VB>(rows, buf0, st, st < c1, lane);
+  constexpr int kStep = kWaves * kST;
+  // ring of kDepth + 1 register sets: the codes of the next kDepth super tiles are
+  // in flight while one is processed
+  Codes<KB, VB> buf[kDepth + 1];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i)
+    issue_loads<KB, VB>(rows, buf[i], st + i * kStep, st + i * kStep < ce, lane);
 
-  // ---- centroid splits, then the operand table (thread r fills row r)
+  // ---- centroid splits, then the operand rows (thread r < 256 fills key row r,
+  // thread 256 + r value row r)
   {
     // centroid tid % 16 of the key (tid < 16) or value codebook, selected from the
     // uniform kernel arguments (straight-line selects: no per-lane argument loads)
@@ -410,65 +486,78 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     if (tid < 32) sp[tid >> 4][tid & 15] = pack_h2(hi, lo);
   }
   lds_barrier();
-  if (tid < 256) {
-    const int r = tid;
-    uint8_t* row = tab + r * kRow;
-    // key row r: the codes of its two elements (3-bit rows: see key_fields)
-    const uint32_t a0 = sp[0][KB == 3 ? (r & 3) | ((r >> 2) & 4) : r & 15];
-    const uint32_t a1 = sp[0][KB == 3 ? ((r >> 2) & 3) | ((r >> 3) & 4) : r >> 4];
-    const uint32_t kh = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // hi(c_lo4), hi(c_hi4)
-    const uint32_t kl = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // lo(c_lo4), lo(c_hi4)
-    const uint4 ke = make_uint4(kh, kl, kh, kl);
-    // all 8 slots of a row hold the same value; rotating the slot a step writes by
-    // the row index spreads the lanes of one store over all banks
-#pragma unroll
-    for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row)[(k + r) & 7] = ke;
-    if constexpr (V2) {
+  {
+    const int r = tid & 255;
+    uint4 e;
+    if (tid < 256) {
+      // key row r: the codes of its two elements (3-bit rows: see key_fields)
+      const uint32_t a0 = sp[0][KB == 3 ? (r & 3) | ((r >> 2) & 4) : r & 15];
+      const uint32_t a1 = sp[0][KB == 3 ? ((r >> 2) & 3) | ((r >> 3) & 4) : r >> 4];
+      const uint32_t kh = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // hi(c_lo4), hi(c_hi4)
+      const uint32_t kl = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // lo(c_lo4), lo(c_hi4)
+      e = make_uint4(kh, kl, kh, kl);
+    } else if constexpr (V2) {
       const uint32_t va = sp[1][r & 3], vb = sp[1][(r >> 2) & 3];
       const uint32_t vc = sp[1][(r >> 4) & 3], vd = sp[1][r >> 6];
-      const uint4 ve = make_uint4(__builtin_amdgcn_perm(vb, va, 0x05040100u),
-                                  __builtin_amdgcn_perm(vb, va, 0x07060302u),
-                                  __builtin_amdgcn_perm(vd, vc, 0x05040100u),
-                                  __builtin_amdgcn_perm(vd, vc, 0x07060302u));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row + 128)[(k + r) & 7] = ve;
-    } else if constexpr (!VSH) {
+      e = make_uint4(__builtin_amdgcn_perm(vb, va, 0x05040100u),
+                     __builtin_amdgcn_perm(vb, va, 0x07060302u),
+                     __builtin_amdgcn_perm(vd, vc, 0x05040100u),
+                     __builtin_amdgcn_perm(vd, vc, 0x07060302u));
+    } else {
       const uint32_t v0 = sp[1][r & 15], v1 = sp[1][r >> 4];
       const uint32_t vh = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
       const uint32_t vl = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
-      const uint4 ve = make_uint4(vh, vl, vh, vl);
+      e = make_uint4(vh, vl, vh, vl);
+    }
+    if (tid < 256 || (!VSH && tid < 512)) {
+      uint8_t* row = tab + (tid < 256 ? 0 : kVBase) + r * kRow;
+      // every 16-byte slot of a row holds the same entry; rotating the slot a step
+      // per row index spreads the 16 lanes of one store cycle over all banks
 #pragma unroll
-      for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(row + 128)[(k + r) & 7] = ve;
+      for (int k = 0; k < 16; ++k) reinterpret_cast<uint4*>(row)[(k + r) & 15] = e;
     }
   }
 
-  // ---- q' = s2 * H (s * q): stride 64 in-lane, strides 32 .. 1 across lanes; the
-  // largest |q'| of each head to LDS
-  float qx[2][2];
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      qx[hs][i] = __uint_as_float(a.q_is_bf16 ? qraw[hs][i] << 16 : qraw[hs][i]);
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    float x0 = bit_of(sw1, lane) ? -qx[hs][0] : qx[hs][0];
-    float x1 = bit_of(sw1, lane + 64) ? -qx[hs][1] : qx[hs][1];
+  // ---- q' = s2 * H (s * q) of head `wave`: stride 64 in-lane, strides 32 .. 1 across
+  // lanes; its largest |q'| to LDS
+  float qx0 = __uint_as_float(a.q_is_bf16 ? qraw[0] << 16 : qraw[0]);
+  float qx1 = __uint_as_float(a.q_is_bf16 ? qraw[1] << 16 : qraw[1]);
+  {
+    const float x0 = bit_of(sw1, lane) ? -qx0 : qx0;
+    const float x1 = bit_of(sw1, lane + 64) ? -qx1 : qx1;
     float u = x0 + x1, v = x0 - x1;
-#pragma unroll
-    for (int L = 32; L >= 1; L >>= 1) {
-      const float pu = __shfl_xor(u, L, 64), pv = __shfl_xor(v, L, 64);
+    // butterflies of strides 32 .. 1 across lanes (the partner lane's value by a swap
+    // across the wave halves, an LDS swizzle across rows, DPP within a row)
+    auto stage = [&](auto xor_of, int L) {
+      const float pu = xor_of(u), pv = xor_of(v);
       const bool up = (lane & L) != 0;
       u = up ? pu - u : u + pu;
       v = up ? pv - v : v + pv;
-    }
-    qx[hs][0] = sw.two && bit_of(sw2, lane) ? -u : u;
-    qx[hs][1] = sw.two && bit_of(sw2, lane + 64) ? -v : v;
-    float mx = fmaxf(fabsf(u), fabsf(v));
-#pragma unroll
-    for (int s2 = 32; s2 >= 1; s2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s2, 64));
-    const int h = wave + kWaves * hs;
-    if (lane == 0 && h < G) qmx[h] = mx;
+    };
+    stage([](float x) { return __shfl_xor(x, 32, 64); }, 32);
+    stage([](float x) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                                   0x401F));   // xor 16
+    }, 16);
+    stage([](float x) { return dpp_f<0x128>(x); }, 8);   // row_ror:8 = xor 8 in a row
+    stage([lane](float x) {
+      const float r = dpp_f<0x114>(x), l = dpp_f<0x104>(x);   // row_shr:4, row_shl:4
+      return (lane & 4) ? r : l;
+    }, 4);
+    stage([](float x) { return dpp_f<0x4E>(x); }, 2);    // quad_perm [2, 3, 0, 1]
+    stage([](float x) { return dpp_f<0xB1>(x); }, 1);    // quad_perm [1, 0, 3, 2]
+    qx0 = sw.two && bit_of(sw2, lane) ? -u : u;
+    qx1 = sw.two && bit_of(sw2, lane + 64) ? -v : v;
+    const float rm = row_max16(fmaxf(fabsf(u), fabsf(v)));
+    const float mx = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 0)),
+                                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 16))),
+                           fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 32)),
+                                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 48))));
+    if (lane == 0 && wave < G) qmx[wave] = mx;
   }
   lds_barrier();   // tables and per-head maxima complete
   float qmax = 0.0f;
@@ -480,28 +569,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   const float qscale = qmax > 0.0f ? ldexpf(1.0f, max(qex - 14, -110)) : 1.0f;
   {
     const float inv = kInvSqrtQK / qscale;
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const int h = wave + kWaves * hs;
-      if (h < G) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          _Float16 hi, lo;
-          split_h(qx[hs][i] * inv, hi, lo);
-          qhl[h][lane + 64 * i] = __builtin_bit_cast(uint16_t, hi);
-          qhl[kMaxG + h][lane + 64 * i] = __builtin_bit_cast(uint16_t, lo);
-        }
-      }
+    if (wave < G) {
+      _Float16 hi, lo;
+      split_h(qx0 * inv, hi, lo);
+      qhl[wave][lane] = __builtin_bit_cast(uint16_t, hi);
+      qhl[kMaxG + wave][lane] = __builtin_bit_cast(uint16_t, lo);
+      split_h(qx1 * inv, hi, lo);
+      qhl[wave][lane + 64] = __builtin_bit_cast(uint16_t, hi);
+      qhl[kMaxG + wave][lane + 64] = __builtin_bit_cast(uint16_t, lo);
     }
     if (tid < 64) reinterpret_cast<uint32_t*>(&qhl[2 * kMaxG][0])[tid] = 0u;
   }
   lds_barrier();   // q' halves complete
 
   // ---- B operands of the score product: k-step m covers elements 32qq + 4m .. +3;
-  // column n < G: hi(q'_n), G <= n < 2G: lo(q'_{n-G}), else zero
+  // column h < G: hi(q'_h), column 15 - h: lo(q'_h), else zero
   h8 bq[8];
   {
-    const int qrow = n < G ? n : (n < 2 * G ? kMaxG + n - G : 2 * kMaxG);
+    const int qrow = hi_lane ? n : (use ? kMaxG + 15 - n : 2 * kMaxG);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const uint2 d = *reinterpret_cast<const uint2*>(&qhl[qrow][32 * qq + 4 * m]);
@@ -509,11 +594,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     }
   }
   const float sc2 = a.scale * kLog2e * qscale / kCScale;
-  // byte 0: key replica offset, byte 1: value replica offset (+128) of this lane
-  const uint32_t R = ((lane & 15) << 3) |
-                     ((VSH ? ((lane & 15) << 3) : V2 ? 128 + ((lane & 7) << 4) : 128 + ((lane & 15) << 3)) << 8);
+  // ---- the sequence range; later loads are bounded by the sequence length
+  const int64_t len64 = static_cast<int64_t>(len_raw) + a.len_add;
+  const int len = len64 < 0 ? 0 : (len64 > a.t_max ? a.t_max : static_cast<int>(len64));
+  const int c1 = min(len, c0 + a.chunk);
+  rows = make_rows<KB, VB>(a, kvb, len, lane);
+  // byte 0: key replica offset, byte 1: value replica offset, byte 2: value-row base
+  const uint32_t R = ((lane & 31) << 3) | ((V2 ? (lane & 15) << 4 : (lane & 31) << 3) << 8) |
+                     (static_cast<uint32_t>(kVBase >> 16) << 16);
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  // byte selector of the lane's 16-bit half in the 2-bit value words
+  const uint32_t vsel = (n & 1) ? 0x07030602u : 0x05010400u;
+  float m_ref = -INFINITY, l_run = 0.0f;
+  bool started = false;   // a super tile has set the softmax reference (wave-uniform)
   // value weight scale of this wave's stream; above any value a norm needs, so the
   // first super tile with a nonzero value norm sets it
   float vs = 18446744073709551616.0f;   // 2^64
@@ -522,150 +615,217 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
   for (int m = 0; m < 8; ++m) o[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   auto process = [&](const Codes<KB, VB>& cur, int s0) {
-    // per-token factors through LDS: key scale (0 when masked), key bias (-inf when
-    // masked), value weight factor n_V * vs
+    // ---- per-token factors through LDS: key scale, value weight factor n_V * vs
     {
-      const int t = s0 + (lane & 31);
-      const float nf = __half2float(__ushort_as_half(static_cast<uint16_t>(cur.nrm)));
+      // (0 past the sequence: the first super tiles are loaded to the chunk's end)
+      const float nf = s0 + (lane & 31) < c1
+                           ? __half2float(__ushort_as_half(static_cast<uint16_t>(
+                                 __builtin_amdgcn_ubfe(lane < 32 ? cur.nk : cur.nv,
+                                                       16 * ((s0 + lane + rows.nsh) & 1), 16))))
+                           : 0.0f;
       // the largest value norm of the super tile (lanes 32..63; past the sequence the
-      // loads return 0) bounds every weight p n_V (p <= 1): lower vs, and rescale the
-      // accumulator by the same power of two, when it would push a weight past kWMax
-      const float rm = row_max16(nf);
-      const float vmax = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                   __builtin_bit_cast(int, rm), 32)),
-                               __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                   __builtin_bit_cast(int, rm), 48)));
-      if (vmax * vs > kWMax) {
+      // loads return 0) bounds every n_V: lower vs, and rescale the accumulator by the
+      // same power of two, when n_V * vs would pass kVMax
+      // (tested lane by lane; the wave-wide maximum only when some norm passes)
+      if (__ballot(lane >= 32 && nf * vs > kVMax)) {
+        const float rm = row_max16(lane >= 32 ? nf : 0.0f);
+        const float vmax = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 32)),
+                                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                     __builtin_bit_cast(int, rm), 48)));
         int e = 0;
         frexpf(vmax, &e);                       // vmax < 2^e
-        const float vs_new = ldexpf(kWMax, -e);  // vmax * vs_new < 2^15
+        const float vs_new = ldexpf(kVMax, -e);  // vmax * vs_new < kVMax
         const float r = vs_new / vs;            // a power of two
 #pragma unroll
         for (int m = 0; m < 8; ++m) o[m] *= r;
         vs = vs_new;
       }
-      if (lane < 32) {
-        nrm[wave][0][lane] = t < c1 ? nf * sc2 : 0.0f;
-        nrm[wave][1][lane] = t < c1 ? 0.0f : -INFINITY;
-      } else {
-        nrm[wave][2][lane - 32] = nf * vs;
-      }
+      nrm[wave][lane >> 5][lane & 31] = nf * (lane < 32 ? sc2 : vs);
     }
     __builtin_amdgcn_wave_barrier();
-    // ---- scores
-    float sc[2][4];
+    // ---- key look-ups of both tiles, then the score products: sum = the head's full
+    // score before the key factor (hi + lo columns)
+    uint2 ke[2][16];
 #pragma unroll
     for (int t4 = 0; t4 < 2; ++t4) {
       uint32_t f[4];
       key_fields<KB>(cur.k[t4], f);
-      f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      f4 acc1 = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const uint32_t w = f[m >> 1];
         uint32_t a0, a1;
         if (m & 1) {
-          a0 = taddr<2, 0>(w, R);
-          a1 = taddr<3, 0>(w, R);
+          a0 = kaddr<2>(w, R);
+          a1 = kaddr<3>(w, R);
         } else {
-          a0 = taddr<0, 0>(w, R);
-          a1 = taddr<1, 0>(w, R);
+          a0 = kaddr<0>(w, R);
+          a1 = kaddr<1>(w, R);
         }
-        const uint2 e0 = *reinterpret_cast<const uint2*>(tab + a0);
-        const uint2 e1 = *reinterpret_cast<const uint2*>(tab + a1);
-        // two accumulators halve the chain of dependent products
-        if (m & 1) acc1 = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc1);
-        else acc = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc);
-      }
-      acc += acc1;
-      const float4 fk = *reinterpret_cast<const float4*>(&nrm[wave][0][16 * t4 + 4 * qq]);
-      const float4 zb = *reinterpret_cast<const float4*>(&nrm[wave][1][16 * t4 + 4 * qq]);
-      sc[t4][0] = fmaf(acc[0] + row_down<GT>(acc[0], G), fk.x, zb.x);
-      sc[t4][1] = fmaf(acc[1] + row_down<GT>(acc[1], G), fk.y, zb.y);
-      sc[t4][2] = fmaf(acc[2] + row_down<GT>(acc[2], G), fk.z, zb.z);
-      sc[t4][3] = fmaf(acc[3] + row_down<GT>(acc[3], G), fk.w, zb.w);
-    }
-    // ---- online softmax (lanes n < G carry head n; other columns are ignored)
-    float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(m_run, mloc);
-    float p[2][4];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int t4 = 0; t4 < 2; ++t4)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[t4][j] = __builtin_amdgcn_exp2f(sc[t4][j] - mnew);
-        lsum += p[t4][j];
-      }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (__ballot(mnew > m_run && n < G)) {   // rescale only when a running maximum grew
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float ar = __shfl(alpha, (4 * qq + j) % G, 64);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) o[m][j] *= ar;
+        ke[t4][2 * m] = *reinterpret_cast<const uint2*>(tab + a0);
+        ke[t4][2 * m + 1] = *reinterpret_cast<const uint2*>(tab + a1);
       }
     }
-    l_run += lsum;
-    m_run = mnew;
-    // ---- value product: A = [p_a, p_b, p_a, p_b, p_c, p_d, p_c, p_d] for tokens
-    // 4qq..4qq+3; rows < G hi(p'), rows G..2G-1 lo(p') (moved up by G lanes)
+    __builtin_amdgcn_sched_barrier(0);
+    float sum[2][4];
+    float4 fk[2];
 #pragma unroll
     for (int t4 = 0; t4 < 2; ++t4) {
-      const float4 fv = *reinterpret_cast<const float4*>(&nrm[wave][2][16 * t4 + 4 * qq]);
-      const float pa = p[t4][0] * fv.x, pb = p[t4][1] * fv.y;
-      const float pc = p[t4][2] * fv.z, pd = p[t4][3] * fv.w;
-      // hi = nearest fp16, lo = nearest fp16 of the exact fp32 remainder
-      _Float16 ha, la, hb, lb, hc, lc, hd, ld;
-      split_h(pa, ha, la);
-      split_h(pb, hb, lb);
-      split_h(pc, hc, lc);
-      split_h(pd, hd, ld);
-      const h2 hab = {ha, hb}, hcd = {hc, hd}, lab2 = {la, lb}, lcd2 = {lc, ld};
-      const uint32_t lab = row_up<GT>(__builtin_bit_cast(uint32_t, lab2), G);
-      const uint32_t lcd = row_up<GT>(__builtin_bit_cast(uint32_t, lcd2), G);
-      const uint32_t pab = n < G ? __builtin_bit_cast(uint32_t, hab) : (n < 2 * G ? lab : 0u);
-      const uint32_t pcd = n < G ? __builtin_bit_cast(uint32_t, hcd) : (n < 2 * G ? lcd : 0u);
-      const h8 ap = h8_of(pab, pab, pcd, pcd);
+      f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const uint2 e0 = ke[t4][2 * m], e1 = ke[t4][2 * m + 1];
+        acc = mfma32(h8_of(e0.x, e0.y, e1.x, e1.y), bq[m], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[t4][j] = acc[j] + dpp_f<0x140>(acc[j]);   // row_mirror
+      fk[t4] = *reinterpret_cast<const float4*>(&nrm[wave][0][16 * t4 + 4 * qq]);
+    }
+    // ---- value look-ups of both tiles (B operands; they need only the codes), in
+    // flight during the softmax
+    using VEnt = typename std::conditional<V2, uint4, uint2>::type;
+    VEnt ve[2][V2 ? 8 : 16];
+#pragma unroll
+    for (int t4 = 0; t4 < 2; ++t4) {
       if constexpr (V2) {
         uint32_t ze, zo;
-        quad_index2(cur.v[t4][0][0], cur.v[t4][1][0], cur.v[t4][2][0], cur.v[t4][3][0], ze, zo);
+        quad_index2(cur.v[t4][0][0], cur.v[t4][1][0], cur.v[t4][2][0], cur.v[t4][3][0], vsel,
+                    ze, zo);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const uint32_t z = (m & 1) ? zo : ze;
           uint32_t ad;
-          if ((m >> 1) == 0) ad = taddr<0, 1>(z, R);
-          else if ((m >> 1) == 1) ad = taddr<1, 1>(z, R);
-          else if ((m >> 1) == 2) ad = taddr<2, 1>(z, R);
-          else ad = taddr<3, 1>(z, R);
-          const uint4 ev = *reinterpret_cast<const uint4*>(tab + ad);
-          o[m] = mfma32(ap, h8_of(ev.x, ev.y, ev.z, ev.w), o[m]);
+          if ((m >> 1) == 0) ad = vaddr<0>(z, R);
+          else if ((m >> 1) == 1) ad = vaddr<1>(z, R);
+          else if ((m >> 1) == 2) ad = vaddr<2>(z, R);
+          else ad = vaddr<3>(z, R);
+          ve[t4][m] = *reinterpret_cast<const VEnt*>(tab + ad);
         }
       } else {
-        const uint32_t wa = value_fields<VB>(cur.v[t4][0]), wb = value_fields<VB>(cur.v[t4][1]);
-        const uint32_t wc = value_fields<VB>(cur.v[t4][2]), wd = value_fields<VB>(cur.v[t4][3]);
+        const uint32_t wa4 = value_fields<VB>(cur.v[t4][0], n);
+        const uint32_t wb4 = value_fields<VB>(cur.v[t4][1], n);
+        const uint32_t wc4 = value_fields<VB>(cur.v[t4][2], n);
+        const uint32_t wd4 = value_fields<VB>(cur.v[t4][3], n);
         // byte k of ze: element 2k (tokens a | b << 4); zo: element 2k + 1
-        const uint32_t ze0 = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
-        const uint32_t zo0 = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
-        const uint32_t ze1 = (wc & 0x0F0F0F0Fu) | ((wd << 4) & 0xF0F0F0F0u);
-        const uint32_t zo1 = ((wc >> 4) & 0x0F0F0F0Fu) | (wd & 0xF0F0F0F0u);
-        constexpr int RS = VSH ? 0 : 1;
+        const uint32_t ze0 = (wa4 & 0x0F0F0F0Fu) | ((wb4 << 4) & 0xF0F0F0F0u);
+        const uint32_t zo0 = ((wa4 >> 4) & 0x0F0F0F0Fu) | (wb4 & 0xF0F0F0F0u);
+        const uint32_t ze1 = (wc4 & 0x0F0F0F0Fu) | ((wd4 << 4) & 0xF0F0F0F0u);
+        const uint32_t zo1 = ((wc4 >> 4) & 0x0F0F0F0Fu) | (wd4 & 0xF0F0F0F0u);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const uint32_t z0 = (m & 1) ? zo0 : ze0, z1 = (m & 1) ? zo1 : ze1;
           uint32_t i0, i1;
-          if ((m >> 1) == 0) { i0 = taddr<0, RS>(z0, R); i1 = taddr<0, RS>(z1, R); }
-          else if ((m >> 1) == 1) { i0 = taddr<1, RS>(z0, R); i1 = taddr<1, RS>(z1, R); }
-          else if ((m >> 1) == 2) { i0 = taddr<2, RS>(z0, R); i1 = taddr<2, RS>(z1, R); }
-          else { i0 = taddr<3, RS>(z0, R); i1 = taddr<3, RS>(z1, R); }
-          const uint2 eab = *reinterpret_cast<const uint2*>(tab + i0);
-          const uint2 ecd = *reinterpret_cast<const uint2*>(tab + i1);
+          if constexpr (VSH) {
+            if ((m >> 1) == 0) { i0 = kaddr<0>(z0, R); i1 = kaddr<0>(z1, R); }
+            else if ((m >> 1) == 1) { i0 = kaddr<1>(z0, R); i1 = kaddr<1>(z1, R); }
+            else if ((m >> 1) == 2) { i0 = kaddr<2>(z0, R); i1 = kaddr<2>(z1, R); }
+            else { i0 = kaddr<3>(z0, R); i1 = kaddr<3>(z1, R); }
+          } else {
+            if ((m >> 1) == 0) { i0 = vaddr<0>(z0, R); i1 = vaddr<0>(z1, R); }
+            else if ((m >> 1) == 1) { i0 = vaddr<1>(z0, R); i1 = vaddr<1>(z1, R); }
+            else if ((m >> 1) == 2) { i0 = vaddr<2>(z0, R); i1 = vaddr<2>(z1, R); }
+            else { i0 = vaddr<3>(z0, R); i1 = vaddr<3>(z1, R); }
+          }
+          ve[t4][2 * m] = *reinterpret_cast<const VEnt*>(tab + i0);
+          ve[t4][2 * m + 1] = *reinterpret_cast<const VEnt*>(tab + i1);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- exponents against the reference: x = s - m_ref (masked tokens -inf)
+    float x[2][4];
+    const float nm = -m_ref;
+#pragma unroll
+    for (int t4 = 0; t4 < 2; ++t4) {
+      x[t4][0] = fmaf(sum[t4][0], fk[t4].x, nm);
+      x[t4][1] = fmaf(sum[t4][1], fk[t4].y, nm);
+      x[t4][2] = fmaf(sum[t4][2], fk[t4].z, nm);
+      x[t4][3] = fmaf(sum[t4][3], fk[t4].w, nm);
+    }
+    const bool partial = s0 + kST > c1;   // uniform: only a stream's last super tile
+    if (partial) {
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[t4][j] = s0 + 16 * t4 + 4 * qq + j < c1 ? x[t4][j] : -INFINITY;
+    }
+    // a score above m_ref + kTau (or the first tile, m_ref = -inf: x = +inf) moves the
+    // reference to the super tile's true maximum
+    // (the test compares the bit patterns as integers: for a positive bound that is the
+    // float order, -inf and every negative value fall below it, +inf and NaN above)
+    int xm = __builtin_bit_cast(int, x[0][0]);
+#pragma unroll
+    for (int t4 = 0; t4 < 2; ++t4)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xm = max(xm, __builtin_bit_cast(int, x[t4][j]));
+    if (__ballot(use && xm > __builtin_bit_cast(int, kTau))) {
+      float sc[2][4];
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4) {
+        sc[t4][0] = sum[t4][0] * fk[t4].x;
+        sc[t4][1] = sum[t4][1] * fk[t4].y;
+        sc[t4][2] = sum[t4][2] * fk[t4].z;
+        sc[t4][3] = sum[t4][3] * fk[t4].w;
+        if (partial) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sc[t4][j] = s0 + 16 * t4 + 4 * qq + j < c1 ? sc[t4][j] : -INFINITY;
+        }
+      }
+      float mt = max8(sc);
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_ref, mt);
+      if (started) {   // nothing to rescale before the first super tile
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= alpha;
+        // accumulator row 4 qq + j belongs to head r (r < G) or 15 - r (r >= 16 - G)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * qq + j;
+          const float ar = __shfl(alpha, r < G ? r : 15 - r, 64);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) o[m][j] *= ar;
+        }
+      }
+      started = true;
+      m_ref = m_new;
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[t4][j] = sc[t4][j] - m_ref;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int t4 = 0; t4 < 2; ++t4)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[t4][j] = __builtin_amdgcn_exp2f(x[t4][j]);
+        l_run += p[t4][j];
+      }
+    // ---- value product: A = [w_a, w_b, w_a, w_b, w_c, w_d, w_c, w_d] for tokens
+    // 4qq..4qq+3, the hi halves in the rows of lanes h < G, the lo halves in rows 15 - h
+#pragma unroll
+    for (int t4 = 0; t4 < 2; ++t4) {
+      const float4 fv = *reinterpret_cast<const float4*>(&nrm[wave][1][16 * t4 + 4 * qq]);
+      const float wa = p[t4][0] * fv.x, wb = p[t4][1] * fv.y;
+      const float wc = p[t4][2] * fv.z, wd = p[t4][3] * fv.w;
+      _Float16 ha, la, hb, lb, hc, lc, hd, ld;
+      split_h(wa, ha, la);
+      split_h(wb, hb, lb);
+      split_h(wc, hc, lc);
+      split_h(wd, hd, ld);
+      const uint32_t pab = hi_lane ? pack_h2(ha, hb) : pack_h2(la, lb);
+      const uint32_t pcd = hi_lane ? pack_h2(hc, hd) : pack_h2(lc, ld);
+      const h8 ap = h8_of(pab, pab, pcd, pcd);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if constexpr (V2) {
+          const uint4 ev = ve[t4][m];
+          o[m] = mfma32(ap, h8_of(ev.x, ev.y, ev.z, ev.w), o[m]);
+        } else {
+          const uint2 eab = ve[t4][2 * m], ecd = ve[t4][2 * m + 1];
           o[m] = mfma32(ap, h8_of(eab.x, eab.y, ecd.x, ecd.y), o[m]);
         }
       }
@@ -673,19 +833,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
     __builtin_amdgcn_wave_barrier();
   };
 
-  constexpr int kStep = kWaves * kST;
-  // ---- main loop: two register sets, the next super tile loading while one is used
-  while (st < c1) {
-    issue_loads<KB, VB>(rows, buf1, st + kStep, st + kStep < c1, lane);
-    process(buf0, st);
-    st += kStep;
-    if (st >= c1) break;
-    issue_loads<KB, VB>(rows, buf0, st + kStep, st + kStep < c1, lane);
-    process(buf1, st);
-    st += kStep;
+  // ---- main loop over the ring, kDepth + 1 super tiles per pass: the loads of set
+  // i + kDepth go out before set i is processed, every step issuing its loads (past
+  // the stream they return zeros without touching memory) so that the compiler's
+  // count of loads in flight is the same on every path; only the processing of a
+  // super tile past the stream is skipped (a uniform branch)
+  const int n_tiles = st < c1 ? (c1 - st + kStep - 1) / kStep : 0;
+  for (int it = 0; it < n_tiles; it += kDepth + 1) {
+#pragma unroll
+    for (int i = 0; i <= kDepth; ++i) {
+      // (past the sequence the length-bounded ranges return zeros: no test needed)
+      issue_loads<KB, VB>(rows, buf[(i + kDepth) % (kDepth + 1)], st + kDepth * kStep, true,
+                          lane);
+      if (st < c1) process(buf[i], st);
+      st += kStep;
+    }
   }
 
-  // ---- merge the four waves in LDS (the table is no longer needed) and write this
+  // ---- merge the waves in LDS (the table is no longer needed) and write this
   // split's partial (m, l, o') per head
   __syncthreads();
   float* comb_o = reinterpret_cast<float*>(tab);
@@ -693,21 +858,23 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * qq + j;
-    if (r < 2 * G) {
+    const int slot = r < G ? r : (r >= 16 - G ? kMaxG + 15 - r : -1);
+    if (slot >= 0) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        comb_o[(wave * 2 * kMaxG + r) * QK + 8 * n + m] = o[m][j] * ovs;
+        comb_o[(wave * 2 * kMaxG + slot) * QK + 8 * n + m] = o[m][j] * ovs;
     }
   }
-  if (qq == 0 && n < G) {
-    comb_ml[wave][n][0] = m_run;
-    comb_ml[wave][n][1] = l_run;
+  // the head's l: the lanes of its column in the four row groups
+  float lsum = l_run + __shfl_xor(l_run, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qq == 0 && hi_lane) {
+    comb_ml[wave][n][0] = m_ref;
+    comb_ml[wave][n][1] = lsum;
   }
   __syncthreads();
   const int ns = a.n_split;
-  float* ws_o = static_cast<float*>(a.workspace);
-  float* ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * ns * QK;
-  const int64_t rbase = (static_cast<int64_t>(b) * a.hq + g * G) * ns;
+  const Partials pt = unit_partials(a, b, g, G);
   for (int idx = tid; idx < G * (QK / 4); idx += kThreads) {
     const int h = idx >> 5, e4 = idx & 31;
     float M = -INFINITY;
@@ -721,7 +888,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
         const float m_w = comb_ml[w][h][0];
         const float f = m_w > -INFINITY ? __builtin_amdgcn_exp2f(m_w - M) : 0.0f;
         const float4 hi4 = reinterpret_cast<const float4*>(comb_o + (w * 2 * kMaxG + h) * QK)[e4];
-        const float4 lo4 = reinterpret_cast<const float4*>(comb_o + (w * 2 * kMaxG + G + h) * QK)[e4];
+        const float4 lo4 =
+            reinterpret_cast<const float4*>(comb_o + (w * 2 * kMaxG + kMaxG + h) * QK)[e4];
         os.x += f * (hi4.x + lo4.x);
         os.y += f * (hi4.y + lo4.y);
         os.z += f * (hi4.z + lo4.z);
@@ -729,9 +897,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_kernel(AttnLaunch a, KT
         ls += f * comb_ml[w][h][1];
       }
     }
-    const int64_t r = rbase + static_cast<int64_t>(h) * ns + split;
-    reinterpret_cast<float4*>(ws_o + r * QK)[e4] = os;
-    if (e4 == 0) reinterpret_cast<float2*>(ws_ml)[r] = make_float2(M, ls);
+    const int j = h * ns + split;
+    store4(pt.o, (j * QK + 4 * e4) * 4, os);
+    if (e4 == 0) store2(pt.ml, j * 8, make_float2(M, ls));
   }
 }
 
@@ -816,25 +984,27 @@ __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, Si
 
 bool attn_mfma_supported(int32_t hq, int32_t hkv) { return hq / hkv <= kMaxG; }
 
+// Splits per (sequence, KV head) so that the grid holds about FATQ_ATTN_WANT_WG
+// workgroups (one per compute unit), each chunk a multiple of a round of super tiles
+// (kWaves * kST tokens) so every wave of a full chunk gets the same work.
 void attn_mfma_partition(int32_t batch, int32_t hkv, int32_t t_max, int32_t* n_split,
                          int32_t* chunk) {
+  constexpr int64_t kRound = kWaves * kST;
   const int64_t units = static_cast<int64_t>(batch > 0 ? batch : 1) * hkv;
-  const int64_t want = FATQ_ATTN_WANT_WG;   // workgroups in flight
+  const int64_t want = FATQ_ATTN_WANT_WG;
   int64_t ns = (want + units - 1) / units;
-  const int64_t min_chunk = FATQ_ATTN_MIN_CHUNK;   // tokens per split at least
-  const int64_t max_ns = t_max > 0 ? (t_max + min_chunk - 1) / min_chunk : 1;
+  const int64_t max_ns = t_max > 0 ? (t_max + kRound - 1) / kRound : 1;
   if (ns > max_ns) ns = max_ns;
   if (ns > kMaxSplit) ns = kMaxSplit;
   if (ns < 1) ns = 1;
-  int64_t c = t_max > 0 ? (t_max + ns - 1) / ns : kST;
-  c = (c + kST - 1) / kST * kST;
+  int64_t c = t_max > 0 ? (t_max + ns - 1) / ns : kRound;
+  c = (c + kRound - 1) / kRound * kRound;
   ns = t_max > 0 ? (t_max + c - 1) / c : 1;
   *n_split = static_cast<int32_t>(ns);
   *chunk = static_cast<int32_t>(c);
 }
 
 size_t attn_mfma_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t n_split) {
-  (void)hkv;
   return static_cast<size_t>(batch) * hq * n_split * (QK + 2) * sizeof(float);
 }
 
@@ -846,7 +1016,7 @@ void launch_g(const AttnLaunch& a, const KTable& tk, const KTable& tv, const Sig
   hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT>), g1, b1, 0, stream, a, tk, tv, sw)
 #define FATQ_ATS(K) \
   hipLaunchKernelGGL((attn_mfma_kernel<K, K, true, GT>), g1, b1, 0, stream, a, tk, tv, sw)
-  // shared key/value entries for 4-bit tables (3-bit key rows have their own layout)
+  // shared key/value rows for identical 4-bit tables (3-bit key rows have their own layout)
   if (same && tk.bits == 4) {
     FATQ_ATS(4);
     return;

@@ -8,10 +8,10 @@ Llama-3-8B-shaped layer: 1 x 32768 tokens, 32 query / 8 KV heads, head_dim 128.
 Prints one JSON line.  ``value`` = algorithmic bytes of a step / step time (GB/s).
 Algorithmic bytes: encode = input bytes + packed code bytes + 2-byte norm per
 128-block; attention = per (sequence, token, KV head) the K and V code bytes and
-the two norms, plus the query and output.  Inputs rotate over 4 copies (a step
-streams 160 MB of encode traffic, so a copy comes back after 480 MB) and packed
-caches over 32 copies (840 MB, which the attention phase cycles through), so no call
-finds its data in the 256 MB last-level cache.
+the two norms, plus the query and output.  Inputs rotate over 12 copies (an encode
+streams about 84 MB, so a copy comes back only after 11 other encodes of its phase,
+over 900 MB of traffic) and packed caches over 32 copies (the attention phase cycles
+through 840 MB), so no call finds its data in the 256 MB last-level cache.
 
 The K timed steps run in rounds of R steps, phase by phase within a round: R encodes
 of the K cache back to back, then R encodes of the V cache, then R attentions, step
@@ -28,7 +28,18 @@ Other modes:
   --calibrate-copy        before the steps, copy a 256 MiB buffer 5 times (the
                           plain copy whose counters calibrate FETCH_SIZE/WRITE_SIZE);
   --summarize-rocprof DIR print per-kernel means of a rocprofv3 CSV directory
-                          (kernel_stats or counter_collection) and exit.
+                          (kernel_stats or counter_collection) and exit;
+  --cpu-baseline-only     the bounded CPU-oracle baseline of the step alone (no GPU;
+                          the GPU run starts it as a child process);
+  --cpu-baseline-full     the CPU oracle on every workload at full size (prefill: a
+                          stated subset), one worker and N worker processes (no GPU).
+
+Each kernel's per-call distribution (median, p10, p90) comes from a separate pass of
+60 calls, each between its own pair of HIP events; the step figures above are means
+over back-to-back calls.  ``attn_decode_graph`` times the attention as a HIP graph of
+32 calls over the cache copies (GPU time per call without host launch gaps), and
+``attn_decode_vector_alu`` the same calls on the vector-ALU attention kernels
+(FA_TQ_ATTN_VECTOR_ALU) for comparison with the matrix-core ones.
 
 After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv restoring
 the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
@@ -65,7 +76,8 @@ ROUND = 10   # timed steps per round (see the module docstring)
 CSRC = os.path.join(ROOT, "kv_cache_vector_fa_amd", "csrc")
 # kernel name prefix (as rocprofv3 reports it) -> source file that defines it
 KERNEL_SOURCE = {"encode_kernel": "codec.hip", "attn_mfma_kernel": "attn_mfma.hip",
-                 "attn_merge_splits_kernel": "attn_mfma.hip"}
+                 "attn_merge_splits_kernel": "attn_mfma.hip", "attn_split_kernel": "attn.hip",
+                 "attn_merge_kernel": "attn.hip", "decode_kv_kernel": "codec.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama_layer_pmc_traffic.txt")
 CALIB_BYTES = 256 << 20
 
@@ -76,12 +88,16 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama_layer")
-    p.add_argument("--copies", type=int, default=4, help="input copies rotated per step")
+    p.add_argument("--copies", type=int, default=12, help="input copies rotated per step")
     p.add_argument("--cache-copies", type=int, default=32, help="packed-cache copies rotated")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-append", action="store_true", help="skip the append_decode figure")
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--summarize-rocprof", metavar="DIR")
+    p.add_argument("--cpu-baseline-only", action="store_true")
+    p.add_argument("--cpu-baseline-full", action="store_true")
+    p.add_argument("--workers", type=int, default=0,
+                   help="CPU-oracle worker processes (default: os.cpu_count(), at most 16)")
     return p.parse_args()
 
 
@@ -154,6 +170,64 @@ def traffic_for(kernel: str):
     if kernel not in vals or src is None or hashes.get(src) != source_hash(src):
         return None
     return vals[kernel]
+
+
+def per_call_distribution(calls, n=60) -> dict:
+    """Median, p10 and p90 (us) of n single calls, each between its own pair of HIP
+    events on the current stream (calls rotate over the given list)."""
+    import torch
+    for c in calls[:4]:
+        c()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        calls[i % len(calls)]()
+        e1.record()
+    torch.cuda.synchronize()
+    us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"median_us": round(float(p50), 3), "p10_us": round(float(p10), 3),
+            "p90_us": round(float(p90), 3), "calls": n}
+
+
+def attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out, ws, nbytes, flags=0,
+                    n_calls=32, replays=10) -> dict:
+    """GPU time per attention call from replays of a HIP graph of n_calls calls over
+    the cache copies (no host launch gaps), with the given variant flags."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls = [fa.attn_decode_call(cbk, cbv, seed, q, *c, lens, scale, out, ws, flags=flags)
+                 for c in caches]
+        for i in range(n_calls):
+            calls[i % len(calls)]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls = [fa.attn_decode_call(cbk, cbv, seed, q, *c, lens, scale, out, ws, flags=flags)
+                 for c in caches]
+        for i in range(n_calls):
+            calls[i % len(calls)]()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    us = float(np.median(per))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    p10, p90 = np.percentile(per, [10, 90])
+    return {"us": round(us, 3), "p10_us": round(float(p10), 3), "p90_us": round(float(p90), 3),
+            "gbps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": f"median over {replays} replays of a HIP graph of {n_calls} calls"}
 
 
 def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -> dict:
@@ -286,9 +360,18 @@ def prefill_whole(fa, seed, reps=10) -> dict:
         nvec = B * H * T
         nbytes = nvec * (2 * d + codes.shape[-2] * fa.code_bytes(cb.bits) + 2 * nnorm)
         gbs = nbytes / (us * 1e-6) / 1e9
+        # round trip on the GPU over the first sequence (8 heads x 16384 vectors):
+        # mean ||x - x^||^2 / ||x||^2 per vector, x^ restored by fa_tq_decode_kv in fp32
+        xr = fa.decode_kv(cb, seed, codes[:1].contiguous(), norms[:1].contiguous(),
+                          out_dtype=torch.float32, flags=flags, head_dim=d)
+        x0 = x[:1].float()
+        rel = ((x0 - xr) ** 2).sum(-1) / (x0 ** 2).sum(-1).clamp_min(1e-30)
         out[mode] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
                      "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
-                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "roundtrip_rel_mse": float(rel.mean().item()),
+                     "roundtrip_vectors": int(rel.numel())}
+        del xr, x0, rel
         del codes, norms, x
     del k
     return out
@@ -313,6 +396,23 @@ def other_attention(fa, seed, reps=20) -> dict:
         cbk, cbv = fa.codebook_init(128, w.k_bits), fa.codebook_init(128, w.v_bits)
         kc, kn = fa.encode(cbk, seed, k)
         vc, vn = fa.encode(cbv, seed, v)
+        enc = {}
+        for tag, cb, x, c, n_ in (("encode_k", cbk, k, kc, kn), ("encode_v", cbv, v, vc, vn)):
+            call = fa.encode_call(cb, seed, x, c, n_)
+            call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            eus = e0.elapsed_time(e1) * 1e3 / 3
+            nblk = B * Hkv * T
+            eb = enc_bytes(nblk, 256, cb.bits)
+            enc[tag] = {"us": round(eus, 1), "vectors_per_s": round(nblk / (eus * 1e-6), 1),
+                        "algorithmic_bytes": int(eb), "gbps": round(eb / eus / 1e3, 1),
+                        "frac_hbm_peak": round(eb / eus / 1e3 / HBM_PEAK_GBS, 4)}
         del k, v
         nbytes = attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits)
         copies = max(1, -(-768_000_000 // nbytes))
@@ -335,66 +435,249 @@ def other_attention(fa, seed, reps=20) -> dict:
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 1), "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "cache_copies": copies,
-                     "shape": f"{B}x{Hkv}x{T} K{w.k_bits}/V{w.v_bits}, {Hq} query heads"}
+                     "shape": f"{B}x{Hkv}x{T} K{w.k_bits}/V{w.v_bits}, {Hq} query heads",
+                     "per_call": per_call_distribution(calls, 30),
+                     "graph": attention_graph(fa, cbk, cbv, seed, q, caches, lens,
+                                              1 / np.sqrt(d), o, ws, nbytes,
+                                              n_calls=max(8, len(caches)), replays=5),
+                     **enc}
         del caches, kc, kn, vc, vn, ws, o
     return out
 
 
-def cpu_baseline(w, seed: int, n_slices: int | None = None, min_seconds: float = 10.0) -> dict:
-    """The oracle as it stands, on ``n_slices`` (batch, KV head) slices of the workload
-    (default: all of them): encode their K and V blocks in canonical fp32 and run fp64
-    attention for their query heads; repeated until ``min_seconds`` have passed."""
-    n_slices = n_slices or w.n_kv_heads
+# ---------------------------------------------------------------- CPU-oracle baseline
+# Work units are independent (sequence, KV head) slices (prefill: (layer, KV head));
+# the N-worker runs fork processes that share the parent's input arrays.  Nothing here
+# touches the GPU: the GPU run starts this leg as a child process.
+_UNITS: dict = {}
+
+
+def _cpu_info(workers: int) -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name')} {dep.get('version')}"
+    except Exception:   # noqa: BLE001 - numpy builds differ in what they report
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "workers": workers,
+            "numpy": np.__version__, "blas": blas}
+
+
+def _default_workers() -> int:
+    # one GPU's share of the host: at most 16 processes
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _unit_attention(u: int):
+    """Oracle work of unit u of the workload in _UNITS: encode its K and V vectors
+    (canonical fp32), pack them, fp64 attention for its query heads."""
     from threadpoolctl import threadpool_limits
 
-    import workloads
     from oracle import attention as o_att
-    from oracle import codebook as o_cb
     from oracle import codec
-    from oracle import signs as o_signs
+    W = _UNITS
+    b, g = divmod(u, W["hkv"])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k32 = W["k"][b, g][None, None]
+        v32 = W["v"][b, g][None, None]
+        kc, kn, _ = codec.encode_mse(k32, W["s"], W["bk"])
+        vc, vn, _ = codec.encode_mse(v32, W["s"], W["bv"])
+        kp, vp = codec.pack(kc, W["kb"]), codec.pack(vc, W["vb"])
+        t1 = time.perf_counter()
+        q = W["q"][b, g * W["grp"]:(g + 1) * W["grp"]][None]
+        o_att.attend_fused(q, kp, kn, vp, vn, [int(W["lens"][b])], W["kb"], W["vb"], W["ck"],
+                           W["cv"], W["s"], 1 / np.sqrt(128))
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
 
-    T = w.tokens
-    k, v = workloads.make_kv(w, "cpu", batch=1)
-    q = workloads.make_q(w, "cpu", batch=1)
+
+def _unit_prefill(u: int):
+    """Oracle encode of unit u = (layer, KV head) of the prefill subset: K4 one d=256
+    rotation per vector, V2 in 128-blocks, and the 8-bit grid in 128-blocks."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import codec
+    W = _UNITS
+    li, g = divmod(u, W["hkv"])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k32, v32 = W["k"][li, g], W["v"][li, g]
+        codec.encode_mse_whole(k32, W["s256"], W["bk256"])
+        t1 = time.perf_counter()
+        vc, _, _ = codec.encode_mse(v32, W["s"], W["bv"])
+        codec.pack(vc, 2)
+        t2 = time.perf_counter()
+        codec.encode_u8(k32, W["s"])
+        t3 = time.perf_counter()
+    return t1 - t0, t2 - t1, t3 - t2
+
+
+def _run_units(fn, n_units: int, workers: int):
+    """Wall time of fn over all units: one process (workers == 1) or a fork pool."""
+    t0 = time.perf_counter()
+    if workers == 1:
+        parts = [fn(u) for u in range(n_units)]
+    else:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(workers) as pool:
+            parts = pool.map(fn, range(n_units), chunksize=1)
+    return time.perf_counter() - t0, np.sum(np.array(parts), axis=0)
+
+
+def _load_attention_units(w, seed: int, n_slices: int | None = None):
     import torch
-    k32 = k[:, :n_slices].to(torch.float32).numpy()
-    v32 = v[:, :n_slices].to(torch.float32).numpy()
-    grp = w.n_q_heads // w.n_kv_heads
-    q32 = q[:, :grp * n_slices].to(torch.float32).numpy()
-    s = o_signs.signs(seed, 128)
+
+    import workloads
+    from oracle import codebook as o_cb
+    from oracle import signs as o_signs
+    if w.name == "tiny":
+        k, v, q = workloads.tiny_inputs()
+        k, v, q = k[None, None], v[None, None], q[None, None].astype(np.float64)
+        lens = np.array([k.shape[2]])
+    else:
+        kt, vt = workloads.make_kv(w, "cpu")
+        k = kt.to(torch.float32).numpy()
+        v = vt.to(torch.float32).numpy()
+        del kt, vt
+        q = workloads.make_q(w, "cpu").to(torch.float32).numpy().astype(np.float64)
+        lens = workloads.make_seq_lens(w)
     bk, ck = o_cb.codebook(w.k_bits)
     bv, cv = o_cb.codebook(w.v_bits)
-    reps, t_enc, t_att = 0, 0.0, 0.0
-    with threadpool_limits(limits=1):
-        while reps == 0 or (t_enc + t_att < min_seconds and reps < 50):
-            t0 = time.perf_counter()
-            kc, kn, _ = codec.encode_mse(k32, s, bk)
-            vc, vn, _ = codec.encode_mse(v32, s, bv)
-            kp, vp = codec.pack(kc, w.k_bits), codec.pack(vc, w.v_bits)
-            t1 = time.perf_counter()
-            o_att.attend_fused(q32, kp, kn, vp, vn, [T], w.k_bits, w.v_bits, ck, cv, s,
-                               1 / np.sqrt(128))
-            t2 = time.perf_counter()
-            t_enc += t1 - t0
-            t_att += t2 - t1
-            reps += 1
-    nbytes = (enc_bytes(n_slices * T, 256, w.k_bits) + enc_bytes(n_slices * T, 256, w.v_bits)
-              + attn_bytes([T], n_slices, grp * n_slices, w.k_bits, w.v_bits))
-    per = (t_enc + t_att) / reps
-    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_slices} of the {w.n_kv_heads} KV heads of the workload: encode "
-                      f"{n_slices * T} K and V blocks each (canonical fp32) + fp64 attention "
-                      f"for their {grp * n_slices} query heads; "
-                      f"mean of {reps} repetitions: encode {t_enc / reps:.2f} s, attention "
-                      f"{t_att / reps:.2f} s; numpy, one thread",
-            "seconds": round(t_enc + t_att, 2)}
+    _UNITS.clear()
+    _UNITS.update(k=k, v=v, q=q, lens=lens, s=o_signs.signs(seed, 128), bk=bk, ck=ck, bv=bv,
+                  cv=cv, kb=w.k_bits, vb=w.v_bits, hkv=w.n_kv_heads,
+                  grp=w.n_q_heads // w.n_kv_heads)
+    n_units = k.shape[0] * k.shape[1]
+    return n_units if n_slices is None else min(n_slices, n_units)
+
+
+def _attention_record(w, n_units: int, workers: int, reps: int = 1) -> dict:
+    """Oracle throughput over the first n_units slices: encode K and V of each slice
+    and fp64 attention for its query heads; bytes as the GPU path counts them."""
+    lens = _UNITS["lens"]
+    hkv = _UNITS["hkv"]
+    T = _UNITS["k"].shape[2]
+    units_b = [u // hkv for u in range(n_units)]
+    tok = int(sum(T for _ in units_b))
+    att_tok = int(sum(int(lens[b]) for b in units_b))
+    enc_b = enc_bytes(tok, 256, w.k_bits) + enc_bytes(tok, 256, w.v_bits)
+    cbk, cbv = {2: 32, 3: 48, 4: 64}[w.k_bits], {2: 32, 3: 48, 4: 64}[w.v_bits]
+    att_b = att_tok * (cbk + cbv + 4) + n_units * _UNITS["grp"] * 128 * (2 + 4)
+    wall, parts = 0.0, np.zeros(2)
+    for _ in range(reps):
+        wl, pt = _run_units(_unit_attention, n_units, workers)
+        wall += wl
+        parts += pt
+    wall /= reps
+    parts /= reps
+    return {"value": round((enc_b + att_b) / wall / 1e9, 4), "unit": "GB/s",
+            "cores": min(workers, n_units),
+            "seconds": round(wall, 3),
+            "encode_vectors_per_cpu_s": round(2 * tok / float(parts[0]), 1),
+            "cpu_s_encode": round(float(parts[0]), 3), "cpu_s_attention": round(float(parts[1]), 3),
+            "units": n_units, "algorithmic_bytes": int(enc_b + att_b), "repetitions": reps}
+
+
+def cpu_baseline(seed: int, workers: int) -> dict:
+    """The oracle as it stands, on the step's workload (all 8 KV-head slices of the
+    Llama-shaped layer: encode K and V, fp64 attention): one worker, then N worker
+    processes over the slices."""
+    import workloads
+    w = workloads.WORKLOADS["llama_layer"]
+    n = _load_attention_units(w, seed)
+    one = _attention_record(w, n, 1, reps=3)
+    many = _attention_record(w, n, workers, reps=5)
+    rec = dict(many)
+    rec.update({"kind": "oracle",
+                "sample": f"the whole step workload ({n} (sequence, KV head) slices x "
+                          f"{w.tokens} tokens): encode K and V (canonical fp32) + fp64 "
+                          f"attention for {w.n_q_heads} query heads; numpy, "
+                          f"{min(workers, n)} worker processes, one slice each (mean of 5 "
+                          f"runs; single_worker: one process, mean of 3 runs)",
+                "single_worker": one})
+    rec.update(_cpu_info(workers))
+    return rec
+
+
+def cpu_baseline_full(seed: int, workers: int) -> dict:
+    """The oracle on every workload: configs tiny, llama_layer, batched and
+    long_context at full size, and the prefill encode on layers {0, 31}, all 8 KV
+    heads, tokens [0, 8192); each with one worker and with N worker processes."""
+    import torch
+
+    import workloads
+    from oracle import codebook as o_cb
+    from oracle import signs as o_signs
+    out = {"info": _cpu_info(workers)}
+    for name in ("tiny", "llama_layer", "batched", "long_context"):
+        w = workloads.WORKLOADS[name]
+        t0 = time.perf_counter()
+        n = _load_attention_units(w, seed)
+        gen = time.perf_counter() - t0
+        out[name] = {"1_worker": _attention_record(w, n, 1),
+                     f"{workers}_workers": _attention_record(w, n, workers),
+                     "input_generation_s": round(gen, 1)}
+        print(f"# cpu oracle {name}: {out[name]}", file=sys.stderr, flush=True)
+    w = workloads.WORKLOADS["prefill"]
+    T = 8192
+    kt, vt = workloads.make_kv(w, "cpu", tokens=T)
+    k = kt[[0, w.batch - 1]].to(torch.float32).numpy()
+    v = vt[[0, w.batch - 1]].to(torch.float32).numpy()
+    del kt, vt
+    bk256, _ = o_cb.codebook(4, 256)
+    bv, _ = o_cb.codebook(2)
+    _UNITS.clear()
+    _UNITS.update(k=k, v=v, s=o_signs.signs(seed, 128), s256=o_signs.signs(seed, 256),
+                  bk256=bk256, bv=bv, hkv=w.n_kv_heads)
+    n = 2 * w.n_kv_heads
+    nvec = n * T
+    rec = {}
+    for nw in (1, workers):
+        wall, parts = _run_units(_unit_prefill, n, nw)
+        rec[f"{nw}_worker" + ("s" if nw > 1 else "")] = {
+            "seconds": round(wall, 3), "cores": nw,
+            "vectors_per_s_all_three": round(3 * nvec / wall, 1),
+            "cpu_s": {"k4_whole_d256": round(float(parts[0]), 3),
+                      "v2_blocked": round(float(parts[1]), 3),
+                      "k8_blocked": round(float(parts[2]), 3)},
+            "vectors_per_s_k4_whole_d256_1core": round(nvec / float(parts[0]), 1)}
+    out["prefill_subset"] = {"subset": f"layers 0 and {w.batch - 1}, {w.n_kv_heads} KV heads, "
+                                       f"tokens [0, {T}), head_dim 256", **rec}
+    return out
+
+
+def _cpu_baseline_child(workers: int) -> dict:
+    """Run the bounded CPU baseline in a child process (the GPU process never forks)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+           "--workers", str(workers)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"CPU baseline failed ({r.returncode}): {r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
     args = parse()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    workers = args.workers or _default_workers()
+    if args.cpu_baseline_only or args.cpu_baseline_full:
+        import workloads
+        seed = workloads.ROTATION_SEED
+        res = cpu_baseline_full(seed, workers) if args.cpu_baseline_full else \
+            cpu_baseline(seed, workers)
+        print(json.dumps(res), flush=True)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark measures one GPU only; run with --gpus 1"}))
@@ -503,6 +786,11 @@ def main():
         "kernels": kern,
         "roofline": roof,
     }
+    rec["per_call"] = {n: per_call_distribution(c) for n, c in zip(names, calls)}
+    rec["attn_decode_graph"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out,
+                                               ws, nbytes[2])
+    rec["attn_decode_vector_alu"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale,
+                                                    out, ws, nbytes[2], flags=fa.ATTN_VECTOR_ALU)
     if not args.no_append:
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)
@@ -510,7 +798,7 @@ def main():
         rec["prefill_encode_d256"] = prefill_whole(fa, seed)
         rec["attention_other_workloads"] = other_attention(fa, seed)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, seed)
+        rec["cpu_baseline"] = _cpu_baseline_child(workers)
     print(json.dumps(rec), flush=True)
 
 

@@ -74,11 +74,17 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  *     blocked layout.  Arithmetic as the blocked mode over d' elements (squares
  *     summed over index bits 0, 1, ... in order, the padding adding zeros;
  *     butterflies in stage order 1 .. d'/2, c = fp32(1/sqrt(d'))).
+ *   FA_TQ_ATTN_VECTOR_ALU (fa_tq_attn_decode_ex and fa_tq_attn_decode_noalloc only):
+ *     run the vector-ALU attention kernels (the ones used when n_q_heads / n_kv_heads
+ *     is above 8) for any group size instead of the matrix-core kernels, e.g. to
+ *     compare the two; the result is the same computation ([Spec] "Optimization:
+ *     Fused dequant-dot") under the same accuracy bound.
  * Entry points without _ex use flags 0.
  */
 #define FA_TQ_TWO_SIGNS 1u
 #define FA_TQ_NORM_CORRECT 2u
 #define FA_TQ_WHOLE_VECTOR 4u
+#define FA_TQ_ATTN_VECTOR_ALU 8u
 
 /*
  * Scalar quantizer for one 128-element block ([Spec] "Step 2: Lloyd-Max Scalar
@@ -226,7 +232,8 @@ fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook 
                                float scale, float *out,
                                void *workspace, size_t workspace_bytes, void *stream);
 
-/* fa_tq_attn_decode with flags 0 or FA_TQ_TWO_SIGNS (the cache's rotation). */
+/* fa_tq_attn_decode with flags: FA_TQ_TWO_SIGNS (the cache's rotation) and/or
+ * FA_TQ_ATTN_VECTOR_ALU (the kernel family). */
 fa_tq_status fa_tq_attn_decode_ex(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
                                   uint64_t seed, uint32_t flags, int32_t head_dim,
                                   const void *q, fa_tq_dtype q_dtype,

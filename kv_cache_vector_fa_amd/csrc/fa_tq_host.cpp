@@ -414,7 +414,9 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   if (st != FA_TQ_OK) return st;
   if ((st = check_codebook(cb_v, who, false, &tv)) != FA_TQ_OK)
     return st;
-  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS, nullptr, who)) != FA_TQ_OK) return st;
+  if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_ATTN_VECTOR_ALU, nullptr, who)) !=
+      FA_TQ_OK)
+    return st;
   if ((st = check_head_dim(head_dim)) != FA_TQ_OK) return st;
   if (head_dim != fatq::QK)
     return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (the attention kernels take 128)", who,
@@ -465,7 +467,7 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   a.out = out;
   a.workspace = workspace;
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
-  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+  if (!(flags & FA_TQ_ATTN_VECTOR_ALU) && fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
     // the MFMA kernels address one (batch, KV head) row of codes with 32-bit offsets
     if (static_cast<int64_t>(t_max) * 64 >= (int64_t{1} << 31))
       return fail(FA_TQ_EUNSUPPORTED, "%s: t_max %d: a cache row spans 2 GiB or more", who,
@@ -524,13 +526,15 @@ size_t fa_tq_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0 || head_dim != fatq::QK ||
       n_q_heads % n_kv_heads != 0)
     return 0;
+  // enough for either kernel family (FA_TQ_ATTN_VECTOR_ALU selects the vector-ALU one)
   int32_t n_split = 1, chunk = 0;
+  fatq::attn_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
+  size_t need = fatq::attn_workspace_bytes(batch, n_q_heads, n_split);
   if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
     fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
-    return fatq::attn_mfma_workspace_bytes(batch, n_q_heads, n_kv_heads, n_split);
+    need = std::max(need, fatq::attn_mfma_workspace_bytes(batch, n_q_heads, n_kv_heads, n_split));
   }
-  fatq::attn_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
-  return fatq::attn_workspace_bytes(batch, n_q_heads, n_split);
+  return need;
 }
 
 fa_tq_status fa_tq_encode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,

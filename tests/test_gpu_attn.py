@@ -40,7 +40,7 @@ def _random_cache(B, H, T, bits, seed):
     return packed, norms
 
 
-def _run(fa, q, kp, kn, vp, vn, lens, kb, vb, scale, heads=None, where=""):
+def _run(fa, q, kp, kn, vp, vn, lens, kb, vb, scale, heads=None, where="", flags=0):
     torch = _torch()
     dev = "cuda"
     ck, cv = fa.codebook_init(128, kb), fa.codebook_init(128, vb)
@@ -48,7 +48,7 @@ def _run(fa, q, kp, kn, vp, vn, lens, kb, vb, scale, heads=None, where=""):
     out = fa.attn_decode(ck, cv, SEED, qt, torch.from_numpy(kp).to(dev),
                          torch.from_numpy(kn.view(np.int16)).to(dev),
                          torch.from_numpy(vp).to(dev), torch.from_numpy(vn.view(np.int16)).to(dev),
-                         torch.tensor(lens, dtype=torch.int32, device=dev), scale)
+                         torch.tensor(lens, dtype=torch.int32, device=dev), scale, flags=flags)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     q32 = bf16_to_f32(qt) if qt.dtype == torch.bfloat16 else qt.cpu().numpy()
@@ -90,6 +90,23 @@ def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
     kp, kn = _oracle_cache(k, kb)
     vp, vn = _oracle_cache(v, vb)
     _run(gpu_lib, q.cuda(), kp, kn, vp, vn, lens, kb, vb, 1 / np.sqrt(128), where="ragged")
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [(2, 32, 8, 1500, [1500, 901]), (1, 4, 4, 300, [257])])
+def test_attn_vector_alu_kernels(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
+    """FA_TQ_ATTN_VECTOR_ALU: the vector-ALU kernels at group sizes the matrix-core
+    kernels also take, against the same oracle."""
+    torch = _torch()
+    say(f"attn vector-ALU K{kb}V{vb} B={B} Hq={Hq} Hkv={Hkv} T={T} lens={lens}")
+    rng = np.random.default_rng(kb * 100 + vb + T)
+    k = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32)).to(torch.bfloat16)
+    kp, kn = _oracle_cache(k, kb)
+    vp, vn = _oracle_cache(v, vb)
+    _run(gpu_lib, q.cuda(), kp, kn, vp, vn, lens, kb, vb, 1 / np.sqrt(128), where="valu",
+         flags=gpu_lib.ATTN_VECTOR_ALU)
 
 
 def test_attn_fp32_query_and_scales(gpu_lib):

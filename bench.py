@@ -513,10 +513,10 @@ def _unit_prefill(u: int):
         k32, v32 = W["k"][li, g], W["v"][li, g]
         codec.encode_mse_whole(k32, W["s256"], W["bk256"])
         t1 = time.perf_counter()
-        vc, _, _ = codec.encode_mse(v32, W["s"], W["bv"])
+        vc, _, _ = codec.encode_mse(v32, W["s256"], W["bv"])
         codec.pack(vc, 2)
         t2 = time.perf_counter()
-        codec.encode_u8(k32, W["s"])
+        codec.encode_u8(k32, W["s256"])
         t3 = time.perf_counter()
     return t1 - t0, t2 - t1, t3 - t2
 
@@ -636,7 +636,7 @@ def cpu_baseline_full(seed: int, workers: int) -> dict:
     bk256, _ = o_cb.codebook(4, 256)
     bv, _ = o_cb.codebook(2)
     _UNITS.clear()
-    _UNITS.update(k=k, v=v, s=o_signs.signs(seed, 128), s256=o_signs.signs(seed, 256),
+    _UNITS.update(k=k, v=v, s256=o_signs.signs(seed, 256),
                   bk256=bk256, bv=bv, hkv=w.n_kv_heads)
     n = 2 * w.n_kv_heads
     nvec = n * T

@@ -834,17 +834,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   };
 
   // ---- main loop over the ring, kDepth + 1 super tiles per pass: the loads of set
-  // i + kDepth go out before set i is processed, every step issuing its loads (past
-  // the stream they return zeros without touching memory) so that the compiler's
-  // count of loads in flight is the same on every path; only the processing of a
-  // super tile past the stream is skipped (a uniform branch)
+  // i + kDepth go out before set i is processed, every step issuing its loads so that
+  // the compiler's count of loads in flight is the same on every path; a super tile
+  // past this split's stream is loaded at the out-of-range offset (zeros, no memory
+  // access: the tokens after the chunk are the next split's) and not processed (a
+  // uniform branch)
   const int n_tiles = st < c1 ? (c1 - st + kStep - 1) / kStep : 0;
   for (int it = 0; it < n_tiles; it += kDepth + 1) {
 #pragma unroll
     for (int i = 0; i <= kDepth; ++i) {
-      // (past the sequence the length-bounded ranges return zeros: no test needed)
-      issue_loads<KB, VB>(rows, buf[(i + kDepth) % (kDepth + 1)], st + kDepth * kStep, true,
-                          lane);
+      const int sn = st + kDepth * kStep;
+      issue_loads<KB, VB>(rows, buf[(i + kDepth) % (kDepth + 1)], sn, sn < c1, lane);
       if (st < c1) process(buf[i], st);
       st += kStep;
     }

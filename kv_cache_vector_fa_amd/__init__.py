@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa_tq.so")
+# FA_TQ_LIB names another build of the library (e.g. the AddressSanitizer host build)
+LIB_PATH = os.environ.get("FA_TQ_LIB") or os.path.join(_HERE, "libfa_tq.so")
 
 FA_TQ_OK, FA_TQ_EINVAL, FA_TQ_EUNSUPPORTED, FA_TQ_EHIP = 0, 1, 2, 3
 FA_TQ_F32, FA_TQ_BF16 = 0, 1

@@ -62,5 +62,46 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     return OUT
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libfa_tq_asan.so")
+# AddressSanitizer on the host code only (-Xarch_host before each sanitizer flag):
+# the device code is compiled as usual
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of hipcc's clang (to LD_PRELOAD into a
+    process that loads the ASan build)."""
+    out = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    return out
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The host library fa_tq_host.cpp (argument checks, codebooks, signs, dispatch)
+    compiled with AddressSanitizer and linked with the kernel objects of ``build``
+    into ``_build/asan/libfa_tq_asan.so``; runs without a GPU for the host-side tests.
+    Load it with the runtime from ``asan_runtime()`` preloaded."""
+    objs = [os.path.join(BUILD_DIR, src + ".o") for src, _ in SOURCES[1:]]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    host = os.path.join(ASAN_DIR, "fa_tq_host.o")
+    src, flags = SOURCES[0]
+    cmd = [hipcc()] + COMMON + flags + ASAN_HOST + ["-c", os.path.join(CSRC, src), "-o", host]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libasan"] + \
+        ASAN_HOST + ["-o", ASAN_LIB, host] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -433,21 +433,29 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   const bool hi_lane = n < G;
   const bool use = hi_lane || n >= 16 - G;
 
-  // ---- loads that need only the kernel arguments go out first: wave w < G rotates
-  // head w, lane holding elements lane and lane + 64 (raw bits, widened later)
+  // ---- loads that need only the kernel arguments go out first.  The code rows'
+  // resources are built before the query loads, so that every kernel argument
+  // arrives in one round of scalar loads.
+  const int len_raw = a.lens[b];
+  const int c0 = split * a.chunk;
+  const int ce = min(a.t_max, c0 + a.chunk);
+  const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g) * a.t_max;
+  Rows rows = make_rows<KB, VB>(a, kvb, ce > 0 ? ce : 0, lane);
+  // The query: wave w < G rotates head w, lane holding elements lane and lane + 64
+  // (raw bits, widened later); one load form for both dtypes (no branch on the dtype
+  // argument): a bf16 element is read as the aligned word holding it.
   uint32_t qraw[2];
   {
     const int hc = wave < G ? wave : 0;
     const int64_t qo = (static_cast<int64_t>(b) * a.hq + g * G + hc) * QK;
-    if (a.q_is_bf16) {
-      const uint16_t* qb = static_cast<const uint16_t*>(a.q) + qo;
-      qraw[0] = qb[lane];
-      qraw[1] = qb[lane + 64];
-    } else {
-      const uint32_t* qf = static_cast<const uint32_t*>(a.q) + qo;
-      qraw[0] = qf[lane];
-      qraw[1] = qf[lane + 64];
-    }
+    const uint32_t es = a.q_is_bf16 ? 2u : 4u;
+    const char* qp = static_cast<const char*>(a.q) + qo * es;
+    const uint32_t o0 = (static_cast<uint32_t>(lane) * es) & ~3u;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(qp + o0);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(qp + o0 + 64 * es);
+    const uint32_t sh = a.q_is_bf16 ? (lane & 1) * 16u : 0u;
+    qraw[0] = w0 >> sh;
+    qraw[1] = w1 >> sh;
   }
   // sign words of elements lane and lane + 64 (the same word; see sign_bit)
   const uint32_t sw1 = sw.w[0][(lane >> 3) & 3], sw2 = sw.w2[0][(lane >> 3) & 3];
@@ -456,11 +464,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   // ---- the first super tiles' loads go out at once, bounded by the split's chunk
   // (tokens past the sequence are masked when processed), so they need not wait for
   // the sequence length, which arrives while the table is built
-  const int len_raw = a.lens[b];
-  const int c0 = split * a.chunk;
-  const int ce = min(a.t_max, c0 + a.chunk);
-  const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g) * a.t_max;
-  Rows rows = make_rows<KB, VB>(a, kvb, ce > 0 ? ce : 0, lane);
   int st = c0 + wave * kST;
   constexpr int kStep = kWaves * kST;
   // ring of kDepth + 1 register sets: the codes of the next kDepth super tiles are

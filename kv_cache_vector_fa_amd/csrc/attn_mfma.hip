@@ -196,34 +196,48 @@ struct Codes {
   uint32_t nk, nv;
 };
 
+// One (sequence, KV head) row of the cache: uniform row starts (norm rows aligned down
+// to a word), the readable token count, and the lane's constant byte offsets within a
+// super tile.  A super tile's loads use buffer resources based at its first token whose
+// range ends at the readable count (zero for a tile not loaded), so the per-tile address
+// arithmetic is scalar and a lane past the end reads zeros without touching memory.
 struct Rows {
-  Rsrc kc, vc, kn, vn;
-  int ksh, vsh;   // norm rows: tokens of the half-word offset of their start
-  int nsh;        // this lane's (ksh for lanes < 32, vsh for lanes >= 32)
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint8_t* kn;
+  const uint8_t* vn;
+  int ntok;        // tokens [0, ntok) are readable
+  int ksh, vsh;    // norm rows: tokens of the half-word offset of their start
+  int nsh;         // this lane's (ksh for lanes < 32, vsh for lanes >= 32)
+  uint32_t ko, ko3, vo, vo3;   // code offsets of the lane in a super tile (3-bit high planes)
+  uint32_t okn, ovn;           // norm word offsets (kOOB for the other half of the wave)
 };
 
 template <int KB, int VB>
 __device__ __forceinline__ void issue_loads(const Rows& r, Codes<KB, VB>& c, int s0, bool live,
                                             int lane) {
   constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
-  const int n = lane & 15, qq = lane >> 4;
-  const uint32_t tk = static_cast<uint32_t>(s0 + n);
-  const uint32_t tv = static_cast<uint32_t>(s0 + 4 * qq);
+  // s0 is even (super tiles start at multiples of 32 tokens), so a norm word of the
+  // tile starts at word s0 / 2 of the row
+  const uint32_t rem = live && s0 < r.ntok ? static_cast<uint32_t>(r.ntok - s0) : 0u;
+  const uint32_t nw = live ? static_cast<uint32_t>(max((r.ntok + r.ksh + 1) / 2 - s0 / 2, 0)) : 0u;
+  const uint32_t vw = live ? static_cast<uint32_t>(max((r.ntok + r.vsh + 1) / 2 - s0 / 2, 0)) : 0u;
+  const Rsrc kc = make_rsrc(r.kc + static_cast<uint32_t>(s0) * KCB, rem * KCB);
+  const Rsrc vc = make_rsrc(r.vc + static_cast<uint32_t>(s0) * VCB, rem * VCB);
+  const Rsrc kn = make_rsrc(r.kn + 2u * static_cast<uint32_t>(s0), nw * 4u);
+  const Rsrc vn = make_rsrc(r.vn + 2u * static_cast<uint32_t>(s0), vw * 4u);
 #pragma unroll
   for (int t4 = 0; t4 < 2; ++t4) {
     if constexpr (KB == 4) {
-      const uint32_t o = live ? tk * KCB + 16 * qq : kOOB;
       const uint4 w = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kc, o + 16 * KCB * t4, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, r.ko + 16 * KCB * t4, 0, 0));
       c.k[t4][0] = w.x; c.k[t4][1] = w.y; c.k[t4][2] = w.z; c.k[t4][3] = w.w;
     } else {
-      const uint32_t o = live ? tk * KCB + 8 * qq : kOOB;
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(r.kc, o + 16 * KCB * t4, 0, 0);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(kc, r.ko + 16 * KCB * t4, 0, 0);
       c.k[t4][0] = w[0];
       c.k[t4][1] = w[1];
       if constexpr (KB == 3) {
-        const uint32_t oh = live ? tk * KCB + 32 + 4 * qq : kOOB;
-        c.k[t4][2] = __builtin_amdgcn_raw_buffer_load_b32(r.kc, oh + 16 * KCB * t4, 0, 0);
+        c.k[t4][2] = __builtin_amdgcn_raw_buffer_load_b32(kc, r.ko3 + 16 * KCB * t4, 0, 0);
       } else {
         c.k[t4][2] = 0;
       }
@@ -231,26 +245,15 @@ __device__ __forceinline__ void issue_loads(const Rows& r, Codes<KB, VB>& c, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t d = (16 * t4 + j) * VCB;
-      if constexpr (VB == 4) {
-        const uint32_t o = live ? tv * VCB + 4 * n : kOOB;
-        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o + d, 0, 0);
-      } else {
-        const uint32_t o = live ? tv * VCB + 4 * (n >> 1) : kOOB;
-        c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o + d, 0, 0);
-        if constexpr (VB == 3) {
-          const uint32_t oh = live ? tv * VCB + 32 + 4 * (n >> 2) : kOOB;
-          c.v[t4][j][1] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, oh + d, 0, 0);
-        }
-      }
+      c.v[t4][j][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, r.vo + d, 0, 0);
+      if constexpr (VB == 3)
+        c.v[t4][j][1] = __builtin_amdgcn_raw_buffer_load_b32(vc, r.vo3 + d, 0, 0);
     }
   }
   // (two loads with uniform resources, each lane using one: lanes < 32 the key norm
   // word, lanes >= 32 the value norm word)
-  const uint32_t ok = live && lane < 32 ? static_cast<uint32_t>(s0 + lane + r.ksh) / 2 * 4 : kOOB;
-  const uint32_t ov =
-      live && lane >= 32 ? static_cast<uint32_t>(s0 + lane - 32 + r.vsh) / 2 * 4 : kOOB;
-  c.nk = __builtin_amdgcn_raw_buffer_load_b32(r.kn, ok, 0, 0);
-  c.nv = __builtin_amdgcn_raw_buffer_load_b32(r.vn, ov, 0, 0);
+  c.nk = __builtin_amdgcn_raw_buffer_load_b32(kn, r.okn, 0, 0);
+  c.nv = __builtin_amdgcn_raw_buffer_load_b32(vn, r.ovn, 0, 0);
 }
 
 // The key words of one tile as four words of table index bytes (byte i of the 16:
@@ -382,24 +385,33 @@ __device__ __forceinline__ void rotate_out(float2 o, const SignWords& sw, int la
       make_float2(sign_bit(sw, 2 * lane) ? -r0 : r0, sign_bit(sw, 2 * lane + 1) ? -r1 : r1);
 }
 
-// Buffer resources of one (sequence, KV head) row covering tokens [0, ntok): codes, and
-// norm rows read as aligned words (the start rounded down to 4 bytes, 1 token earlier
-// when it is 2 bytes past a word, and the range rounded up to whole words; a word
-// never crosses a page, so the last one is always readable).
+// The row (sequence, KV head) at token offset kvb of the cache, tokens [0, ntok)
+// readable.  Norm rows are read as aligned words: the start rounded down to 4 bytes
+// (1 token earlier when it is 2 bytes past a word) and the range rounded up to whole
+// words; a word never crosses a page, so the last one is always readable.
 template <int KB, int VB>
 __device__ __forceinline__ Rows make_rows(const AttnLaunch& a, int64_t kvb, int ntok, int lane) {
-  const uint32_t u = static_cast<uint32_t>(ntok);
+  constexpr uint32_t KCB = cbytes<KB>(), VCB = cbytes<VB>();
+  const int n = lane & 15, qq = lane >> 4;
   Rows r;
-  r.kc = make_rsrc(a.k_codes + kvb * cbytes<KB>(), u * cbytes<KB>());
-  r.vc = make_rsrc(a.v_codes + kvb * cbytes<VB>(), u * cbytes<VB>());
+  r.kc = a.k_codes + kvb * KCB;
+  r.vc = a.v_codes + kvb * VCB;
   const uintptr_t ka = reinterpret_cast<uintptr_t>(a.k_norms + kvb);
   const uintptr_t va = reinterpret_cast<uintptr_t>(a.v_norms + kvb);
-  const int ksh = static_cast<int>((ka >> 1) & 1), vsh = static_cast<int>((va >> 1) & 1);
-  r.kn = make_rsrc(reinterpret_cast<const void*>(ka & ~uintptr_t{3}), (u + ksh + 1) / 2 * 4);
-  r.vn = make_rsrc(reinterpret_cast<const void*>(va & ~uintptr_t{3}), (u + vsh + 1) / 2 * 4);
-  r.ksh = ksh;
-  r.vsh = vsh;
-  r.nsh = lane < 32 ? ksh : vsh;
+  r.ksh = static_cast<int>((ka >> 1) & 1);
+  r.vsh = static_cast<int>((va >> 1) & 1);
+  r.kn = reinterpret_cast<const uint8_t*>(ka & ~uintptr_t{3});
+  r.vn = reinterpret_cast<const uint8_t*>(va & ~uintptr_t{3});
+  r.ntok = ntok;
+  r.nsh = lane < 32 ? r.ksh : r.vsh;
+  // key words: token n of the tile, 16 (4-bit) or 8 bytes of quarter qq; value words:
+  // token 4 qq of the tile, the word of element 2n (4-bit) or 4 (n >> 1) (2/3-bit)
+  r.ko = n * KCB + (KB == 4 ? 16 : 8) * qq;
+  r.ko3 = n * KCB + 32 + 4 * qq;
+  r.vo = 4 * qq * VCB + (VB == 4 ? 4 * n : 4 * (n >> 1));
+  r.vo3 = 4 * qq * VCB + 32 + 4 * (n >> 2);
+  r.okn = lane < 32 ? static_cast<uint32_t>(lane + r.ksh) / 2 * 4 : kOOB;
+  r.ovn = lane >= 32 ? static_cast<uint32_t>(lane - 32 + r.vsh) / 2 * 4 : kOOB;
   return r;
 }
 
@@ -424,7 +436,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   __shared__ float comb_ml[kWaves][kMaxG][2];
   static_assert(!(VSH && V2), "2-bit values have their own entries");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile indices
   const int n = lane & 15, qq = lane >> 4;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = GT > 0 ? GT : a.hq / a.hkv;

@@ -35,8 +35,10 @@ Other modes:
                           stated subset), one worker and N worker processes (no GPU).
 
 Each kernel's per-call distribution (median, p10, p90) comes from a separate pass of
-60 calls, each between its own pair of HIP events; the step figures above are means
-over back-to-back calls.  ``attn_decode_graph`` times the attention as a HIP graph of
+60 calls, each between its own pair of HIP events (``per_call``: steady state, back to
+back over the rotating copies), and a cold-HBM pass (``cold_hbm``): a 1 GiB write
+before each call, then the call alone between its events; the step figures above
+are means over back-to-back calls.  ``attn_decode_graph`` times the attention as a HIP graph of
 32 calls over the cache copies (GPU time per call without host launch gaps), and
 ``attn_decode_vector_alu`` the same calls on the vector-ALU attention kernels
 (FA_TQ_ATTN_VECTOR_ALU) for comparison with the matrix-core ones.
@@ -228,6 +230,27 @@ def attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out, ws, nbytes,
     return {"us": round(us, 3), "p10_us": round(float(p10), 3), "p90_us": round(float(p90), 3),
             "gbps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "timing": f"median over {replays} replays of a HIP graph of {n_calls} calls"}
+
+
+def cold_hbm(calls, n=20, flush_bytes=1 << 30) -> dict:
+    """Cold-HBM time per call: before each call a 1 GiB scratch buffer is written (the
+    last-level cache then holds none of the call's data), and only the call itself lies
+    between its pair of HIP events.  Median, p10, p90 over n calls."""
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    us = []
+    for i in range(n):
+        scratch.fill_(i & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"median_us": round(float(p50), 3), "p10_us": round(float(p10), 3),
+            "p90_us": round(float(p90), 3), "calls": n, "flush": "1 GiB write before each call"}
 
 
 def append_decode(fa, w, cbk, cbv, seed, q, cache, out, ws, scale, replays=20) -> dict:
@@ -787,6 +810,7 @@ def main():
         "roofline": roof,
     }
     rec["per_call"] = {n: per_call_distribution(c) for n, c in zip(names, calls)}
+    rec["cold_hbm"] = {n: cold_hbm(c) for n, c in zip(names, calls)}
     rec["attn_decode_graph"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out,
                                                ws, nbytes[2])
     rec["attn_decode_vector_alu"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale,

@@ -44,10 +44,12 @@ def _outlier_heads(x):
 
 
 def _slices(name, x):
+    """Four (sequence, KV head) slices; for the batched recipe the two KV heads with
+    the largest values (the x20 channels) and two others."""
     if name == "batched":
         hs = _outlier_heads(x)
-        return [(0, hs[0]), (7, hs[1]), (15, hs[-1])]
-    return [(0, 0), (1, 5), (3, 7)]
+        return [(0, hs[0]), (7, hs[1]), (11, hs[4]), (15, hs[-1])]
+    return [(0, 0), (1, 5), (2, 2), (3, 7)]
 
 
 @pytest.mark.parametrize("name", ["batched", "long_context"])

@@ -19,10 +19,12 @@ Modules:
 * ``rotation``  -- Walsh-Hadamard transform (fp64 math mode and canonical fp32 stages).
 * ``codec``     -- norm, bucketize, bit-pack, decode, and the 8-bit variant.
 * ``attention`` -- fused rotated-domain decode attention and its brute-force check.
+* ``dense``     -- the dense random orthogonal rotation for head_dims that are not a
+                 power of two, and its encode / decode.
 
 Arithmetic modes: fp64 "math" mode for invariants and the attention reference, and
 "canonical fp32" mode (numpy float32, IEEE round-to-nearest-even, no fused
 multiply-add, a fixed operation order) which defines the exact code and norm bits.
 """
 
-from . import codebook, signs, rotation, codec, attention  # noqa: F401
+from . import codebook, signs, rotation, codec, attention, dense  # noqa: F401

@@ -107,3 +107,34 @@ def test_corrected_norm_with_the_fp16_input_norm_is_caught():
     r64 = np.linalg.norm(np.asarray(c, np.float32).astype(np.float64)[codes], axis=-1)
     q64 = (np.linalg.norm(x.astype(np.float64), axis=-1) / r64).astype(np.float16)
     assert np.count_nonzero(q64 != wrong[..., 0]) > 40
+
+
+def test_dense_rotation_without_sign_fix_is_caught(monkeypatch):
+    """Dropping the column sign fix of the QR factor breaks the positive-diagonal
+    characterization the dense-rotation pin checks."""
+    from oracle import dense
+
+    def unfixed(seed, d):
+        g = dense.normals(seed, d * d, 2 * d).reshape(d, d)
+        q, _ = np.linalg.qr(g)
+        return q
+
+    monkeypatch.setattr(dense, "dense_rotation", unfixed)
+    d = 96
+    r = dense.dense_rotation(42, d)
+    g = dense.normals(42, d * d, 2 * d).reshape(d, d)
+    assert not np.all(np.diag(r.T @ g) > 0)
+
+
+def test_dense_rotation_transposed_in_encode_is_caught():
+    """Multiplying by R^T instead of R changes u (R is not symmetric)."""
+    from oracle import dense
+    d = 96
+    r32 = dense.rotation_f32(42, d)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((8, d)).astype(np.float32)
+    b, _ = cbm.codebook(4, d)
+    _, _, u = dense.encode_dense(x, r32, b)
+    n = codec.norm_f32(codec.pad_pow2(x)).astype(np.float64)
+    wrong = (x.astype(np.float64) @ r32.astype(np.float64)) / n[:, None]
+    assert np.max(np.abs(u - wrong)) > 1e-3

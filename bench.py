@@ -47,7 +47,8 @@ After the timed steps (outside them), ``restore_bf16`` times fa_tq_decode_kv res
 the K cache to bf16 in the LMCache layout, ``encode_k_variants`` the K encode with the
 second sign vector and corrected norm, ``prefill_encode_d256`` a head_dim-256 encode in
 the whole-vector and blocked modes (and head_dim 192 zero-padded to 256 in the
-whole-vector mode), ``attention_other_workloads`` decode attention on the batched
+whole-vector mode, or with the dense random orthogonal rotation),
+``attention_other_workloads`` decode attention on the batched
 and long-context workloads, and ``append_decode`` reports the decode-loop call
 fa_tq_attn_append: one new token per sequence quantized into the full cache (ring
 slot), then attention over all T_max slots.  Eight such calls with distinct
@@ -353,7 +354,8 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     in the whole-vector mode (one 256-point rotation, the d = 256 codebook, one norm
     per vector) and in the blocked mode (two 128-blocks), for comparison; the blocked
     8-bit uniform grid (turboq8); and the first 192 channels of the same vectors (a
-    contiguous head_dim-192 tensor) in the whole-vector mode, zero-padded to 256."""
+    contiguous head_dim-192 tensor) in the whole-vector mode, zero-padded to 256, and
+    with the dense random orthogonal rotation (``dense_d192``)."""
     import torch
     import workloads
     w = workloads.WORKLOADS["prefill"]
@@ -396,6 +398,33 @@ def prefill_whole(fa, seed, reps=10) -> dict:
                      "roundtrip_vectors": int(rel.numel())}
         del xr, x0, rel
         del codes, norms, x
+    # the same first 192 channels with the dense random orthogonal rotation (the other
+    # option for a head_dim that is not a power of two): d^2 multiply-adds per vector
+    x = k[..., :192].contiguous()
+    d = 192
+    cb = fa.codebook_init(d, 4)
+    rot = torch.from_numpy(fa.rotation_dense(seed, d)).cuda()
+    codes, norms = fa.encode_dense(cb, rot, x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fa.encode_dense(cb, rot, x, codes=codes, norms=norms)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nvec = B * H * T
+    nbytes = nvec * (2 * d + codes.shape[-2] * fa.code_bytes(4) + 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    xr = fa.decode_dense(cb, rot, codes[:1].contiguous(), norms[:1].contiguous(), d)
+    x0 = x[:1].float()
+    rel = ((x0 - xr) ** 2).sum(-1) / (x0 ** 2).sum(-1).clamp_min(1e-30)
+    out["dense_d192"] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
+                         "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "roundtrip_rel_mse": float(rel.mean().item()),
+                         "roundtrip_vectors": int(rel.numel())}
+    del codes, norms, x, xr, x0, rel
     del k
     return out
 

@@ -206,6 +206,54 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook *cb, uint64_t seed, uint32_t f
                              fa_tq_layout out_layout, void *stream);
 
 /*
+ * Dense random orthogonal rotation ([Spec] "Hadamard Transform Detail": for a
+ * head_dim that is not a power of two, the alternative to zero-padding; [Spec] "Step 1:
+ * Random Orthogonal Rotation": a fixed d x d orthogonal R from the seed, rotate(x) =
+ * R x).  G[i][j] is standard normal number i*dim + j from the seed's SplitMix64
+ * stream, continuing after the 2*dim draws of the two sign vectors (draws 2*dim,
+ * 2*dim + 1, ...): draws z1, z2 give u1 = ((z1 >> 11) + 1/2) 2^-53, u2 = (z2 >> 11)
+ * 2^-53 and the Box-Muller pair r cos(2 pi u2), r sin(2 pi u2), r = sqrt(-2 ln u1).
+ * R is the Q factor of G = Q T with T's diagonal positive (fp64), rounded to fp32.
+ *   out: host, float[dim * dim], R row-major (R[i][j] at out[i*dim + j]).
+ *   dim in [2, 512] (FA_TQ_EINVAL outside).
+ */
+fa_tq_status fa_tq_rotation_dense(uint64_t seed, int32_t dim, float *out);
+
+/*
+ * Encode with the dense rotation: per vector x (head_dim elements, bf16 or fp32),
+ * n = the fp32 norm of x (squares summed pairwise over index bits 0, 1, ... of x
+ * zero-padded to a power of two), stored as fp16; codes of u = (R x) / n against cb
+ * (code = #{j : b_j < u_j}).  The head_dim codes fill ceil(head_dim / 128) packed
+ * 128-element blocks (the blocked byte layout; code 0 past head_dim); one norm per
+ * vector: norms[B][Hkv][T_max].
+ *   cb: a 2-4 bit codebook built for dim = head_dim; rotation: device, R as written
+ *   by fa_tq_rotation_dense (fp32 row-major, 16-byte aligned, owned by the caller).
+ *   head_dim in [4, 192] (FA_TQ_EUNSUPPORTED outside).  x: device, element
+ *   (b, h, t, c) at b*stride_b + h*stride_h + t*stride_t + c (non-negative strides),
+ *   aligned to its element size.  t0 / t_max / codes / norms as fa_tq_encode, except
+ *   that positions outside [0, t_max) are skipped (no ring).
+ * The product R x is an fp32 dot product (j ascending), so a code next to a decision
+ * boundary can differ from an exact evaluation by one level.
+ */
+fa_tq_status fa_tq_encode_dense(const fa_tq_codebook *cb, const float *rotation,
+                                int32_t head_dim, const void *x, fa_tq_dtype x_dtype,
+                                fa_tq_layout x_layout, int32_t batch, int32_t n_kv_heads,
+                                int32_t n_tokens, const int32_t *t0, int32_t t_max,
+                                uint8_t *codes, uint16_t *norms, void *stream);
+
+/*
+ * Decode of a dense-rotation cache: x_hat = R^T (n16 * c[code]) over the head_dim
+ * codes of each vector (fp32 accumulation), tokens t < n_tokens of every row written
+ * to out at (b, h, t, c) as fp32 or bf16 (round to nearest even); out aligned to its
+ * element size, non-negative strides.  n_tokens <= t_max.
+ */
+fa_tq_status fa_tq_decode_dense(const fa_tq_codebook *cb, const float *rotation,
+                                int32_t head_dim, const uint8_t *codes, const uint16_t *norms,
+                                int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                                int32_t t_max, void *out, fa_tq_dtype out_dtype,
+                                fa_tq_layout out_layout, void *stream);
+
+/*
  * Single-query decode attention over the packed cache ([Spec] "Optimization: Fused
  * dequant-dot"): per (b, query head h), with g = h / (n_q_heads / n_kv_heads):
  *   q' = R q;  s_t = scale * n_K[t] * <q', c_K[code_K[t]]>  for t < seq_lens[b];

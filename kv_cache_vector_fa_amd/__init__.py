@@ -88,6 +88,17 @@ _SIGS["fa_tq_attn_decode_noalloc"] = (
                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                    ctypes.c_float, _P, _P])
 NOALLOC_SCRATCH_BYTES = 8 << 20   # FA_TQ_NOALLOC_SCRATCH_BYTES
+# Dense random orthogonal rotation (head_dims that are not a power of two).
+_SIGS["fa_tq_rotation_dense"] = (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int32, _P])
+_SIGS["fa_tq_encode_dense"] = (
+    ctypes.c_int, [ctypes.POINTER(Codebook), _P, ctypes.c_int32, _P, ctypes.c_int, Layout,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                   _P])
+_SIGS["fa_tq_decode_dense"] = (
+    ctypes.c_int, [ctypes.POINTER(Codebook), _P, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int, Layout,
+                   _P])
+DENSE_MAX_HEAD_DIM = 192
 # The _ex entry points take the variant flags right after the seed.
 for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
     _r, _a = _SIGS[_name]
@@ -160,6 +171,14 @@ def signs(seed: int, head_dim: int) -> np.ndarray:
     lib = load()
     out = np.zeros(head_dim, np.int8)
     _check(lib.fa_tq_signs(seed, head_dim, out.ctypes.data))
+    return out
+
+
+def rotation_dense(seed: int, dim: int) -> np.ndarray:
+    """The dense rotation R (fp32 [dim, dim], row-major) of ``fa_tq_rotation_dense``."""
+    lib = load()
+    out = np.zeros((dim, dim), np.float32)
+    _check(lib.fa_tq_rotation_dense(seed, dim, out.ctypes.data))
     return out
 
 
@@ -502,3 +521,75 @@ def attn_append_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_new, v_new,
         _check(fn(*args))
         return keep
     return call
+
+
+def dense_cache_buffers(batch, n_kv_heads, t_max, head_dim, bits, device="cuda"):
+    """(codes, norms) of a dense-rotation cache: [B, Hkv, T_max, ceil(d/128), cb] uint8
+    and one fp16 norm per vector [B, Hkv, T_max] (int16 bits)."""
+    import torch
+    nblk = -(-head_dim // QK)
+    codes = torch.zeros((batch, n_kv_heads, t_max, nblk, code_bytes(bits)), dtype=torch.uint8,
+                        device=device)
+    norms = torch.zeros((batch, n_kv_heads, t_max), dtype=torch.int16, device=device)
+    return codes, norms
+
+
+def encode_dense(cb: Codebook, rotation, x, t_max: int | None = None, t0=None, codes=None,
+                 norms=None, stream=None):
+    """Encode x [B, Hkv, T, d] (bf16/fp32, channel stride 1) with the dense rotation
+    (``rotation``: device fp32 [d, d] from ``rotation_dense``)."""
+    import torch
+    lib = load()
+    B, H, T, d = x.shape
+    t_max = T if t_max is None else t_max
+    if codes is None or norms is None:
+        codes, norms = dense_cache_buffers(B, H, t_max, d, cb.bits, x.device)
+    nblk = -(-d // QK)
+    if tuple(codes.shape) != (B, H, t_max, nblk, code_bytes(cb.bits)) or \
+            codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError(f"codes: expected contiguous uint8 {(B, H, t_max, nblk, code_bytes(cb.bits))}")
+    if tuple(norms.shape) != (B, H, t_max) or norms.dtype != torch.int16 or \
+            not norms.is_contiguous():
+        raise ValueError(f"norms: expected contiguous int16 {(B, H, t_max)}")
+    if tuple(rotation.shape) != (d, d) or rotation.dtype != torch.float32 or \
+            not rotation.is_contiguous():
+        raise ValueError(f"rotation: expected contiguous float32 {(d, d)}")
+    if x.stride(3) != 1:
+        raise ValueError("x: channel stride must be 1")
+    if t0 is not None and (t0.dtype != torch.int32 or tuple(t0.shape) != (B,)):
+        raise ValueError("t0: expected int32 of shape (B,)")
+    _same_device(x, codes, norms, rotation, *([t0] if t0 is not None else []))
+    lay = Layout(x.stride(0), x.stride(1), x.stride(2))
+    _check(lib.fa_tq_encode_dense(ctypes.byref(cb), _ptr(rotation), d, _ptr(x), _dtype_code(x),
+                                  lay, B, H, T, _ptr(t0), t_max, _ptr(codes), _ptr(norms),
+                                  _stream(stream)))
+    return codes, norms
+
+
+def decode_dense(cb: Codebook, rotation, codes, norms, head_dim: int, n_tokens: int | None = None,
+                 out=None, out_dtype=None, stream=None):
+    """Restore a dense-rotation cache to out [B, Hkv, n_tokens, head_dim] (fp32 by
+    default, or bf16; channel stride 1)."""
+    import torch
+    lib = load()
+    B, H, t_max, nblk, cbytes = codes.shape
+    n_tokens = t_max if n_tokens is None else n_tokens
+    if nblk != -(-head_dim // QK) or cbytes != code_bytes(cb.bits) or not codes.is_contiguous():
+        raise ValueError("codes: not a dense-rotation cache of this head_dim and bit width")
+    if tuple(norms.shape) != (B, H, t_max) or norms.dtype != torch.int16 or \
+            not norms.is_contiguous():
+        raise ValueError(f"norms: expected contiguous int16 {(B, H, t_max)}")
+    if tuple(rotation.shape) != (head_dim, head_dim) or rotation.dtype != torch.float32 or \
+            not rotation.is_contiguous():
+        raise ValueError(f"rotation: expected contiguous float32 {(head_dim, head_dim)}")
+    if out is None:
+        out = torch.empty((B, H, n_tokens, head_dim), dtype=out_dtype or torch.float32,
+                          device=codes.device)
+    if tuple(out.shape) != (B, H, n_tokens, head_dim) or out.stride(3) != 1:
+        raise ValueError(f"out {tuple(out.shape)} for a cache of {tuple(codes.shape)}")
+    _same_device(codes, norms, rotation, out)
+    lay = Layout(out.stride(0), out.stride(1), out.stride(2))
+    _check(lib.fa_tq_decode_dense(ctypes.byref(cb), _ptr(rotation), head_dim, _ptr(codes),
+                                  _ptr(norms), B, H, n_tokens, t_max, _ptr(out), _dtype_code(out),
+                                  lay, _stream(stream)))
+    return out

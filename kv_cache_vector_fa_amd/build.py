@@ -31,6 +31,7 @@ SOURCES = [
     ("codec.hip", ["-ffp-contract=off"]),
     ("attn.hip", []),
     ("attn_mfma.hip", []),
+    ("dense.hip", ["-ffp-contract=off"]),
 ]
 
 

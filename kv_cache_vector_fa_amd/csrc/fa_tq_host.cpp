@@ -481,11 +481,175 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
                   who);
 }
 
+
+// Dense random orthogonal rotation ([Spec] "Hadamard Transform Detail": the option for
+// head_dims that are not a power of two; "Step 1": a fixed d x d orthogonal R from the
+// seed).  The Gaussian matrix G (row-major) takes SplitMix64 draws 2d, 2d + 1, ... of
+// the seed's stream (after the two sign vectors' draws) in pairs through the
+// Box-Muller transform (Box and Muller, 1958); R is the Q factor of G = Q T by
+// Householder reflections in fp64, with the columns' signs chosen so that T has a
+// positive diagonal; stored rounded to fp32.
+void make_dense_rotation(uint64_t seed, int d, float* out) {
+  const size_t n = static_cast<size_t>(d) * d;
+  SplitMix64 g{seed};
+  for (int i = 0; i < 2 * d; ++i) g.next();
+  std::vector<double> a(n + 1);
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (size_t t = 0; t < n; t += 2) {
+    const uint64_t z1 = g.next(), z2 = g.next();
+    const double u1 = (static_cast<double>(z1 >> 11) + 0.5) * 0x1p-53;
+    const double u2 = static_cast<double>(z2 >> 11) * 0x1p-53;
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    a[t] = r * std::cos(two_pi * u2);
+    a[t + 1] = r * std::sin(two_pi * u2);   // a has one spare element for odd n
+  }
+  auto A = [&](int i, int j) -> double& { return a[static_cast<size_t>(i) * d + j]; };
+  std::vector<double> v(n, 0.0), diag(d);
+  for (int k = 0; k < d; ++k) {
+    double* vk = &v[static_cast<size_t>(k) * d];
+    double norm = 0.0;
+    for (int i = k; i < d; ++i) norm += A(i, k) * A(i, k);
+    norm = std::sqrt(norm);
+    const double alpha = A(k, k) > 0.0 ? -norm : norm;
+    for (int i = k; i < d; ++i) vk[i] = A(i, k);
+    vk[k] -= alpha;
+    double vn = 0.0;
+    for (int i = k; i < d; ++i) vn += vk[i] * vk[i];
+    vn = std::sqrt(vn);
+    if (vn > 0.0)
+      for (int i = k; i < d; ++i) vk[i] /= vn;
+    for (int j = k; j < d; ++j) {
+      double sdot = 0.0;
+      for (int i = k; i < d; ++i) sdot += vk[i] * A(i, j);
+      for (int i = k; i < d; ++i) A(i, j) -= 2.0 * sdot * vk[i];
+    }
+    diag[k] = A(k, k);
+  }
+  // Q = H_0 H_1 ... H_{d-1}, applied to the identity from the last reflection back
+  std::vector<double> q(n, 0.0);
+  for (int i = 0; i < d; ++i) q[static_cast<size_t>(i) * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    const double* vk = &v[static_cast<size_t>(k) * d];
+    for (int j = 0; j < d; ++j) {
+      double sdot = 0.0;
+      for (int i = k; i < d; ++i) sdot += vk[i] * q[static_cast<size_t>(i) * d + j];
+      for (int i = k; i < d; ++i) q[static_cast<size_t>(i) * d + j] -= 2.0 * sdot * vk[i];
+    }
+  }
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < d; ++k) {
+      const double x = q[static_cast<size_t>(i) * d + k];
+      out[static_cast<size_t>(i) * d + k] = static_cast<float>(diag[k] < 0.0 ? -x : x);
+    }
+}
+
+// The dense-rotation calls: head_dim in [4, kDenseMax], a 2-4 bit codebook of dim
+// head_dim.
+fa_tq_status check_dense(const fa_tq_codebook* cb, const float* rotation, int32_t head_dim,
+                         const char* who, fatq::KTable* tab) {
+  if (head_dim < 4 || head_dim > fatq::kDenseMax)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d not in [4, %d]", who, head_dim,
+                fatq::kDenseMax);
+  fa_tq_status st = check_codebook(cb, who, false, tab, head_dim);
+  if (st != FA_TQ_OK) return st;
+  if (!rotation) return fail(FA_TQ_EINVAL, "%s: rotation is NULL", who);
+  if (!aligned16(rotation)) return fail(FA_TQ_EINVAL, "%s: rotation must be 16-byte aligned", who);
+  return ok();
+}
 }  // namespace
 
 extern "C" {
 
 const char* fa_tq_last_error(void) { return g_last_error.c_str(); }
+
+fa_tq_status fa_tq_rotation_dense(uint64_t seed, int32_t dim, float* out) {
+  if (!out) return fail(FA_TQ_EINVAL, "fa_tq_rotation_dense: out is NULL");
+  if (dim < 2 || dim > 512)
+    return fail(FA_TQ_EINVAL, "fa_tq_rotation_dense: dim %d not in [2, 512]", dim);
+  make_dense_rotation(seed, dim, out);
+  return ok();
+}
+
+fa_tq_status fa_tq_encode_dense(const fa_tq_codebook* cb, const float* rotation,
+                                int32_t head_dim, const void* x, fa_tq_dtype x_dtype,
+                                fa_tq_layout x_layout, int32_t batch, int32_t n_kv_heads,
+                                int32_t n_tokens, const int32_t* t0, int32_t t_max,
+                                uint8_t* codes, uint16_t* norms, void* stream) {
+  static const char* who = "fa_tq_encode_dense";
+  fatq::KTable tab;
+  fa_tq_status st = check_dense(cb, rotation, head_dim, who, &tab);
+  if (st != FA_TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative size", who);
+  if (x_dtype != FA_TQ_F32 && x_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: input dtype %d", who, (int)x_dtype);
+  if (x_layout.stride_b < 0 || x_layout.stride_h < 0 || x_layout.stride_t < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative stride", who);
+  if (n_tokens > t_max && !t0)
+    return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if (!x || !codes || !norms) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if ((reinterpret_cast<uintptr_t>(x) & (x_dtype == FA_TQ_BF16 ? 1u : 3u)) || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(norms) & 1u))
+    return fail(FA_TQ_EINVAL, "%s: misaligned pointer", who);
+  fatq::DenseLaunch a;
+  a.x = x;
+  a.sb = x_layout.stride_b;
+  a.sh = x_layout.stride_h;
+  a.st = x_layout.stride_t;
+  a.batch = batch;
+  a.heads = n_kv_heads;
+  a.tokens = n_tokens;
+  a.t_max = t_max;
+  a.dim = head_dim;
+  a.nblk = (head_dim + fatq::QK - 1) / fatq::QK;
+  a.t0 = t0;
+  a.rot = rotation;
+  a.codes = codes;
+  a.norms = norms;
+  a.x_is_bf16 = x_dtype == FA_TQ_BF16;
+  return launched(fatq::launch_dense_encode(a, tab, static_cast<hipStream_t>(stream)), who);
+}
+
+fa_tq_status fa_tq_decode_dense(const fa_tq_codebook* cb, const float* rotation,
+                                int32_t head_dim, const uint8_t* codes, const uint16_t* norms,
+                                int32_t batch, int32_t n_kv_heads, int32_t n_tokens,
+                                int32_t t_max, void* out, fa_tq_dtype out_dtype,
+                                fa_tq_layout out_layout, void* stream) {
+  static const char* who = "fa_tq_decode_dense";
+  fatq::KTable tab;
+  fa_tq_status st = check_dense(cb, rotation, head_dim, who, &tab);
+  if (st != FA_TQ_OK) return st;
+  if (batch < 0 || n_kv_heads < 0 || n_tokens < 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative size", who);
+  if (n_tokens > t_max)
+    return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (out_dtype != FA_TQ_F32 && out_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: output dtype %d", who, (int)out_dtype);
+  if (out_layout.stride_b < 0 || out_layout.stride_h < 0 || out_layout.stride_t < 0)
+    return fail(FA_TQ_EINVAL, "%s: negative stride", who);
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if (!codes || !norms || !out) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if (!aligned16(codes) || (reinterpret_cast<uintptr_t>(norms) & 1u) ||
+      (reinterpret_cast<uintptr_t>(out) & (out_dtype == FA_TQ_BF16 ? 1u : 3u)))
+    return fail(FA_TQ_EINVAL, "%s: misaligned pointer", who);
+  fatq::DenseDecodeLaunch d;
+  d.codes = codes;
+  d.norms = norms;
+  d.rot = rotation;
+  d.rows = static_cast<int64_t>(batch) * n_kv_heads;
+  d.tokens = n_tokens;
+  d.t_max = t_max;
+  d.heads = n_kv_heads;
+  d.dim = head_dim;
+  d.nblk = (head_dim + fatq::QK - 1) / fatq::QK;
+  d.out = out;
+  d.sb = out_layout.stride_b;
+  d.sh = out_layout.stride_h;
+  d.st = out_layout.stride_t;
+  d.out_bf16 = out_dtype == FA_TQ_BF16;
+  return launched(fatq::launch_dense_decode(d, tab, static_cast<hipStream_t>(stream)), who);
+}
 
 int32_t fa_tq_code_bytes(int32_t bits) {
   switch (bits) {

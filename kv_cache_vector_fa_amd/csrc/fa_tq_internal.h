@@ -86,6 +86,38 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWords& sw,
                          bool whole, hipStream_t stream);
 
+// Dense random orthogonal rotation ([Spec] "Hadamard Transform Detail", the option for
+// head_dims that are not a power of two): encode and decode with a d x d fp32 matrix R
+// (row-major, device memory), d <= kDenseMax; codes of the d coordinates in
+// nblk = ceil(d / 128) blocks (code 0 past d), one fp16 norm per vector.
+constexpr int kDenseMax = 192;
+
+struct DenseLaunch {
+  const void* x;
+  int64_t sb, sh, st;   // element strides
+  int32_t batch, heads, tokens, t_max, dim, nblk;
+  const int32_t* t0;    // first cache position per sequence, or null (0)
+  const float* rot;
+  uint8_t* codes;
+  uint16_t* norms;      // [rows][t_max]
+  int32_t x_is_bf16;
+};
+
+struct DenseDecodeLaunch {
+  const uint8_t* codes;
+  const uint16_t* norms;
+  const float* rot;
+  int64_t rows, tokens, t_max;
+  int32_t heads, dim, nblk;
+  void* out;
+  int64_t sb, sh, st;
+  int32_t out_bf16;
+};
+
+hipError_t launch_dense_encode(const DenseLaunch& a, const KTable& tab, hipStream_t stream);
+hipError_t launch_dense_decode(const DenseDecodeLaunch& a, const KTable& tab,
+                               hipStream_t stream);
+
 struct AttnLaunch {
   const void* q;
   int32_t q_is_bf16;

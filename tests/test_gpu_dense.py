@@ -1,0 +1,149 @@
+"""GPU parity of the dense-rotation encode and decode (head_dims that are not a power
+of two) against the CPU oracle (oracle/dense.py).
+
+Encode: the GPU encodes seeded inputs with the library's rotation matrix; codes are
+compared with the oracle's encode of the same values (fp64 product, so a code next to
+a decision boundary may differ by one level: the flip budget), norms bit for bit.
+Decode: the oracle encodes and packs; the GPU decodes those codes; the result is
+compared with the oracle's fp64 decode (relative L2 error per vector).
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import codebook as o_cb
+from oracle import codec
+from oracle import dense
+from tests.gpu_helpers import DECODE_REL_L2, bf16_to_f32, compare_norms, say, FLIP_BUDGET
+
+pytestmark = pytest.mark.gpu
+SEED = workloads.ROTATION_SEED
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_codes(gpu_codes, oracle_codes, bits, d, where):
+    """gpu_codes [N, nblk, cb] packed, oracle_codes [N, d]: adjacent flips within the
+    budget, code 0 past d, bytes equal when nothing flips."""
+    n = gpu_codes.shape[0]
+    g = codec.unpack(gpu_codes, bits).astype(np.int64)          # [N, nblk * 128]
+    assert np.all(g[:, d:] == 0), f"{where}: nonzero code past head_dim"
+    diff = g[:, :d] - oracle_codes.astype(np.int64)
+    assert np.all(np.abs(diff) <= 1), f"{where}: non-adjacent code mismatch"
+    flips = int(np.count_nonzero(diff))
+    assert flips <= max(1, FLIP_BUDGET * diff.size), f"{where}: {flips} flips in {diff.size}"
+    if flips == 0:
+        np.testing.assert_array_equal(gpu_codes, dense.pack_dense(oracle_codes, bits).reshape(gpu_codes.shape))
+    return flips
+
+
+@pytest.mark.parametrize("d", [40, 96, 160, 192])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dense_encode(gpu_lib, d, bits, dtype):
+    torch = _torch()
+    say(f"dense encode d={d} bits={bits} {dtype}")
+    rng = np.random.default_rng(d * 10 + bits)
+    B, H, T = 2, 3, 257
+    x = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    x *= rng.uniform(0.05, 20.0, (B, H, T, 1)).astype(np.float32)
+    xt = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    x32 = bf16_to_f32(xt) if dtype == "bf16" else x
+    cb = gpu_lib.codebook_init(d, bits)
+    r = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).cuda()
+    codes, norms = gpu_lib.encode_dense(cb, r, xt)
+    torch.cuda.synchronize()
+    b, _ = o_cb.codebook(bits, d)
+    oc, on, _ = dense.encode_dense(x32.reshape(-1, d), dense.rotation_f32(SEED, d), b)
+    flips = _check_codes(codes.cpu().numpy().reshape(B * H * T, -1, codes.shape[-1]), oc, bits, d,
+                         f"dense d={d} bits={bits} {dtype}")
+    compare_norms(norms.cpu().numpy(), on, f"dense d={d} norms")
+    say(f"dense d={d} bits={bits} {dtype}: {flips} flips")
+
+
+def test_dense_encode_positions_and_strides(gpu_lib):
+    """t0 positions (some past t_max: skipped), a strided input view."""
+    torch = _torch()
+    d, bits, B, H, T, t_max = 96, 4, 3, 2, 50, 64
+    rng = np.random.default_rng(5)
+    big = torch.from_numpy(rng.standard_normal((B, T, H, 128)).astype(np.float32)).cuda()
+    x = big[..., :d].permute(0, 2, 1, 3)               # [B, H, T, d], strides (T*H*128, 128, H*128)
+    t0 = torch.tensor([0, 10, 40], dtype=torch.int32, device="cuda")
+    cb = gpu_lib.codebook_init(d, bits)
+    r = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).cuda()
+    codes, norms = gpu_lib.dense_cache_buffers(B, H, t_max, d, bits)
+    codes.fill_(0xAB)
+    norms.fill_(0x1234)
+    gpu_lib.encode_dense(cb, r, x, t_max=t_max, t0=t0, codes=codes, norms=norms)
+    torch.cuda.synchronize()
+    b, _ = o_cb.codebook(bits, d)
+    gc, gn = codes.cpu().numpy(), norms.cpu().numpy()
+    x32 = x.cpu().numpy()
+    for bi, start in enumerate([0, 10, 40]):
+        n_in = min(T, t_max - start)
+        oc, on, _ = dense.encode_dense(np.ascontiguousarray(x32[bi, :, :n_in]).reshape(-1, d),
+                                       dense.rotation_f32(SEED, d), b)
+        _check_codes(gc[bi, :, start:start + n_in].reshape(H * n_in, 1, -1), oc, bits, d, "positions")
+        compare_norms(gn[bi, :, start:start + n_in], on, "positions")
+        # slots before the start and after the last position are untouched
+        assert np.all(gc[bi, :, :start] == 0xAB) and np.all(gc[bi, :, start + n_in:] == 0xAB)
+
+
+@pytest.mark.parametrize("d,bits", [(40, 4), (96, 2), (160, 3), (192, 4)])
+def test_dense_decode(gpu_lib, d, bits):
+    torch = _torch()
+    say(f"dense decode d={d} bits={bits}")
+    rng = np.random.default_rng(d + 100 * bits)
+    B, H, T = 2, 2, 300
+    x = rng.standard_normal((B, H, T, d)).astype(np.float32) * 3.0
+    b, c = o_cb.codebook(bits, d)
+    r32 = dense.rotation_f32(SEED, d)
+    oc, on, _ = dense.encode_dense(x.reshape(-1, d), r32, b)
+    packed = dense.pack_dense(oc, bits).reshape(B, H, T, -1, codec.code_bytes(bits))
+    norms = on.reshape(B, H, T).view(np.int16)
+    ref = dense.decode_dense(oc, on, r32, c).reshape(B, H, T, d)
+    cb = gpu_lib.codebook_init(d, bits)
+    r = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).cuda()
+    ct, nt = torch.from_numpy(packed).cuda(), torch.from_numpy(norms).cuda()
+    out = gpu_lib.decode_dense(cb, r, ct, nt, d).cpu().numpy()
+    err = np.linalg.norm(out - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    assert float(err.max()) <= DECODE_REL_L2, float(err.max())
+    # bf16 output: the fp32 result rounded to nearest even
+    outb = gpu_lib.decode_dense(cb, r, ct, nt, d, out_dtype=torch.bfloat16)
+    want = torch.from_numpy(out).cuda().to(torch.bfloat16)
+    assert torch.equal(outb.view(torch.int16), want.view(torch.int16))
+    # a sub-range of tokens
+    part = gpu_lib.decode_dense(cb, r, ct, nt, d, n_tokens=7).cpu().numpy()
+    np.testing.assert_array_equal(part, out[:, :, :7])
+
+
+def test_dense_prefill_slice_sampled(gpu_lib):
+    """The first 192 channels of a prefill-shaped slice (8 x 8 x 4096 vectors, bf16 AR(1)
+    rho 0.9), all encoded on the GPU, 32768 sampled vectors compared with the oracle."""
+    torch = _torch()
+    w = workloads.WORKLOADS["prefill"]
+    k, _ = workloads.make_kv(w, "cuda", tokens=4096, batch=8)
+    x = k[..., :192].contiguous()
+    del k
+    d, bits = 192, 4
+    cb = gpu_lib.codebook_init(d, bits)
+    r = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).cuda()
+    codes, norms = gpu_lib.encode_dense(cb, r, x)
+    torch.cuda.synchronize()
+    nvec = x.shape[0] * x.shape[1] * x.shape[2]
+    pick = np.sort(np.random.default_rng(1).choice(nvec, 32768, replace=False))
+    idx = torch.from_numpy(pick).cuda()
+    xs = x.reshape(nvec, d).index_select(0, idx)
+    gc = codes.reshape(nvec, -1, codes.shape[-1]).index_select(0, idx).cpu().numpy()
+    gn = norms.reshape(nvec).index_select(0, idx).cpu().numpy()
+    b, _ = o_cb.codebook(bits, d)
+    oc, on, _ = dense.encode_dense(bf16_to_f32(xs), dense.rotation_f32(SEED, d), b)
+    flips = _check_codes(gc, oc, bits, d, "prefill dense")
+    compare_norms(gn, on, "prefill dense")
+    say(f"prefill dense d=192: {flips} flips in {oc.size} codes")

@@ -311,3 +311,42 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
                                        T, 0.1, fake, None)
     assert st == fa.FA_TQ_EUNSUPPORTED
     assert "scratch" in lib.fa_tq_last_error().decode()
+
+
+@pytest.mark.parametrize("dim", [24, 96, 160, 192, 250])
+def test_dense_rotation_matches_oracle(lib, dim):
+    """fa_tq_rotation_dense (C++ Householder) and the oracle (numpy QR) give the same
+    fp32 matrix: two independent implementations of the sign-fixed QR factor."""
+    from oracle import dense
+    out = fa.rotation_dense(42, dim)
+    ref = dense.rotation_f32(42, dim)
+    assert np.max(np.abs(out.astype(np.float64) - ref.astype(np.float64))) <= 2 ** -23
+    assert np.count_nonzero(out != ref) <= dim * dim // 1000
+
+
+def test_dense_rejections_before_launch(lib):
+    ctypes_cb = fa.codebook_init(96, 4)
+    lay = fa.Layout(0, 0, 96)
+    x = ctypes.c_void_p(256)
+    rot = ctypes.c_void_p(4096)
+    codes = ctypes.c_void_p(4096)
+    norms = ctypes.c_void_p(4096)
+    # head_dim past the dense limit
+    cb300 = fa.codebook_init(300, 4)
+    assert lib.fa_tq_encode_dense(ctypes.byref(cb300), rot, 300, x, fa.FA_TQ_BF16, lay, 1, 1, 1,
+                                  None, 1, codes, norms, None) == fa.FA_TQ_EUNSUPPORTED
+    # codebook built for another dim
+    cb128 = fa.codebook_init(128, 4)
+    assert lib.fa_tq_encode_dense(ctypes.byref(cb128), rot, 96, x, fa.FA_TQ_BF16, lay, 1, 1, 1,
+                                  None, 1, codes, norms, None) == fa.FA_TQ_EINVAL
+    # no rotation
+    assert lib.fa_tq_encode_dense(ctypes.byref(ctypes_cb), None, 96, x, fa.FA_TQ_BF16, lay, 1, 1,
+                                  1, None, 1, codes, norms, None) == fa.FA_TQ_EINVAL
+    # the 8-bit grid has no dense form
+    cb8 = fa.codebook_init(96, 8)
+    assert lib.fa_tq_decode_dense(ctypes.byref(cb8), rot, 96, codes, norms, 1, 1, 1, 1,
+                                  ctypes.c_void_p(4096), fa.FA_TQ_F32, lay, None) != fa.FA_TQ_OK
+    # n_tokens > t_max on decode
+    assert lib.fa_tq_decode_dense(ctypes.byref(ctypes_cb), rot, 96, codes, norms, 1, 1, 5, 4,
+                                  ctypes.c_void_p(4096), fa.FA_TQ_F32, lay, None) == fa.FA_TQ_EINVAL
+    assert lib.fa_tq_rotation_dense(42, 1, ctypes.c_void_p(4096)) == fa.FA_TQ_EINVAL

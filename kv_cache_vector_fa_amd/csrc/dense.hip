@@ -118,6 +118,7 @@ __global__ void __launch_bounds__(kDThreads) dense_encode_kernel(DenseLaunch a, 
     for (int k = 0; k < 3; ++k)
 #pragma unroll
       for (int v = 0; v < kDV; ++v) y[k][v] = 0.0f;
+#pragma unroll 4
     for (int j = 0; j < d; ++j) {
       const Stage xv = xs[wave][j];
       const float* rj = rt + j * d + lane;
@@ -142,7 +143,9 @@ __global__ void __launch_bounds__(kDThreads) dense_encode_kernel(DenseLaunch a, 
         uint32_t code = 0;
         if (k < 3 && i < d) {
           const float u = y[k][v] * g;
-          for (int q = 0; q < tab.nb; ++q) code += u > tab.b[q] ? 1u : 0u;
+          // the boundaries past nb are +inf (never below u)
+#pragma unroll
+          for (int q = 0; q < 15; ++q) code += u > tab.b[q] ? 1u : 0u;
         }
         cs[v * 256 + i] = static_cast<uint8_t>(code);
       }
@@ -246,6 +249,7 @@ __global__ void __launch_bounds__(kDThreads) dense_decode_kernel(DenseDecodeLaun
 #pragma unroll
       for (int v = 0; v < kDV; ++v) x[k][v] = 0.0f;
     // x_hat[j] = sum_i R[i][j] * (n c[code_i]), j = lane + 64 k, i ascending
+#pragma unroll 4
     for (int i = 0; i < d; ++i) {
       const Stage cv = vs[wave][i];
       const float* ri = r + i * d + lane;

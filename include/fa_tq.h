@@ -226,14 +226,21 @@ fa_tq_status fa_tq_rotation_dense(uint64_t seed, int32_t dim, float *out);
  * (code = #{j : b_j < u_j}).  The head_dim codes fill ceil(head_dim / 128) packed
  * 128-element blocks (the blocked byte layout; code 0 past head_dim); one norm per
  * vector: norms[B][Hkv][T_max].
- *   cb: a 2-4 bit codebook built for dim = head_dim; rotation: device, R as written
- *   by fa_tq_rotation_dense (fp32 row-major, 16-byte aligned, owned by the caller).
+ *   cb: a 2-4 bit codebook built for dim = head_dim whose adjacent boundaries are
+ *   more than 2/1024 apart (they must fall in distinct cells of the encoder's uniform
+ *   1024-cell grid over [-1, 1]; FA_TQ_EUNSUPPORTED otherwise; every Lloyd-Max table
+ *   for head_dim <= 192 qualifies); rotation: device, R as written by
+ *   fa_tq_rotation_dense (fp32 row-major, 16-byte aligned, owned by the caller).
  *   head_dim in [4, 192] (FA_TQ_EUNSUPPORTED outside).  x: device, element
  *   (b, h, t, c) at b*stride_b + h*stride_h + t*stride_t + c (non-negative strides),
- *   aligned to its element size.  t0 / t_max / codes / norms as fa_tq_encode, except
- *   that positions outside [0, t_max) are skipped (no ring).
- * The product R x is an fp32 dot product (j ascending), so a code next to a decision
- * boundary can differ from an exact evaluation by one level.
+ *   aligned to its element size (16-byte aligned rows with head_dim % 8 == 0 take the
+ *   fast path).  t0 / t_max / codes / norms as fa_tq_encode, except that positions
+ *   outside [0, t_max) are skipped (no ring).  At most 2^31 - 1 vectors per call
+ *   (FA_TQ_EUNSUPPORTED otherwise).
+ * The product R x runs on fp16 matrix instructions with R split into two fp16 halves
+ * (about 22 significant bits; an fp32 input is split the same way) and fp32
+ * accumulation, so a code next to a decision boundary can differ from an exact
+ * evaluation by one level.
  */
 fa_tq_status fa_tq_encode_dense(const fa_tq_codebook *cb, const float *rotation,
                                 int32_t head_dim, const void *x, fa_tq_dtype x_dtype,
@@ -242,10 +249,12 @@ fa_tq_status fa_tq_encode_dense(const fa_tq_codebook *cb, const float *rotation,
                                 uint8_t *codes, uint16_t *norms, void *stream);
 
 /*
- * Decode of a dense-rotation cache: x_hat = R^T (n16 * c[code]) over the head_dim
- * codes of each vector (fp32 accumulation), tokens t < n_tokens of every row written
- * to out at (b, h, t, c) as fp32 or bf16 (round to nearest even); out aligned to its
- * element size, non-negative strides.  n_tokens <= t_max.
+ * Decode of a dense-rotation cache: x_hat = n16 * (R^T c[code]) over the head_dim
+ * codes of each vector (R and the centroids split into two fp16 halves each, fp32
+ * accumulation: about 2^-21 relative), tokens t < n_tokens of every row written to
+ * out at (b, h, t, c) as fp32 or bf16 (round to nearest even); out aligned to its
+ * element size, non-negative strides.  n_tokens <= t_max; at most 2^31 - 1 vectors
+ * per call (FA_TQ_EUNSUPPORTED otherwise).
  */
 fa_tq_status fa_tq_decode_dense(const fa_tq_codebook *cb, const float *rotation,
                                 int32_t head_dim, const uint8_t *codes, const uint16_t *norms,

@@ -543,8 +543,18 @@ void make_dense_rotation(uint64_t seed, int d, float* out) {
     }
 }
 
+// Cell of u in the dense encoder's bucketize grid: clamp(floor(fma(u, G/2, G/2)), 0,
+// G - 1) in fp32, the same operations as the kernel's, so a boundary's cell here is
+// its cell there.
+int dense_grid_cell(float u) {
+  const float h = 0.5f * fatq::kDenseGrid;
+  const float f = std::fmin(std::fmax(std::fmaf(u, h, h), 0.0f),
+                            static_cast<float>(fatq::kDenseGrid - 1));
+  return static_cast<int>(std::floor(f));
+}
+
 // The dense-rotation calls: head_dim in [4, kDenseMax], a 2-4 bit codebook of dim
-// head_dim.
+// head_dim whose boundaries lie in distinct cells of the encoder's grid.
 fa_tq_status check_dense(const fa_tq_codebook* cb, const float* rotation, int32_t head_dim,
                          const char* who, fatq::KTable* tab) {
   if (head_dim < 4 || head_dim > fatq::kDenseMax)
@@ -552,6 +562,11 @@ fa_tq_status check_dense(const fa_tq_codebook* cb, const float* rotation, int32_
                 fatq::kDenseMax);
   fa_tq_status st = check_codebook(cb, who, false, tab, head_dim);
   if (st != FA_TQ_OK) return st;
+  for (int j = 1; j < tab->nb; ++j)
+    if (dense_grid_cell(tab->b[j]) == dense_grid_cell(tab->b[j - 1]))
+      return fail(FA_TQ_EUNSUPPORTED,
+                  "%s: boundaries %d and %d share a cell of the encoder's grid (width 2/%d)",
+                  who, j - 1, j, fatq::kDenseGrid);
   if (!rotation) return fail(FA_TQ_EINVAL, "%s: rotation is NULL", who);
   if (!aligned16(rotation)) return fail(FA_TQ_EINVAL, "%s: rotation must be 16-byte aligned", who);
   return ok();
@@ -587,6 +602,9 @@ fa_tq_status fa_tq_encode_dense(const fa_tq_codebook* cb, const float* rotation,
     return fail(FA_TQ_EINVAL, "%s: negative stride", who);
   if (n_tokens > t_max && !t0)
     return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (static_cast<int64_t>(batch) * n_kv_heads * n_tokens >= (int64_t{1} << 31))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: %lld vectors in one call (at most 2^31 - 1)", who,
+                static_cast<long long>(static_cast<int64_t>(batch) * n_kv_heads * n_tokens));
   if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
   if (!x || !codes || !norms) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
   if ((reinterpret_cast<uintptr_t>(x) & (x_dtype == FA_TQ_BF16 ? 1u : 3u)) || !aligned16(codes) ||
@@ -608,6 +626,13 @@ fa_tq_status fa_tq_encode_dense(const fa_tq_codebook* cb, const float* rotation,
   a.codes = codes;
   a.norms = norms;
   a.x_is_bf16 = x_dtype == FA_TQ_BF16;
+  {
+    const int64_t q = x_dtype == FA_TQ_BF16 ? 8 : 4;   // elements per 16 bytes
+    // 16-byte loads of whole 8-element chunks (a lane without a vector reads the
+    // first chunk of the input instead)
+    a.vec = head_dim % 8 == 0 && aligned16(x) && a.sb % q == 0 && a.sh % q == 0 &&
+            a.st % q == 0;
+  }
   return launched(fatq::launch_dense_encode(a, tab, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -624,6 +649,9 @@ fa_tq_status fa_tq_decode_dense(const fa_tq_codebook* cb, const float* rotation,
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
   if (n_tokens > t_max)
     return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (static_cast<int64_t>(batch) * n_kv_heads * n_tokens >= (int64_t{1} << 31))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: %lld vectors in one call (at most 2^31 - 1)", who,
+                static_cast<long long>(static_cast<int64_t>(batch) * n_kv_heads * n_tokens));
   if (out_dtype != FA_TQ_F32 && out_dtype != FA_TQ_BF16)
     return fail(FA_TQ_EUNSUPPORTED, "%s: output dtype %d", who, (int)out_dtype);
   if (out_layout.stride_b < 0 || out_layout.stride_h < 0 || out_layout.stride_t < 0)
@@ -648,6 +676,7 @@ fa_tq_status fa_tq_decode_dense(const fa_tq_codebook* cb, const float* rotation,
   d.sh = out_layout.stride_h;
   d.st = out_layout.stride_t;
   d.out_bf16 = out_dtype == FA_TQ_BF16;
+  d.vec = aligned16(out) && d.sb % 4 == 0 && d.sh % 4 == 0 && d.st % 4 == 0;
   return launched(fatq::launch_dense_decode(d, tab, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -781,6 +810,9 @@ fa_tq_status fa_tq_decode_kv(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
     return fail(FA_TQ_EINVAL, "%s: negative size", who);
   if (n_tokens > t_max)
     return fail(FA_TQ_EINVAL, "%s: n_tokens %d > t_max %d", who, n_tokens, t_max);
+  if (static_cast<int64_t>(batch) * n_kv_heads * n_tokens >= (int64_t{1} << 31))
+    return fail(FA_TQ_EUNSUPPORTED, "%s: %lld vectors in one call (at most 2^31 - 1)", who,
+                static_cast<long long>(static_cast<int64_t>(batch) * n_kv_heads * n_tokens));
   if (out_dtype != FA_TQ_F32 && out_dtype != FA_TQ_BF16)
     return fail(FA_TQ_EUNSUPPORTED, "%s: output dtype %d", who, (int)out_dtype);
   if (out_layout.stride_b % 8 || out_layout.stride_h % 8 || out_layout.stride_t % 8 ||

@@ -91,6 +91,8 @@ hipError_t launch_decode(const DecodeLaunch& d, const KTable& tab, const SignWor
 // (row-major, device memory), d <= kDenseMax; codes of the d coordinates in
 // nblk = ceil(d / 128) blocks (code 0 past d), one fp16 norm per vector.
 constexpr int kDenseMax = 192;
+// cells of the dense encoder's bucketize grid over [-1, 1] (see dense_grid_cell)
+constexpr int kDenseGrid = 1024;
 
 struct DenseLaunch {
   const void* x;
@@ -101,6 +103,7 @@ struct DenseLaunch {
   uint8_t* codes;
   uint16_t* norms;      // [rows][t_max]
   int32_t x_is_bf16;
+  int32_t vec;          // x 16-byte aligned, strides of 16 bytes, d % 8 == 0: 16-byte loads
 };
 
 struct DenseDecodeLaunch {
@@ -112,6 +115,7 @@ struct DenseDecodeLaunch {
   void* out;
   int64_t sb, sh, st;
   int32_t out_bf16;
+  int32_t vec;          // out 16-byte aligned, strides multiples of 4 elements: 8/16-byte stores
 };
 
 hipError_t launch_dense_encode(const DenseLaunch& a, const KTable& tab, hipStream_t stream);

@@ -41,7 +41,7 @@ def _check_codes(gpu_codes, oracle_codes, bits, d, where):
     return flips
 
 
-@pytest.mark.parametrize("d", [40, 96, 160, 192])
+@pytest.mark.parametrize("d", [40, 70, 96, 100, 160, 192])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dense_encode(gpu_lib, d, bits, dtype):
@@ -95,7 +95,7 @@ def test_dense_encode_positions_and_strides(gpu_lib):
         assert np.all(gc[bi, :, :start] == 0xAB) and np.all(gc[bi, :, start + n_in:] == 0xAB)
 
 
-@pytest.mark.parametrize("d,bits", [(40, 4), (96, 2), (160, 3), (192, 4)])
+@pytest.mark.parametrize("d,bits", [(40, 4), (70, 3), (96, 2), (100, 4), (160, 3), (192, 4), (192, 2)])
 def test_dense_decode(gpu_lib, d, bits):
     torch = _torch()
     say(f"dense decode d={d} bits={bits}")

@@ -350,3 +350,17 @@ def test_dense_rejections_before_launch(lib):
     assert lib.fa_tq_decode_dense(ctypes.byref(ctypes_cb), rot, 96, codes, norms, 1, 1, 5, 4,
                                   ctypes.c_void_p(4096), fa.FA_TQ_F32, lay, None) == fa.FA_TQ_EINVAL
     assert lib.fa_tq_rotation_dense(42, 1, ctypes.c_void_p(4096)) == fa.FA_TQ_EINVAL
+    # two boundaries in one cell of the encoder's 1024-cell grid over [-1, 1] (0 and
+    # 0.001: distinct cells of the blocked encoder's table, one cell of the grid)
+    close = fa.codebook_init(96, 4)
+    assert close.boundaries[7] == 0.0
+    close.boundaries[8] = 0.001
+    assert lib.fa_tq_encode_dense(ctypes.byref(close), rot, 96, x, fa.FA_TQ_BF16, lay, 1, 1, 1,
+                                  None, 1, codes, norms, None) == fa.FA_TQ_EUNSUPPORTED
+    # 2^31 vectors in one call
+    assert lib.fa_tq_encode_dense(ctypes.byref(ctypes_cb), rot, 96, x, fa.FA_TQ_BF16, lay,
+                                  1 << 16, 1 << 8, 1 << 7, None, 1 << 7, codes, norms,
+                                  None) == fa.FA_TQ_EUNSUPPORTED
+    assert lib.fa_tq_decode_dense(ctypes.byref(ctypes_cb), rot, 96, codes, norms, 1 << 16,
+                                  1 << 8, 1 << 7, 1 << 7, ctypes.c_void_p(4096), fa.FA_TQ_F32,
+                                  lay, None) == fa.FA_TQ_EUNSUPPORTED

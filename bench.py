@@ -99,6 +99,9 @@ def parse():
     p.add_argument("--summarize-rocprof", metavar="DIR")
     p.add_argument("--cpu-baseline-only", action="store_true")
     p.add_argument("--cpu-baseline-full", action="store_true")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="run only the prefill-slice encode figures (whole-vector, blocked, "
+                        "8-bit, padded and dense-rotation head_dim 192) and print them")
     p.add_argument("--workers", type=int, default=0,
                    help="CPU-oracle worker processes (default: os.cpu_count(), at most 16)")
     return p.parse_args()
@@ -416,12 +419,30 @@ def prefill_whole(fa, seed, reps=10) -> dict:
     nvec = B * H * T
     nbytes = nvec * (2 * d + codes.shape[-2] * fa.code_bytes(4) + 2)
     gbs = nbytes / (us * 1e-6) / 1e9
+    # matrix-core work as executed: the hi and lo halves of R, 2 d^2 flops each
+    tflops = 2 * 2 * d * d * nvec / (us * 1e-6) / 1e12
+    # restore of the whole slice to bf16 (R^T times the centroids' hi and lo halves)
+    xb = torch.empty_like(x)
+    fa.decode_dense(cb, rot, codes, norms, d, out=xb)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fa.decode_dense(cb, rot, codes, norms, d, out=xb)
+    e1.record()
+    torch.cuda.synchronize()
+    dus = e0.elapsed_time(e1) * 1e3 / reps
+    dbytes = nvec * (codes.shape[-2] * fa.code_bytes(4) + 2 + 2 * d)
+    del xb
     xr = fa.decode_dense(cb, rot, codes[:1].contiguous(), norms[:1].contiguous(), d)
     x0 = x[:1].float()
     rel = ((x0 - xr) ** 2).sum(-1) / (x0 ** 2).sum(-1).clamp_min(1e-30)
     out["dense_d192"] = {"us": round(us, 1), "vectors_per_s": round(nvec / (us * 1e-6), 1),
                          "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "mfma_tflops": round(tflops, 1),
+                         "frac_mfma_fp16_peak": round(tflops / 2500.0, 4),
+                         "decode_bf16_us": round(dus, 1),
+                         "decode_bf16_gbps": round(dbytes / (dus * 1e-6) / 1e9, 1),
                          "roundtrip_rel_mse": float(rel.mean().item()),
                          "roundtrip_vectors": int(rel.numel())}
     del codes, norms, x, xr, x0, rel
@@ -748,6 +769,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.prefill_only:
+        print(json.dumps({"prefill_encode_d256": prefill_whole(fa, workloads.ROTATION_SEED)}),
+              flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     seed = workloads.ROTATION_SEED
     B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim

@@ -545,19 +545,13 @@ def encode_dense(cb: Codebook, rotation, x, t_max: int | None = None, t0=None, c
     if codes is None or norms is None:
         codes, norms = dense_cache_buffers(B, H, t_max, d, cb.bits, x.device)
     nblk = -(-d // QK)
-    if tuple(codes.shape) != (B, H, t_max, nblk, code_bytes(cb.bits)) or \
-            codes.dtype != torch.uint8 or not codes.is_contiguous():
-        raise ValueError(f"codes: expected contiguous uint8 {(B, H, t_max, nblk, code_bytes(cb.bits))}")
-    if tuple(norms.shape) != (B, H, t_max) or norms.dtype != torch.int16 or \
-            not norms.is_contiguous():
-        raise ValueError(f"norms: expected contiguous int16 {(B, H, t_max)}")
-    if tuple(rotation.shape) != (d, d) or rotation.dtype != torch.float32 or \
-            not rotation.is_contiguous():
-        raise ValueError(f"rotation: expected contiguous float32 {(d, d)}")
+    _expect(codes, (B, H, t_max, nblk, code_bytes(cb.bits)), torch.uint8, "codes")
+    _expect(norms, (B, H, t_max), torch.int16, "norms")
+    _expect(rotation, (d, d), torch.float32, "rotation")
     if x.stride(3) != 1:
         raise ValueError("x: channel stride must be 1")
-    if t0 is not None and (t0.dtype != torch.int32 or tuple(t0.shape) != (B,)):
-        raise ValueError("t0: expected int32 of shape (B,)")
+    if t0 is not None:
+        _expect(t0, (B,), torch.int32, "t0")
     _same_device(x, codes, norms, rotation, *([t0] if t0 is not None else []))
     lay = Layout(x.stride(0), x.stride(1), x.stride(2))
     _check(lib.fa_tq_encode_dense(ctypes.byref(cb), _ptr(rotation), d, _ptr(x), _dtype_code(x),
@@ -574,14 +568,11 @@ def decode_dense(cb: Codebook, rotation, codes, norms, head_dim: int, n_tokens: 
     lib = load()
     B, H, t_max, nblk, cbytes = codes.shape
     n_tokens = t_max if n_tokens is None else n_tokens
-    if nblk != -(-head_dim // QK) or cbytes != code_bytes(cb.bits) or not codes.is_contiguous():
+    if nblk != -(-head_dim // QK) or cbytes != code_bytes(cb.bits):
         raise ValueError("codes: not a dense-rotation cache of this head_dim and bit width")
-    if tuple(norms.shape) != (B, H, t_max) or norms.dtype != torch.int16 or \
-            not norms.is_contiguous():
-        raise ValueError(f"norms: expected contiguous int16 {(B, H, t_max)}")
-    if tuple(rotation.shape) != (head_dim, head_dim) or rotation.dtype != torch.float32 or \
-            not rotation.is_contiguous():
-        raise ValueError(f"rotation: expected contiguous float32 {(head_dim, head_dim)}")
+    _expect(codes, (B, H, t_max, nblk, cbytes), torch.uint8, "codes")
+    _expect(norms, (B, H, t_max), torch.int16, "norms")
+    _expect(rotation, (head_dim, head_dim), torch.float32, "rotation")
     if out is None:
         out = torch.empty((B, H, n_tokens, head_dim), dtype=out_dtype or torch.float32,
                           device=codes.device)

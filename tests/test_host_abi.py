@@ -299,6 +299,31 @@ def test_encode_and_decode_binding_reject_bad_buffers(lib):
         fa.decode(cb, 42, codes, norms, 128, out=torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16))
 
 
+def test_dense_binding_rejects_bad_buffers(lib):
+    """The dense-rotation binding checks every tensor before the library sees it (CPU
+    tensors: the checks run before the device check)."""
+    import torch
+    d = 96
+    cb = fa.codebook_init(d, 4)
+    x = torch.zeros((2, 2, 16, d), dtype=torch.bfloat16)
+    rot = torch.zeros((d, d), dtype=torch.float32)
+    codes = torch.zeros((2, 2, 16, 1, 64), dtype=torch.uint8)
+    norms = torch.zeros((2, 2, 16), dtype=torch.int16)
+    with pytest.raises(ValueError):   # t0 not contiguous (every other int32 of a longer row)
+        fa.encode_dense(cb, rot, x, codes=codes, norms=norms,
+                        t0=torch.zeros(4, dtype=torch.int32)[::2])
+    with pytest.raises(ValueError):   # a rotation of another size
+        fa.encode_dense(cb, torch.zeros((d + 1, d + 1)), x, codes=codes, norms=norms)
+    with pytest.raises(ValueError):   # codes of 2-bit rows for a 4-bit codebook
+        fa.encode_dense(cb, rot, x, codes=codes[..., :32].contiguous(), norms=norms)
+    with pytest.raises(ValueError):   # norms as float
+        fa.decode_dense(cb, rot, codes, norms.float(), d)
+    with pytest.raises(ValueError):   # codes for a wider head_dim
+        fa.decode_dense(cb, rot, torch.zeros((2, 2, 16, 2, 64), dtype=torch.uint8), norms, d)
+    with pytest.raises(ValueError):   # CPU tensors never reach the library
+        fa.encode_dense(cb, rot, x, codes=codes, norms=norms)
+
+
 def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     """Partials larger than the scratch array are refused before any device call
     (the pointers below are never dereferenced)."""

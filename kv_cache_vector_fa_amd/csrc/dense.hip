@@ -35,11 +35,11 @@
 // pieces), three products per tile, then x = acc * (n16 2^-28).
 //
 // Work layout: one workgroup of eight waves per compute unit (the two R halves take up
-// to 150 KB of LDS, the grid table 8 KB); a wave processes 16 NV vectors per pass, its inputs held in
-// registers as B operands for the whole pass, and loops over the output tiles (16 rows
-// of R), reading each A operand from LDS once for NV products.  LDS rows are padded by
-// 16 bytes, so the 16 lanes of a row group reading 16 rows at one column hit 16
-// distinct 4-bank groups.
+// to 150 KB of LDS, the encoder's grid table 8 KB more); a wave processes 16 NV vectors
+// per pass, holds them in registers as B operands for the whole pass, issues the next
+// pass's loads, and loops over the output tiles (16 rows of R), reading each A operand
+// from LDS once for NV products.  LDS rows are padded by 16 bytes, so the 16 lanes of a
+// row group reading 16 rows at one column hit 16 distinct 4-bank groups.
 
 #include <type_traits>
 

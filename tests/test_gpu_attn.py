@@ -71,7 +71,7 @@ def test_attn_tiny_workload(gpu_lib):
          where="tiny")
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4), (2, 3), (3, 4)])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4), (2, 3), (3, 4), (2, 2), (4, 3)])
 @pytest.mark.parametrize("B,Hq,Hkv,T,lens", [
     (3, 8, 2, 333, [333, 0, 1]),
     (2, 4, 4, 1000, [1000, 517]),
@@ -79,6 +79,9 @@ def test_attn_tiny_workload(gpu_lib):
     (2, 6, 3, 2100, [64, 2099]),
     (1, 40, 5, 300, [300]),
     (2, 5, 1, 129, [129, 77]),
+    (1, 12, 4, 257, [257]),       # groups of 3
+    (2, 14, 2, 300, [31, 300]),   # groups of 7
+    (1, 24, 2, 200, [199]),       # groups of 12: the vector-ALU kernels
 ])
 def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
     torch = _torch()

@@ -309,13 +309,13 @@ __global__ void __launch_bounds__(kDT, 1) dense_encode_kernel(DenseLaunch a, KTa
       for (int s = 0; s < NS; ++s) {
         float v[8];
         unpack8<F32>(raw[nv][s], v);
-        float p2[4];   // the pairs (2m, 2m + 1): RN(x0^2 + x1^2)
+        float p2[4];   // level 0 of the tree: q[2m] + q[2m + 1], q = RN(x^2)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if constexpr (F32) {
             p2[m] = v[2 * m] * v[2 * m] + v[2 * m + 1] * v[2 * m + 1];
           } else {
-            // a bf16 square is exact in fp32, so one fma gives RN(x0^2 + x1^2)
+            // a bf16 square is exact in fp32 (q = x^2), so one fma gives RN(q0 + q1)
             p2[m] = __builtin_fmaf(v[2 * m], v[2 * m], v[2 * m + 1] * v[2 * m + 1]);
           }
         }

@@ -63,6 +63,38 @@ def _run(fa, q, kp, kn, vp, vn, lens, kb, vb, scale, heads=None, where="", flags
     return err
 
 
+@pytest.mark.parametrize("flags", [0, "valu"])
+def test_attn_lengths_outside_the_cache_are_clamped(gpu_lib, flags):
+    """seq_lens is device data the host cannot check: a negative length gives zeros and a
+    length past t_max attends over the whole cache (the oracle on the clamped lengths)."""
+    torch = _torch()
+    B, Hq, Hkv, T = 3, 8, 2, 300
+    rng = np.random.default_rng(17)
+    k = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32)).to(torch.bfloat16)
+    kp, kn = _oracle_cache(k, 4)
+    vp, vn = _oracle_cache(v, 2)
+    dev = "cuda"
+    ck, cv = gpu_lib.codebook_init(128, 4), gpu_lib.codebook_init(128, 2)
+    fl = gpu_lib.ATTN_VECTOR_ALU if flags == "valu" else 0
+    out = gpu_lib.attn_decode(ck, cv, SEED, q.cuda(), torch.from_numpy(kp).to(dev),
+                              torch.from_numpy(kn.view(np.int16)).to(dev),
+                              torch.from_numpy(vp).to(dev),
+                              torch.from_numpy(vn.view(np.int16)).to(dev),
+                              torch.tensor([-5, T + 1000, 2**31 - 1], dtype=torch.int32,
+                                           device=dev), 1 / np.sqrt(128), flags=fl)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = o_att.attend_fused(bf16_to_f32(q), kp, kn, vp, vn, [0, T, T], 4, 2,
+                             o_cb.codebook(4)[1], o_cb.codebook(2)[1], o_signs.signs(SEED, 128),
+                             1 / np.sqrt(128))
+    assert np.all(got[0] == 0.0)
+    err = float(np.max(np.abs(got - ref)))
+    say(f"clamped lengths ({flags}): max abs err {err:.3e}")
+    assert err <= ATTN_MAX_ABS
+
+
 def test_attn_tiny_workload(gpu_lib):
     k, v, q = workloads.tiny_inputs()
     kp, kn = _oracle_cache(k.reshape(1, 1, 1024, 128), 4)

@@ -22,6 +22,10 @@ Readings (the pages name no generator):
   (``codec.norm_f32`` over the vector zero-padded to a power of two), stored as fp16.
 * Layout: the d codes of a vector fill ceil(d / 128) packed 128-element blocks, the
   positions past d holding code 0; one norm per vector.
+* Attention over such a cache ([Spec] "Optimization: Fused dequant-dot" with this R):
+  the plain definition, softmax(scale q K^T) V over the decoded keys and values
+  K^ = decode_dense(K), V^ = decode_dense(V), in fp64 (a length is clamped to
+  [0, T]; length 0 gives zeros; query head h reads KV head h / (Hq / Hkv)).
 """
 
 from __future__ import annotations
@@ -90,3 +94,29 @@ def pack_dense(codes: np.ndarray, bits: int) -> np.ndarray:
     full = np.zeros(codes.shape[:-1] + (dp,), np.uint8)
     full[..., :d] = codes
     return codec.pack(full, bits)
+
+
+def attend_dense(q: np.ndarray, k_codes: np.ndarray, k_norms16: np.ndarray,
+                 v_codes: np.ndarray, v_norms16: np.ndarray, lens, r32: np.ndarray,
+                 k_centroids: np.ndarray, v_centroids: np.ndarray, scale: float) -> np.ndarray:
+    """q [B, Hq, d]; codes [B, Hkv, T, d] (unpacked), norms fp16 [B, Hkv, T] ->
+    out fp64 [B, Hq, d] = softmax(scale q K^T) V with K^ = decode_dense(K),
+    V^ = decode_dense(V)."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv, T = k_codes.shape[1], k_codes.shape[2]
+    k_hat = decode_dense(k_codes, k_norms16, r32, k_centroids)   # [B, Hkv, T, d]
+    v_hat = decode_dense(v_codes, v_norms16, r32, v_centroids)
+    out = np.zeros((B, Hq, d))
+    grp = Hq // Hkv
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), T))
+        if n == 0:
+            continue
+        for h in range(Hq):
+            g = h // grp
+            s = scale * (k_hat[b, g, :n] @ q[b, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            out[b, h] = p @ v_hat[b, g, :n]
+    return out

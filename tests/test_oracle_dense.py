@@ -110,3 +110,66 @@ def test_pack_dense_pads_with_code_zero():
     assert p.shape == (1, 1, 64)
     back = codec.unpack(p, 4)
     assert np.array_equal(back[0, :96], codes[0]) and np.all(back[0, 96:] == 0)
+
+
+def _dense_cache(rng, B, H, T, d, bits, r32):
+    x = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    b, c = o_cb.codebook(bits, d)
+    codes, norms, _ = dense.encode_dense(x.reshape(-1, d), r32, b)
+    return codes.reshape(B, H, T, d), norms.reshape(B, H, T), c
+
+
+def test_attend_dense_is_the_fused_rotated_domain_attention():
+    """softmax(scale q K^T) V over decoded vectors equals the fused form computed in the
+    rotated domain (q' = R q, scores n <q', c[code]>, o' = sum p n c[code], out = R^T o'):
+    the identity <q, R^T k'> = <R q, k'>.  A transposed R or a wrong GQA map breaks it."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, T, d = 2, 6, 3, 37, 40
+    r = dense.rotation_f32(42, d)
+    kc, kn, ck = _dense_cache(rng, B, Hkv, T, d, 4, r)
+    vc, vn, cv = _dense_cache(rng, B, Hkv, T, d, 2, r)
+    q = rng.standard_normal((B, Hq, d))
+    lens = [37, 20]
+    scale = 1 / np.sqrt(d)
+    got = dense.attend_dense(q, kc, kn, vc, vn, lens, r, ck, cv, scale)
+    r64 = r.astype(np.float64)
+    ckf, cvf = np.asarray(ck, np.float32).astype(np.float64), np.asarray(cv, np.float32).astype(np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            n = lens[b]
+            qr = r64 @ q[b, h]
+            s = np.array([scale * float(kn[b, g, t]) * (ckf[kc[b, g, t]] @ qr) for t in range(n)])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o_rot = sum(p[t] * float(vn[b, g, t]) * cvf[vc[b, g, t]] for t in range(n))
+            np.testing.assert_allclose(got[b, h], r64.T @ o_rot, rtol=0, atol=1e-12)
+
+
+def test_attend_dense_special_cases():
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, T, d = 3, 4, 2, 9, 24
+    r = dense.rotation_f32(5, d)
+    kc, kn, ck = _dense_cache(rng, B, Hkv, T, d, 3, r)
+    vc, vn, cv = _dense_cache(rng, B, Hkv, T, d, 3, r)
+    q = rng.standard_normal((B, Hq, d))
+    v_hat = dense.decode_dense(vc, vn, r, cv)
+    # length 0 -> zeros; a length past T -> the whole cache; length 1 -> the decoded value
+    out = dense.attend_dense(q, kc, kn, vc, vn, [0, T + 50, 1], r, ck, cv, 0.3)
+    assert np.all(out[0] == 0.0)
+    np.testing.assert_array_equal(out[1], dense.attend_dense(q, kc, kn, vc, vn, [0, T, 1], r, ck,
+                                                             cv, 0.3)[1])
+    for h in range(Hq):
+        np.testing.assert_allclose(out[2, h], v_hat[2, h // 2, 0], rtol=0, atol=1e-12)
+    # identical keys -> uniform weights -> the mean of the decoded values
+    kc2 = np.broadcast_to(kc[:, :, :1], kc.shape).copy()
+    kn2 = np.broadcast_to(kn[:, :, :1], kn.shape).copy()
+    out = dense.attend_dense(q, kc2, kn2, vc, vn, [T, T, T], r, ck, cv, 0.3)
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[b, h], v_hat[b, h // 2].mean(axis=0), rtol=0, atol=1e-12)
+    # query head h reads KV head h // 2: zero norms on KV head 0 zero heads 0 and 1 only
+    vn0 = vn.copy()
+    vn0[:, 0] = 0
+    out = dense.attend_dense(q, kc, kn, vc, vn0, [T, T, T], r, ck, cv, 0.3)
+    assert np.all(out[:, :2] == 0.0) and np.all(np.abs(out[:, 2:]).sum(axis=-1) > 0)

@@ -138,3 +138,26 @@ def test_dense_rotation_transposed_in_encode_is_caught():
     n = codec.norm_f32(codec.pad_pow2(x)).astype(np.float64)
     wrong = (x.astype(np.float64) @ r32.astype(np.float64)) / n[:, None]
     assert np.max(np.abs(u - wrong)) > 1e-3
+
+
+def test_dense_attention_with_a_transposed_decode_is_caught(monkeypatch):
+    """Decoding with R instead of R^T breaks the fused-form identity the dense
+    attention pin checks (scores <q, K^> against n <R q, c[code]>)."""
+    from oracle import codebook as o_cb
+    from oracle import dense
+    d = 16
+    r = dense.rotation_f32(42, d)
+    rng = np.random.default_rng(0)
+    b, c = o_cb.codebook(4, d)
+    kc, kn, _ = dense.encode_dense(rng.standard_normal((1, d)).astype(np.float32), r, b)
+    q = rng.standard_normal(d)
+
+    def transposed(codes, norms16, r32, centroids):
+        cc = np.asarray(centroids, np.float32).astype(np.float64)
+        v = cc[np.asarray(codes)] * np.asarray(norms16, np.float16).astype(np.float64)[..., None]
+        return v @ np.asarray(r32, np.float64).T          # R v instead of R^T v
+
+    monkeypatch.setattr(dense, "decode_dense", transposed)
+    k_hat = dense.decode_dense(kc, kn, r, c)
+    fused = float(kn[0]) * (np.asarray(c, np.float32).astype(np.float64)[kc[0]] @ (r.astype(np.float64) @ q))
+    assert abs(float(k_hat[0] @ q) - fused) > 1e-6

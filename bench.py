@@ -328,6 +328,57 @@ def restore_bf16(fa, w, cbk, seed, caches, reps=64) -> dict:
             "what": "packed K cache -> bf16 [tokens][heads*head_dim]"}
 
 
+def dense_attention(fa, w, seed, k, v, q, lens, lens_np, scale) -> dict:
+    """Decode attention over dense-rotation caches of the same layer shape (head_dim
+    128, K4/V2): the keys and values encoded with the dense rotation, cloned to copies
+    holding more than 768 MB of attention bytes, calls rotating over them; the query
+    enters and the result leaves the attention kernels' frame through two small kernels
+    (fa_tq_attn_decode_dense)."""
+    import torch
+    B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim
+    cbk, cbv = fa.codebook_init(d, w.k_bits), fa.codebook_init(d, w.v_bits)
+    rot = torch.from_numpy(fa.rotation_dense(seed, d)).cuda()
+    kc, kn = fa.encode_dense(cbk, rot, k)
+    vc, vn = fa.encode_dense(cbv, rot, v)
+    nbytes = attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits)
+    copies = max(1, -(-768_000_000 // nbytes))
+    caches = [(kc, kn, vc, vn)] + [tuple(t.clone() for t in (kc, kn, vc, vn))
+                                   for _ in range(copies - 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.attn_dense_workspace_bytes(B, Hq, Hkv, T), dtype=torch.uint8,
+                     device="cuda")
+    # a HIP graph of 32 calls (each: query kernel, attention kernels, output kernel),
+    # replayed; the calls are created inside the capture (on its stream)
+    n_calls = 32
+    for i in range(4):
+        fa.attn_decode_dense(cbk, cbv, rot, q, *caches[i % copies], lens, scale, out, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls = [fa.attn_decode_dense_call(cbk, cbv, rot, q, *caches[i % copies], lens, scale,
+                                           out, ws) for i in range(n_calls)]
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(10):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    us = float(np.median(times))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res = {"us": round(us, 2), "algorithmic_bytes": int(nbytes), "gbps": round(gbs, 1),
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "copies": copies,
+           "timing": f"median over 10 replays of a HIP graph of {n_calls} calls"}
+    del g, calls
+    del caches, kc, kn, vc, vn, ws
+    return res
+
+
 def encode_variants(fa, w, cbk, seed, ks, caches, reps=20) -> dict:
     """GPU time of the K encode with the second sign vector and the corrected norm
     (fa_tq_encode_ex), over the same rotating input and cache copies as the step."""
@@ -873,6 +924,8 @@ def main():
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)
         rec["encode_k_variants"] = encode_variants(fa, w, cbk, seed, ks, caches)
+        rec["attn_decode_dense_d128"] = dense_attention(fa, w, seed, k, v, q, lens, lens_np,
+                                                        scale)
         rec["prefill_encode_d256"] = prefill_whole(fa, seed)
         rec["attention_other_workloads"] = other_attention(fa, seed)
     if not args.no_cpu_baseline:

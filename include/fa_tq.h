@@ -263,6 +263,38 @@ fa_tq_status fa_tq_decode_dense(const fa_tq_codebook *cb, const float *rotation,
                                 fa_tq_layout out_layout, void *stream);
 
 /*
+ * Single-query decode attention over a dense-rotation cache written by
+ * fa_tq_encode_dense ([Spec] "Optimization: Fused dequant-dot" with the dense R of
+ * "Hadamard Transform Detail"): per (b, query head h), g = h / (n_q_heads / n_kv_heads):
+ *   q' = R q;  s_t = scale * n_K[t] * <q', c_K[code_K[t]]>  for t < seq_lens[b];
+ *   p = softmax(s);  o' = sum_t p_t n_V[t] c_V[code_V[t]];  out = R^T o'.
+ * The coordinates past head_dim (code 0 in the cache) do not enter: q' is zero there and
+ * out takes the first head_dim coordinates of o'.  The attention kernels run in their
+ * own Walsh-Hadamard frame R_w: the query enters as R_w^-1 (R q) and the result leaves
+ * as R^T (R_w y) (two small kernels around them), so accuracy is that of
+ * fa_tq_attn_decode_ex.
+ *   cb_k, cb_v: 2-4 bit codebooks of dim head_dim; rotation: as fa_tq_encode_dense;
+ *   head_dim in [4, 128] (FA_TQ_EUNSUPPORTED above: the cache then has more than one
+ *   128-element block per vector).  q: device [batch][n_q_heads][head_dim] of q_dtype
+ *   (bf16 or fp32); k/v codes: [batch][n_kv_heads][t_max][1][code bytes]; norms:
+ *   [batch][n_kv_heads][t_max] (one per vector); seq_lens: device [batch] int32,
+ *   clamped to [0, t_max]; out: device fp32 [batch][n_q_heads][head_dim].
+ *   flags: 0 or FA_TQ_ATTN_VECTOR_ALU.  workspace: device, 16-byte aligned, at least
+ *   fa_tq_attn_dense_workspace_bytes(...) bytes, contents on entry do not matter.
+ *   Errors as fa_tq_attn_decode_ex.
+ */
+size_t fa_tq_attn_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t t_max);
+fa_tq_status fa_tq_attn_decode_dense(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                                     const float *rotation, int32_t head_dim, uint32_t flags,
+                                     const void *q, fa_tq_dtype q_dtype,
+                                     const uint8_t *k_codes, const uint16_t *k_norms,
+                                     const uint8_t *v_codes, const uint16_t *v_norms,
+                                     const int32_t *seq_lens, int32_t batch, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t t_max, float scale, float *out,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Single-query decode attention over the packed cache ([Spec] "Optimization: Fused
  * dequant-dot"): per (b, query head h), with g = h / (n_q_heads / n_kv_heads):
  *   q' = R q;  s_t = scale * n_K[t] * <q', c_K[code_K[t]]>  for t < seq_lens[b];

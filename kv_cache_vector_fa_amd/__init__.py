@@ -98,7 +98,14 @@ _SIGS["fa_tq_decode_dense"] = (
     ctypes.c_int, [ctypes.POINTER(Codebook), _P, ctypes.c_int32, _P, _P, ctypes.c_int32,
                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int, Layout,
                    _P])
+_SIGS["fa_tq_attn_dense_workspace_bytes"] = (ctypes.c_size_t, [ctypes.c_int32] * 4)
+_SIGS["fa_tq_attn_decode_dense"] = (
+    ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook), _P, ctypes.c_int32,
+                   ctypes.c_uint32, _P, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P,
+                   ctypes.c_size_t, _P])
 DENSE_MAX_HEAD_DIM = 192
+DENSE_ATTN_MAX_HEAD_DIM = 128
 # The _ex entry points take the variant flags right after the seed.
 for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
     _r, _a = _SIGS[_name]
@@ -558,6 +565,65 @@ def encode_dense(cb: Codebook, rotation, x, t_max: int | None = None, t0=None, c
                                   lay, B, H, T, _ptr(t0), t_max, _ptr(codes), _ptr(norms),
                                   _stream(stream)))
     return codes, norms
+
+
+def attn_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max) -> int:
+    return int(load().fa_tq_attn_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max))
+
+
+def attn_decode_dense_call(cb_k: Codebook, cb_v: Codebook, rotation, q, k_codes, k_norms,
+                           v_codes, v_norms, seq_lens, scale: float, out, workspace,
+                           flags: int = 0, stream=None):
+    """``attn_decode_dense`` with its arguments checked and marshalled once (see
+    ``encode_call``)."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _expect(seq_lens, (B,), torch.int32, "seq_lens")
+    _expect(rotation, (d, d), torch.float32, "rotation")
+    for name, c, n, cb in (("k", k_codes, k_norms, cb_k), ("v", v_codes, v_norms, cb_v)):
+        _expect(c, (B, Hkv, t_max, -(-d // QK), code_bytes(cb.bits)), torch.uint8, f"{name} codes")
+        _expect(n, (B, Hkv, t_max), torch.int16, f"{name} norms")
+    _expect(out, (B, Hq, d), torch.float32, "out")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _same_device(q, seq_lens, rotation, k_codes, k_norms, v_codes, v_norms, out, workspace)
+    args = (ctypes.byref(cb_k), ctypes.byref(cb_v), _ptr(rotation), ctypes.c_int32(d),
+            ctypes.c_uint32(flags), _ptr(q), ctypes.c_int(_dtype_code(q)), _ptr(k_codes),
+            _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(seq_lens), ctypes.c_int32(B),
+            ctypes.c_int32(Hq), ctypes.c_int32(Hkv), ctypes.c_int32(t_max),
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
+    fn = lib.fa_tq_attn_decode_dense
+    keep = (cb_k, cb_v, rotation, q, k_codes, k_norms, v_codes, v_norms, seq_lens, out,
+            workspace)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call
+
+
+def attn_decode_dense(cb_k: Codebook, cb_v: Codebook, rotation, q, k_codes, k_norms, v_codes,
+                      v_norms, seq_lens, scale: float, out=None, workspace=None, flags: int = 0,
+                      stream=None):
+    """Decode attention over dense-rotation caches (``encode_dense``, head_dim <= 128):
+    q [B, Hq, d] (bf16/fp32), caches [B, Hkv, T_max, 1, cb] with norms [B, Hkv, T_max];
+    returns out [B, Hq, d] float32."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, t_max = k_codes.shape[1], k_codes.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(attn_dense_workspace_bytes(B, Hq, Hkv, t_max), 16),
+                                dtype=torch.uint8, device=q.device)
+    attn_decode_dense_call(cb_k, cb_v, rotation, q, k_codes, k_norms, v_codes, v_norms,
+                           seq_lens, scale, out, workspace, flags, stream)()
+    return out
 
 
 def decode_dense(cb: Codebook, rotation, codes, norms, head_dim: int, n_tokens: int | None = None,

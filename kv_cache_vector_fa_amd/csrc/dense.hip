@@ -674,6 +674,127 @@ __global__ void __launch_bounds__(kDT, 1) dense_decode_kernel(DenseDecodeLaunch 
   }
 }
 
+// ---- attention over a dense-rotation cache: the query into the attention kernels'
+// Walsh-Hadamard frame and the result out of it (one workgroup of 128 threads per
+// (sequence, query head); thread i owns element i of the 128-point frame).
+
+__device__ __forceinline__ bool frame_sign(const DenseAttnLaunch& a, int i) {
+  return (a.signs[i >> 5] >> (i & 31)) & 1u;
+}
+
+// y <- H y over the 128 elements in LDS (butterflies of strides 1 .. 64); threads with
+// on == false only take part in the barriers
+__device__ __forceinline__ void hadamard128(float* y, int i, bool on) {
+#pragma unroll
+  for (int L = 1; L < QK; L <<= 1) {
+    float own = 0.0f, other = 0.0f;
+    if (on) {
+      own = y[i];
+      other = y[i ^ L];
+    }
+    __syncthreads();
+    if (on) y[i] = (i & L) ? other - own : own + other;
+    __syncthreads();
+  }
+}
+
+// q~ = R_w^-1 (R q) = D H (R q) / (128 c): R q zero-padded to 128, then H, the scale
+// (1 / (128 c) = c up to the rounding of c) and the signs.  The workgroup copies R into
+// LDS with coalesced loads (16-byte ones when d % 4 == 0: the host requires R 16-byte
+// aligned), rows at an odd stride so that thread i < d reads row i without bank
+// conflicts.
+constexpr int kQueryThreads = 256;
+__global__ void __launch_bounds__(kQueryThreads) dense_attn_query_kernel(DenseAttnLaunch a) {
+  __shared__ float rs[kDenseAttnMax * (kDenseAttnMax + 1)];
+  __shared__ float qs[kDenseAttnMax];
+  __shared__ float y[QK];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, d = a.dim;
+  const int ld = d | 1;
+  const int n = d * d;
+  const int64_t row = static_cast<int64_t>(b) * a.hq + h;
+  if (t < d) {
+    qs[t] = a.q_is_bf16
+                ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[row * d + t]) << 16)
+                : static_cast<const float*>(a.q)[row * d + t];
+  }
+  if ((d & 3) == 0) {
+    constexpr int kPer = kDenseAttnMax * kDenseAttnMax / 4 / kQueryThreads;
+    const float4* r4 = reinterpret_cast<const float4*>(a.rot);
+    float4 buf[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      buf[k] = r4[min(t + k * kQueryThreads, n / 4 - 1)];   // clamped: inside R
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = 4 * (t + k * kQueryThreads);
+      if (e < n) {
+        const int r = e / d, c = e - r * d;   // c .. c + 3 stay in row r
+        float* dst = rs + r * ld + c;
+        dst[0] = buf[k].x;
+        dst[1] = buf[k].y;
+        dst[2] = buf[k].z;
+        dst[3] = buf[k].w;
+      }
+    }
+  } else {
+    constexpr int kPer = kDenseAttnMax * kDenseAttnMax / kQueryThreads;
+    float buf[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      buf[k] = a.rot[min(t + k * kQueryThreads, n - 1)];   // clamped: inside R
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = t + k * kQueryThreads;
+      if (e < n) {
+        const int r = e / d;
+        rs[r * ld + (e - r * d)] = buf[k];
+      }
+    }
+  }
+  __syncthreads();
+  if (t < QK) {
+    float acc = 0.0f;
+    if (t < d) {
+      const float* rr = rs + t * ld;
+#pragma unroll 8
+      for (int j = 0; j < d; ++j) acc = __builtin_fmaf(rr[j], qs[j], acc);
+    }
+    y[t] = acc;   // zero past d
+  }
+  __syncthreads();
+  hadamard128(y, t, t < QK);
+  if (t < QK) {
+    const float v = y[t] * kInvSqrtQK;
+    a.qt[row * QK + t] = frame_sign(a, t) ? -v : v;
+  }
+}
+
+// out = R^T (R_w y) = R^T (c H (D y)): the first d elements of the frame's result
+// (the others carry the centroids of the code-0 padding and are zeroed before the
+// product).  Thread i reads column min(i, d - 1) of R, coalesced across the threads,
+// all loads issued at once.
+__global__ void __launch_bounds__(QK) dense_attn_out_kernel(DenseAttnLaunch a) {
+  __shared__ float y[QK];
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x, d = a.dim;
+  const int64_t row = static_cast<int64_t>(b) * a.hq + h;
+  const float* c = a.rot + min(i, d - 1);
+  float rv[QK];
+#pragma unroll
+  for (int k = 0; k < QK; ++k) rv[k] = c[static_cast<int64_t>(min(k, d - 1)) * d];
+  const float v = a.y[row * QK + i];
+  y[i] = frame_sign(a, i) ? -v : v;
+  __syncthreads();
+  hadamard128(y, i, true);
+  y[i] = i < d ? y[i] * kInvSqrtQK : 0.0f;
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < QK; ++k) acc = __builtin_fmaf(rv[k], y[k], acc);
+  if (i < d) a.out[row * d + i] = acc;
+}
+
 int dense_grid(int64_t nvec, int per_wave) {
   const int64_t per = static_cast<int64_t>(kDW) * per_wave;
   const int64_t want = (nvec + per - 1) / per;
@@ -722,6 +843,17 @@ hipError_t launch_dense_encode(const DenseLaunch& a, const KTable& tab, hipStrea
       default: enc_ns<4, true>(a, tab, grid, stream); break;
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_attn_query(const DenseAttnLaunch& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dense_attn_query_kernel, dim3(a.hq, a.batch), dim3(kQueryThreads), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_attn_out(const DenseAttnLaunch& a, hipStream_t stream) {
+  hipLaunchKernelGGL(dense_attn_out_kernel, dim3(a.hq, a.batch), dim3(QK), 0, stream, a);
   return hipGetLastError();
 }
 

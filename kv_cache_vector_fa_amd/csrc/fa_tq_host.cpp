@@ -408,11 +408,12 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
                        const uint16_t* v_norms, const int32_t* seq_lens, const int32_t* pos,
                        int32_t n_new, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int32_t t_max, float scale, float* out, void* workspace,
-                       size_t workspace_bytes, void* stream, bool check_only = false) {
+                       size_t workspace_bytes, void* stream, bool check_only = false,
+                       int32_t cb_dim = fatq::QK) {
   fatq::KTable tk, tv;
-  fa_tq_status st = check_codebook(cb_k, who, false, &tk);
+  fa_tq_status st = check_codebook(cb_k, who, false, &tk, cb_dim);
   if (st != FA_TQ_OK) return st;
-  if ((st = check_codebook(cb_v, who, false, &tv)) != FA_TQ_OK)
+  if ((st = check_codebook(cb_v, who, false, &tv, cb_dim)) != FA_TQ_OK)
     return st;
   if ((st = check_flags(flags, FA_TQ_TWO_SIGNS | FA_TQ_ATTN_VECTOR_ALU, nullptr, who)) !=
       FA_TQ_OK)
@@ -678,6 +679,90 @@ fa_tq_status fa_tq_decode_dense(const fa_tq_codebook* cb, const float* rotation,
   d.out_bf16 = out_dtype == FA_TQ_BF16;
   d.vec = aligned16(out) && d.sb % 4 == 0 && d.sh % 4 == 0 && d.st % 4 == 0;
   return launched(fatq::launch_dense_decode(d, tab, static_cast<hipStream_t>(stream)), who);
+}
+
+// The attention kernels' own frame for attention over a dense-rotation cache: the
+// Walsh-Hadamard rotation of this seed (any seed would do: the frame cancels).
+constexpr uint64_t kDenseFrameSeed = 0;
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t fa_tq_attn_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t t_max) {
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0 ||
+      n_q_heads % n_kv_heads != 0)
+    return 0;
+  const size_t attn = fa_tq_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max, fatq::QK);
+  const size_t frame = align256(static_cast<size_t>(batch) * n_q_heads * fatq::QK * sizeof(float));
+  return 2 * frame + attn;
+}
+
+fa_tq_status fa_tq_attn_decode_dense(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                                     const float* rotation, int32_t head_dim, uint32_t flags,
+                                     const void* q, fa_tq_dtype q_dtype,
+                                     const uint8_t* k_codes, const uint16_t* k_norms,
+                                     const uint8_t* v_codes, const uint16_t* v_norms,
+                                     const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t t_max, float scale, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* who = "fa_tq_attn_decode_dense";
+  fatq::KTable tk, tv;
+  fa_tq_status st = check_dense(cb_k, rotation, head_dim, who, &tk);
+  if (st != FA_TQ_OK) return st;
+  if ((st = check_dense(cb_v, rotation, head_dim, who, &tv)) != FA_TQ_OK) return st;
+  if (head_dim > fatq::kDenseAttnMax)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: head_dim %d (attention over a dense cache takes <= %d)",
+                who, head_dim, fatq::kDenseAttnMax);
+  if ((st = check_flags(flags, FA_TQ_ATTN_VECTOR_ALU, nullptr, who)) != FA_TQ_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || t_max < 0)
+    return fail(FA_TQ_EINVAL, "%s: bad sizes", who);
+  if (q_dtype != FA_TQ_F32 && q_dtype != FA_TQ_BF16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: query dtype %d", who, (int)q_dtype);
+  if (batch == 0) return ok();
+  if (!q || !out || !workspace) return fail(FA_TQ_EINVAL, "%s: NULL device pointer", who);
+  if ((reinterpret_cast<uintptr_t>(q) & (q_dtype == FA_TQ_BF16 ? 1u : 3u)) ||
+      (reinterpret_cast<uintptr_t>(out) & 3u) || !aligned16(workspace))
+    return fail(FA_TQ_EINVAL, "%s: misaligned pointer", who);
+  // the frame's query and result first, then the attention call's own workspace (whose
+  // size, with every other argument, attn_impl checks)
+  const size_t frame = align256(static_cast<size_t>(batch) * n_q_heads * fatq::QK * sizeof(float));
+  if (workspace_bytes < 2 * frame)
+    return fail(FA_TQ_EINVAL, "%s: workspace %zu bytes < %zu", who, workspace_bytes,
+                fa_tq_attn_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, t_max));
+  float* qt = static_cast<float*>(workspace);
+  float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + frame);
+  void* ws = static_cast<char*>(workspace) + 2 * frame;
+  // every check of the attention call itself before anything is launched
+  if ((st = attn_impl(who, cb_k, cb_v, kDenseFrameSeed, flags, fatq::QK, qt, FA_TQ_F32, k_codes,
+                      k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
+                      n_kv_heads, t_max, scale, y, ws, workspace_bytes - 2 * frame, stream,
+                      true, head_dim)) != FA_TQ_OK)
+    return st;
+  fatq::DenseAttnLaunch a;
+  a.q = q;
+  a.q_is_bf16 = q_dtype == FA_TQ_BF16;
+  a.rot = rotation;
+  a.batch = batch;
+  a.hq = n_q_heads;
+  a.dim = head_dim;
+  a.qt = qt;
+  a.y = y;
+  a.out = out;
+  {
+    int8_t sg[fatq::QK];
+    make_signs(kDenseFrameSeed, fatq::QK, sg);
+    for (int w = 0; w < 4; ++w) a.signs[w] = 0;
+    for (int i = 0; i < fatq::QK; ++i)
+      if (sg[i] < 0) a.signs[i >> 5] |= 1u << (i & 31);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launched(fatq::launch_dense_attn_query(a, s), who)) != FA_TQ_OK) return st;
+  if ((st = attn_impl(who, cb_k, cb_v, kDenseFrameSeed, flags, fatq::QK, qt, FA_TQ_F32, k_codes,
+                      k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
+                      n_kv_heads, t_max, scale, y, ws, workspace_bytes - 2 * frame, stream,
+                      false, head_dim)) != FA_TQ_OK)
+    return st;
+  return launched(fatq::launch_dense_attn_out(a, s), who);
 }
 
 int32_t fa_tq_code_bytes(int32_t bits) {

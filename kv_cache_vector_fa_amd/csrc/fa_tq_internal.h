@@ -118,6 +118,25 @@ struct DenseDecodeLaunch {
   int32_t vec;          // out 16-byte aligned, strides multiples of 4 elements: 8/16-byte stores
 };
 
+// Attention over a dense-rotation cache (head_dim <= 128) runs the attention kernels in
+// their own Walsh-Hadamard frame R_w = c H D (D = diag(signs), c = fp32(1/sqrt(128))):
+// the query enters as q~ = R_w^-1 (R q) and the result y leaves as R^T (R_w y).
+constexpr int kDenseAttnMax = QK;
+
+struct DenseAttnLaunch {
+  const void* q;        // [batch][hq][dim], bf16 or fp32
+  int32_t q_is_bf16;
+  const float* rot;     // R, [dim][dim] row-major
+  int32_t batch, hq, dim;
+  float* qt;            // q~, [batch][hq][128] fp32
+  const float* y;       // attention result in the frame, [batch][hq][128] fp32
+  float* out;           // [batch][hq][dim] fp32
+  uint32_t signs[4];    // bit i % 32 of word i / 32: element i of D is -1
+};
+
+hipError_t launch_dense_attn_query(const DenseAttnLaunch& a, hipStream_t stream);
+hipError_t launch_dense_attn_out(const DenseAttnLaunch& a, hipStream_t stream);
+
 hipError_t launch_dense_encode(const DenseLaunch& a, const KTable& tab, hipStream_t stream);
 hipError_t launch_dense_decode(const DenseDecodeLaunch& a, const KTable& tab,
                                hipStream_t stream);

@@ -15,7 +15,7 @@ import workloads
 from oracle import codebook as o_cb
 from oracle import codec
 from oracle import dense
-from tests.gpu_helpers import DECODE_REL_L2, bf16_to_f32, compare_norms, say, FLIP_BUDGET
+from tests.gpu_helpers import ATTN_MAX_ABS, DECODE_REL_L2, bf16_to_f32, compare_norms, say, FLIP_BUDGET
 
 pytestmark = pytest.mark.gpu
 SEED = workloads.ROTATION_SEED
@@ -147,3 +147,78 @@ def test_dense_prefill_slice_sampled(gpu_lib):
     flips = _check_codes(gc, oc, bits, d, "prefill dense")
     compare_norms(gn, on, "prefill dense")
     say(f"prefill dense d=192: {flips} flips in {oc.size} codes")
+
+
+@pytest.mark.parametrize("d", [37, 40, 70, 96, 128])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("flags", [0, "valu"])
+def test_dense_attention(gpu_lib, d, kb, vb, flags):
+    """Attention over oracle-encoded dense caches (ragged lengths, a zero length, GQA
+    groups of 4) against the fp64 definition over the decoded vectors."""
+    torch = _torch()
+    say(f"dense attention d={d} K{kb}V{vb} {flags or 'mfma'}")
+    B, Hq, Hkv, T = 3, 8, 2, 300
+    lens = [300, 0, 129]
+    rng = np.random.default_rng(d * 100 + kb * 10 + vb)
+    k = rng.standard_normal((B, Hkv, T, d)).astype(np.float32)
+    k *= rng.uniform(0.3, 3.0, (1, Hkv, 1, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, T, d)).astype(np.float32)
+    r32 = dense.rotation_f32(SEED, d)
+    bk, ck = o_cb.codebook(kb, d)
+    bv, cv = o_cb.codebook(vb, d)
+    kc, kn, _ = dense.encode_dense(k.reshape(-1, d), r32, bk)
+    vc, vn, _ = dense.encode_dense(v.reshape(-1, d), r32, bv)
+    kc, vc = kc.reshape(B, Hkv, T, d), vc.reshape(B, Hkv, T, d)
+    kn, vn = kn.reshape(B, Hkv, T), vn.reshape(B, Hkv, T)
+    dev = "cuda"
+    kp = torch.from_numpy(dense.pack_dense(kc, kb).reshape(B, Hkv, T, 1, -1)).to(dev)
+    vp = torch.from_numpy(dense.pack_dense(vc, vb).reshape(B, Hkv, T, 1, -1)).to(dev)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(torch.bfloat16)
+    scale = 1 / np.sqrt(d)
+    rot = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).to(dev)
+    out = gpu_lib.attn_decode_dense(
+        gpu_lib.codebook_init(d, kb), gpu_lib.codebook_init(d, vb), rot, q.to(dev), kp,
+        torch.from_numpy(kn.view(np.int16)).to(dev), vp, torch.from_numpy(vn.view(np.int16)).to(dev),
+        torch.tensor(lens, dtype=torch.int32, device=dev), scale,
+        flags=gpu_lib.ATTN_VECTOR_ALU if flags == "valu" else 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = dense.attend_dense(bf16_to_f32(q), kc, kn, vc, vn, lens, r32, ck, cv, scale)
+    assert np.all(got[1] == 0.0)
+    err = float(np.max(np.abs(got - ref)))
+    say(f"dense attention d={d} K{kb}V{vb}: max abs err {err:.3e}")
+    assert err <= ATTN_MAX_ABS
+
+
+def test_dense_attention_graph_replays(gpu_lib):
+    """The dense-attention call (query kernel, attention kernels, output kernel) captured
+    in a HIP graph: every replay, with eager work and synchronizations between them,
+    equals the eager result bit for bit."""
+    torch = _torch()
+    d, B, Hq, Hkv, T = 96, 2, 8, 2, 200
+    dev = "cuda"
+    rng = np.random.default_rng(3)
+    cbk, cbv = gpu_lib.codebook_init(d, 4), gpu_lib.codebook_init(d, 2)
+    rot = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).to(dev)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, T, d)).astype(np.float32)).to(dev)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, T, d)).astype(np.float32)).to(dev)
+    kc, kn = gpu_lib.encode_dense(cbk, rot, k)
+    vc, vn = gpu_lib.encode_dense(cbv, rot, v)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(dev)
+    lens = torch.tensor([200, 77], dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gpu_lib.attn_dense_workspace_bytes(B, Hq, Hkv, T), dtype=torch.uint8,
+                     device=dev)
+    eager = gpu_lib.attn_decode_dense(cbk, cbv, rot, q, kc, kn, vc, vn, lens, 0.1).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call = gpu_lib.attn_decode_dense_call(cbk, cbv, rot, q, kc, kn, vc, vn, lens, 0.1, out, ws)
+        call()
+    for i in range(3):
+        out.fill_(float(i) - 7.0)
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"

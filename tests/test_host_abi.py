@@ -299,6 +299,31 @@ def test_encode_and_decode_binding_reject_bad_buffers(lib):
         fa.decode(cb, 42, codes, norms, 128, out=torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16))
 
 
+def test_dense_attention_rejections_before_launch(lib):
+    """fa_tq_attn_decode_dense refuses before any launch (fake device pointers are never
+    dereferenced)."""
+    fake = ctypes.c_void_p(1 << 20)
+    B, Hq, Hkv, T = 2, 8, 2, 64
+    need = lib.fa_tq_attn_dense_workspace_bytes(B, Hq, Hkv, T)
+    assert need >= 2 * B * Hq * 128 * 4 + fa.attn_workspace_bytes(B, Hq, Hkv, T)
+    assert lib.fa_tq_attn_dense_workspace_bytes(B, 7, 2, T) == 0      # Hq % Hkv != 0
+
+    def call(cbk, cbv, d, flags=0, ws_bytes=need, hq=Hq, rot=fake):
+        return lib.fa_tq_attn_decode_dense(ctypes.byref(cbk), ctypes.byref(cbv), rot, d, flags,
+                                           fake, fa.FA_TQ_BF16, fake, fake, fake, fake, fake, B,
+                                           hq, Hkv, T, 0.1, fake, fake, ws_bytes, None)
+    c96, c96v = fa.codebook_init(96, 4), fa.codebook_init(96, 2)
+    c160 = fa.codebook_init(160, 4)
+    assert call(c160, c160, 160) == fa.FA_TQ_EUNSUPPORTED           # more than one block
+    assert call(fa.codebook_init(128, 4), c96v, 96) == fa.FA_TQ_EINVAL   # codebook dim
+    assert call(c96, c96v, 96, flags=fa.TWO_SIGNS) == fa.FA_TQ_EINVAL
+    assert call(c96, c96v, 96, ws_bytes=need - 256) == fa.FA_TQ_EINVAL
+    assert call(c96, c96v, 96, hq=7) == fa.FA_TQ_EINVAL
+    assert call(c96, fa.codebook_init(96, 8), 96) == fa.FA_TQ_EUNSUPPORTED   # 8-bit grid
+    # the query kernel stages R with 16-byte loads: a 4-byte aligned R is refused
+    assert call(c96, c96v, 96, rot=ctypes.c_void_p((1 << 20) + 4)) == fa.FA_TQ_EINVAL
+
+
 def test_dense_binding_rejects_bad_buffers(lib):
     """The dense-rotation binding checks every tensor before the library sees it (CPU
     tensors: the checks run before the device check)."""

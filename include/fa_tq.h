@@ -270,8 +270,9 @@ fa_tq_status fa_tq_decode_dense(const fa_tq_codebook *cb, const float *rotation,
  *   p = softmax(s);  o' = sum_t p_t n_V[t] c_V[code_V[t]];  out = R^T o'.
  * The coordinates past head_dim (code 0 in the cache) do not enter: q' is zero there and
  * out takes the first head_dim coordinates of o'.  The attention kernels run in their
- * own Walsh-Hadamard frame R_w: the query enters as R_w^-1 (R q) and the result leaves
- * as R^T (R_w y) (two small kernels around them), so accuracy is that of
+ * own Walsh-Hadamard frame R_w: a small kernel maps the query in as R_w^-1 (R q); the
+ * MFMA kernels' merge then writes R^T o' directly, the vector-ALU kernels' result y
+ * leaves through a second small kernel as R^T (R_w y).  Accuracy is that of
  * fa_tq_attn_decode_ex.
  *   cb_k, cb_v: 2-4 bit codebooks of dim head_dim; rotation: as fa_tq_encode_dense;
  *   head_dim in [4, 128] (FA_TQ_EUNSUPPORTED above: the cache then has more than one

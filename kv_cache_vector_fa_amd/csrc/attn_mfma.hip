@@ -924,6 +924,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
 // thread (slice, c) folds float4 column c of splits slice, slice + 8, ... eight at a
 // time with a running maximum (the eight loads of a chunk are all in flight
 // together); the 8 slices are then combined in LDS.
+// DENSE: the codes are those of a dense rotation R (d x d, d <= 128) and the output is
+// R^T o over the first d elements; thread (half, i) sums rows 64 half .. 64 half + 63 of
+// column i of R, loaded before the partials (row and column indexes clamped into R;
+// the rows past d meet zeros of o).
+template <bool DENSE>
 __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, SignWords sw) {
   __shared__ __attribute__((aligned(16))) float po[8][QK];
   __shared__ float pm[8], pl[8];
@@ -934,6 +939,12 @@ __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, Si
   const float* ws_o = static_cast<const float*>(a.workspace);
   const float* ws_ml = ws_o + static_cast<int64_t>(a.batch) * a.hq * ns * QK;
   const int64_t r0 = (static_cast<int64_t>(b) * a.hq + h) * ns;
+  [[maybe_unused]] float rv[DENSE ? 64 : 1];
+  if constexpr (DENSE) {
+    const int d = a.dense_dim, col = min(tid & (QK - 1), d - 1), k0 = (tid >> 7) * 64;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) rv[m] = a.dense_rot[min(k0 + m, d - 1) * d + col];
+  }
   float mx = -INFINITY, den = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   // chunks of 8 splits per thread: all 16 loads issued, then one rescale per chunk
@@ -988,9 +999,21 @@ __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, Si
       }
     }
     ov[tid] = dsum > 0.0f ? num / dsum : 0.0f;
+    if constexpr (DENSE) {
+      if (tid >= a.dense_dim) ov[tid] = 0.0f;
+    }
   }
   __syncthreads();
-  if (tid < 64) {
+  if constexpr (DENSE) {
+    const int d = a.dense_dim, k0 = (tid >> 7) * 64;
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) acc = __builtin_fmaf(rv[m], ov[k0 + m], acc);
+    float* half = &po[0][0];   // rows 0 and 1 of po (their reads ended at the barrier)
+    half[tid] = acc;
+    __syncthreads();
+    if (tid < d) a.out[(static_cast<int64_t>(b) * a.hq + h) * d + tid] = half[tid] + half[tid + QK];
+  } else if (tid < 64) {
     const float2 v = reinterpret_cast<const float2*>(ov)[lane];
     rotate_out(v, sw, lane, a.out + (static_cast<int64_t>(b) * a.hq + h) * QK);
   }
@@ -1065,7 +1088,12 @@ hipError_t launch_attn_mfma(const AttnLaunch& a, const KTable& tk, const KTable&
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_splits_kernel, dim3(a.hq, a.batch), dim3(256), 0, stream, a, sw);
+  if (a.dense_rot)
+    hipLaunchKernelGGL(attn_merge_splits_kernel<true>, dim3(a.hq, a.batch), dim3(256), 0, stream,
+                       a, sw);
+  else
+    hipLaunchKernelGGL(attn_merge_splits_kernel<false>, dim3(a.hq, a.batch), dim3(256), 0,
+                       stream, a, sw);
   return hipGetLastError();
 }
 

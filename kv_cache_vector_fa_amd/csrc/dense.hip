@@ -675,8 +675,9 @@ __global__ void __launch_bounds__(kDT, 1) dense_decode_kernel(DenseDecodeLaunch 
 }
 
 // ---- attention over a dense-rotation cache: the query into the attention kernels'
-// Walsh-Hadamard frame and the result out of it (one workgroup of 128 threads per
-// (sequence, query head); thread i owns element i of the 128-point frame).
+// Walsh-Hadamard frame, and (after the vector-ALU kernels, whose merge leaves the
+// result in that frame) the result out of it.  One workgroup per (sequence, query
+// head); thread i owns element i of the 128-point frame.
 
 __device__ __forceinline__ bool frame_sign(const DenseAttnLaunch& a, int i) {
   return (a.signs[i >> 5] >> (i & 31)) & 1u;
@@ -699,75 +700,67 @@ __device__ __forceinline__ void hadamard128(float* y, int i, bool on) {
 }
 
 // q~ = R_w^-1 (R q) = D H (R q) / (128 c): R q zero-padded to 128, then H, the scale
-// (1 / (128 c) = c up to the rounding of c) and the signs.  The workgroup copies R into
-// LDS with coalesced loads (16-byte ones when d % 4 == 0: the host requires R 16-byte
-// aligned), rows at an odd stride so that thread i < d reads row i without bank
-// conflicts.
+// (1 / (128 c) = c up to the rounding of c) and the signs.  Wave w takes rows 32 w ..
+// 32 w + 31 of R; lane l reads columns l and l + 64 of each (coalesced, all 64 loads in
+// flight together; indexes clamped into R, the columns past d meet zeros of q, the rows
+// past d are dropped), then a halving exchange over the lane bits 5 .. 1 leaves lanes
+// 2r and 2r + 1 with row 32 w + r summed over 32 lanes, and one more exchange over
+// bit 0 completes the sum.
+// One halving step over lane bit 2S: of its 2S row partials v[0 .. 2S), a lane keeps
+// the upper half when that bit is set (else the lower one), sends the other half to
+// its partner and adds what it receives: v[0 .. S) then hold the kept rows summed over
+// both lanes.
+template <int S>
+__device__ __forceinline__ void halve_rows(float* v, int lane) {
+  const bool up = lane & (2 * S);
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const float send = up ? v[j] : v[j + S];
+    const float keep = up ? v[j + S] : v[j];
+    v[j] = keep + __shfl_xor(send, 2 * S);
+  }
+}
+
 constexpr int kQueryThreads = 256;
 __global__ void __launch_bounds__(kQueryThreads) dense_attn_query_kernel(DenseAttnLaunch a) {
-  __shared__ float rs[kDenseAttnMax * (kDenseAttnMax + 1)];
-  __shared__ float qs[kDenseAttnMax];
   __shared__ float y[QK];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, d = a.dim;
-  const int ld = d | 1;
-  const int n = d * d;
+  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform
   const int64_t row = static_cast<int64_t>(b) * a.hq + h;
-  if (t < d) {
-    qs[t] = a.q_is_bf16
-                ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[row * d + t]) << 16)
-                : static_cast<const float*>(a.q)[row * d + t];
-  }
-  if ((d & 3) == 0) {
-    constexpr int kPer = kDenseAttnMax * kDenseAttnMax / 4 / kQueryThreads;
-    const float4* r4 = reinterpret_cast<const float4*>(a.rot);
-    float4 buf[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      buf[k] = r4[min(t + k * kQueryThreads, n / 4 - 1)];   // clamped: inside R
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = 4 * (t + k * kQueryThreads);
-      if (e < n) {
-        const int r = e / d, c = e - r * d;   // c .. c + 3 stay in row r
-        float* dst = rs + r * ld + c;
-        dst[0] = buf[k].x;
-        dst[1] = buf[k].y;
-        dst[2] = buf[k].z;
-        dst[3] = buf[k].w;
-      }
-    }
+  float q0 = 0.0f, q1 = 0.0f;
+  if (a.q_is_bf16) {
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + row * d;
+    if (lane < d) q0 = __uint_as_float(static_cast<uint32_t>(qb[lane]) << 16);
+    if (lane + 64 < d) q1 = __uint_as_float(static_cast<uint32_t>(qb[lane + 64]) << 16);
   } else {
-    constexpr int kPer = kDenseAttnMax * kDenseAttnMax / kQueryThreads;
-    float buf[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      buf[k] = a.rot[min(t + k * kQueryThreads, n - 1)];   // clamped: inside R
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int e = t + k * kQueryThreads;
-      if (e < n) {
-        const int r = e / d;
-        rs[r * ld + (e - r * d)] = buf[k];
-      }
-    }
+    const float* qf = static_cast<const float*>(a.q) + row * d;
+    if (lane < d) q0 = qf[lane];
+    if (lane + 64 < d) q1 = qf[lane + 64];
   }
-  __syncthreads();
-  if (t < QK) {
-    float acc = 0.0f;
-    if (t < d) {
-      const float* rr = rs + t * ld;
-#pragma unroll 8
-      for (int j = 0; j < d; ++j) acc = __builtin_fmaf(rr[j], qs[j], acc);
-    }
-    y[t] = acc;   // zero past d
+  const uint32_t c0 = min(lane, d - 1), c1 = min(lane + 64, d - 1);
+  float r0[32], r1[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float* rr = a.rot + min(32 * w + j, d - 1) * d;
+    r0[j] = rr[c0];
+    r1[j] = rr[c1];
   }
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = __builtin_fmaf(r1[j], q1, r0[j] * q0);
+  halve_rows<16>(v, lane);
+  halve_rows<8>(v, lane);
+  halve_rows<4>(v, lane);
+  halve_rows<2>(v, lane);
+  halve_rows<1>(v, lane);
+  const float sum = v[0] + __shfl_xor(v[0], 1);
+  const int r = 32 * w + (lane >> 1);
+  if ((lane & 1) == 0 && r < QK) y[r] = r < d ? sum : 0.0f;
   __syncthreads();
   hadamard128(y, t, t < QK);
   if (t < QK) {
-    const float v = y[t] * kInvSqrtQK;
-    a.qt[row * QK + t] = frame_sign(a, t) ? -v : v;
+    const float v2 = y[t] * kInvSqrtQK;
+    a.qt[row * QK + t] = frame_sign(a, t) ? -v2 : v2;
   }
 }
 

@@ -400,6 +400,15 @@ fa_tq_status scratch_of_current_device(const char* who, void** out) {
   return ok();
 }
 
+// Attention over a dense-rotation cache: on the MFMA kernels the merge writes
+// out = R^T o (d elements per head) itself and sets written.
+struct DenseOutput {
+  const float* rot;
+  int32_t dim;
+  float* out;
+  bool written;
+};
+
 fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
                        const fa_tq_codebook* cb_v, uint64_t seed, uint32_t flags,
                        int32_t head_dim,
@@ -409,7 +418,7 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
                        int32_t n_new, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int32_t t_max, float scale, float* out, void* workspace,
                        size_t workspace_bytes, void* stream, bool check_only = false,
-                       int32_t cb_dim = fatq::QK) {
+                       int32_t cb_dim = fatq::QK, DenseOutput* dense = nullptr) {
   fatq::KTable tk, tv;
   fa_tq_status st = check_codebook(cb_k, who, false, &tk, cb_dim);
   if (st != FA_TQ_OK) return st;
@@ -474,6 +483,12 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
       return fail(FA_TQ_EUNSUPPORTED, "%s: t_max %d: a cache row spans 2 GiB or more", who,
                   t_max);
     fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+    if (dense) {   // the merge applies R^T and writes the caller's output
+      a.dense_rot = dense->rot;
+      a.dense_dim = dense->dim;
+      a.out = dense->out;
+      dense->written = true;
+    }
     return launched(fatq::launch_attn_mfma(a, tk, tv, sw, static_cast<hipStream_t>(stream)),
                     who);
   }
@@ -757,12 +772,14 @@ fa_tq_status fa_tq_attn_decode_dense(const fa_tq_codebook* cb_k, const fa_tq_cod
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = launched(fatq::launch_dense_attn_query(a, s), who)) != FA_TQ_OK) return st;
+  DenseOutput dense{rotation, head_dim, out, false};
   if ((st = attn_impl(who, cb_k, cb_v, kDenseFrameSeed, flags, fatq::QK, qt, FA_TQ_F32, k_codes,
                       k_norms, v_codes, v_norms, seq_lens, nullptr, 0, batch, n_q_heads,
                       n_kv_heads, t_max, scale, y, ws, workspace_bytes - 2 * frame, stream,
-                      false, head_dim)) != FA_TQ_OK)
+                      false, head_dim, &dense)) != FA_TQ_OK)
     return st;
-  return launched(fatq::launch_dense_attn_out(a, s), who);
+  // the vector-ALU kernels leave the result in the frame: the output kernel maps it back
+  return dense.written ? ok() : launched(fatq::launch_dense_attn_out(a, s), who);
 }
 
 int32_t fa_tq_code_bytes(int32_t bits) {

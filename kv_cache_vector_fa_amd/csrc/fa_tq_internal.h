@@ -158,6 +158,11 @@ struct AttnLaunch {
   float* out;
   void* workspace;
   int32_t n_split, chunk;
+  // MFMA family only: when set, the merge writes out[b][h][0 .. dense_dim) = R^T o with
+  // R = dense_rot (row-major dense_dim x dense_dim) in place of the inverse rotation
+  // (attention over a dense-rotation cache)
+  const float* dense_rot = nullptr;
+  int32_t dense_dim = 0;
 };
 
 // Split-KV partitioning used by both the workspace query and the launch.

@@ -331,8 +331,8 @@ def restore_bf16(fa, w, cbk, seed, caches, reps=64) -> dict:
 def dense_attention(fa, w, seed, k, v, q, lens, lens_np, scale) -> dict:
     """Decode attention over dense-rotation caches of the same layer shape (head_dim
     128, K4/V2): the keys and values encoded with the dense rotation, cloned to copies
-    holding more than 768 MB of attention bytes, calls rotating over them; the query
-    enters and the result leaves the attention kernels' frame through two small kernels
+    holding more than 768 MB of attention bytes, calls rotating over them; a small
+    kernel maps the query into the attention kernels' frame and the merge applies R^T
     (fa_tq_attn_decode_dense)."""
     import torch
     B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim

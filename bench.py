@@ -1,8 +1,9 @@
 """Benchmark of the TurboQuant MSE KV-cache hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input already resident in
-HBM: encode the bf16 K cache (K4), encode the bf16 V cache (V2), then single-query
-decode attention over the packed cache just written.  The workload is the
+HBM: encode the bf16 K cache (K4) and the bf16 V cache (V2) in one call
+(fa_tq_encode_kv: one launch whose workgroups split between the two), then
+single-query decode attention over the packed cache just written.  The workload is the
 Llama-3-8B-shaped layer: 1 x 32768 tokens, 32 query / 8 KV heads, head_dim 128.
 
 Prints one JSON line.  ``value`` = algorithmic bytes of a step / step time (GB/s).
@@ -14,9 +15,8 @@ over 900 MB of traffic) and packed caches over 32 copies (the attention phase cy
 through 840 MB), so no call finds its data in the 256 MB last-level cache.
 
 The K timed steps run in rounds of R steps, phase by phase within a round: R encodes
-of the K cache back to back, then R encodes of the V cache, then R attentions, step
-i's attention reading the cache copy its encodes wrote (every copy holds the same
-codes).  HIP events at the phase boundaries (on the stream the library launches on)
+of K and V back to back, then R attentions, step i's attention reading the cache
+copy its encode wrote (every copy holds the same codes).  HIP events at the phase boundaries (on the stream the library launches on)
 give each kernel's mean launch-to-launch time without the dispatch of a different
 kernel in between, the figure rocprofv3's kernel durations are compared with; the
 rounds spread every kernel over the whole timed region, so a clock change on the
@@ -78,7 +78,8 @@ HBM_PEAK_GBS = 8000.0
 ROUND = 10   # timed steps per round (see the module docstring)
 CSRC = os.path.join(ROOT, "kv_cache_vector_fa_amd", "csrc")
 # kernel name prefix (as rocprofv3 reports it) -> source file that defines it
-KERNEL_SOURCE = {"encode_kernel": "codec.hip", "attn_mfma_kernel": "attn_mfma.hip",
+KERNEL_SOURCE = {"encode_kernel": "codec.hip", "encode_pair_kernel": "codec.hip",
+                 "attn_mfma_kernel": "attn_mfma.hip",
                  "attn_merge_splits_kernel": "attn_mfma.hip", "attn_split_kernel": "attn.hip",
                  "attn_merge_kernel": "attn.hip", "decode_kv_kernel": "codec.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama_layer_pmc_traffic.txt")
@@ -377,6 +378,35 @@ def dense_attention(fa, w, seed, k, v, q, lens, lens_np, scale) -> dict:
     del g, calls
     del caches, kc, kn, vc, vn, ws
     return res
+
+
+def encode_separate(enc_k, enc_v, K, C, nblk, w) -> dict:
+    """The step's encodes as two calls (fa_tq_encode of K, then of V), timed like the
+    step: rounds of R encodes of K, then R of V, over the same copies."""
+    import torch
+    for i in range(4):
+        enc_k[i % C]()
+        enc_v[i % C]()
+    rounds = [(s0, min(K, s0 + ROUND)) for s0 in range(0, K, ROUND)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(rounds) + 1)]
+    torch.cuda.synchronize()
+    for r, (s0, s1) in enumerate(rounds):
+        for j, c in enumerate((enc_k, enc_v)):
+            ev[2 * r + j].record()
+            for i in range(s0, s1):
+                c[i % C]()
+    ev[-1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for j, (name, bits) in enumerate((("encode_k", w.k_bits), ("encode_v", w.v_bits))):
+        us = sum(ev[2 * r + j].elapsed_time(ev[2 * r + j + 1]) for r in range(len(rounds))) \
+            * 1e3 / K
+        nb = enc_bytes(nblk, 256, bits)
+        gbs = nb / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 3), "algorithmic_bytes": nb, "gbps": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    out["sum_us"] = round(out["encode_k"]["us"] + out["encode_v"]["us"], 3)
+    return out
 
 
 def encode_variants(fa, w, cbk, seed, ks, caches, reps=20) -> dict:
@@ -843,24 +873,28 @@ def main():
     scale = 1 / np.sqrt(d)
     # arguments marshalled once per buffer copy: a launch costs one ctypes call
     # step i: input copy i % R, cache copy i % C
-    enc_k = [fa.encode_call(cbk, seed, ks[i % R], caches[i][0], caches[i][1]) for i in range(C)]
-    enc_v = [fa.encode_call(cbv, seed, vs[i % R], caches[i][2], caches[i][3]) for i in range(C)]
+    enc_kv = [fa.encode_kv_call(cbk, cbv, seed, ks[i % R], vs[i % R], *caches[i])
+              for i in range(C)]
     attn = [fa.attn_decode_call(cbk, cbv, seed, q, *caches[i], lens, scale, out, ws)
             for i in range(C)]
-    names = ("encode_k", "encode_v", "attn_decode")
-    calls = (enc_k, enc_v, attn)
+    names = ("encode_kv", "attn_decode")
+    calls = (enc_kv, attn)
+    # the same encodes as two calls (fa_tq_encode of K, then of V), timed beside the step
+    enc_k = [fa.encode_call(cbk, seed, ks[i % R], caches[i][0], caches[i][1]) for i in range(C)]
+    enc_v = [fa.encode_call(cbv, seed, vs[i % R], caches[i][2], caches[i][3]) for i in range(C)]
 
     for i in range(args.warmup):
         for c in calls:
             c[i % C]()
     K = args.steps
     rounds = [(s0, min(K, s0 + ROUND)) for s0 in range(0, K, ROUND)]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * len(rounds) + 1)]
+    P = len(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(P * len(rounds) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r, (s0, s1) in enumerate(rounds):
         for j, c in enumerate(calls):
-            ev[3 * r + j].record()
+            ev[P * r + j].record()
             for i in range(s0, s1):
                 c[i % C]()
     ev[-1].record()
@@ -868,11 +902,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev[0].elapsed_time(ev[-1]) / K
-    kms = [sum(ev[3 * r + j].elapsed_time(ev[3 * r + j + 1]) for r in range(len(rounds))) / K
-           for j in range(3)]
+    kms = [sum(ev[P * r + j].elapsed_time(ev[P * r + j + 1]) for r in range(len(rounds))) / K
+           for j in range(P)]
 
     nblk = B * Hkv * T * (d // 128)
-    nbytes = (enc_bytes(nblk, 256, w.k_bits), enc_bytes(nblk, 256, w.v_bits),
+    nbytes = (enc_bytes(nblk, 256, w.k_bits) + enc_bytes(nblk, 256, w.v_bits),
               attn_bytes(lens_np, Hkv, Hq, w.k_bits, w.v_bits))
     step_bytes = sum(nbytes)
     kern = {}
@@ -880,12 +914,11 @@ def main():
         gbs = nb / (km * 1e-3) / 1e9
         rec = {"us": round(km * 1e3, 3), "algorithmic_bytes": nb, "gbps": round(gbs, 1),
                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        if name.startswith("encode"):
-            rec["vectors_per_s"] = round(nblk / (d // 128) / (km * 1e-3), 1)
+        if name.startswith("encode"):   # key and value vectors
+            rec["vectors_per_s"] = round(2 * nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    kname = {"encode_k": f"encode_kernel<{w.k_bits}, true, false, false, false>",
-             "encode_v": f"encode_kernel<{w.v_bits}, true, false, false, false>"}.get(dom, dom)
+    kname = {"encode_kv": f"encode_pair_kernel<{w.k_bits}, {w.v_bits}, true, false>"}.get(dom, dom)
     traffic = traffic_for(kname)
     roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
@@ -906,7 +939,7 @@ def main():
         "data": "synthetic (seeded; bf16 AR(1) rho 0.9 with lognormal channel scales)",
         "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "tokens": T, "head_dim": d, "k_bits": w.k_bits, "v_bits": w.v_bits,
-                   "step": "encode K + encode V + decode attention", "copies": R,
+                   "step": "encode K and V (one call) + decode attention", "copies": R,
                    "cache_copies": C},
         "step_algorithmic_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
@@ -914,12 +947,14 @@ def main():
         "kernels": kern,
         "roofline": roof,
     }
-    rec["per_call"] = {n: per_call_distribution(c) for n, c in zip(names, calls)}
-    rec["cold_hbm"] = {n: cold_hbm(c) for n, c in zip(names, calls)}
+    rec["encode_separate"] = encode_separate(enc_k, enc_v, K, C, nblk, w)
+    sep = dict(zip(names, calls), encode_k=enc_k, encode_v=enc_v)
+    rec["per_call"] = {n: per_call_distribution(c) for n, c in sep.items()}
+    rec["cold_hbm"] = {n: cold_hbm(c) for n, c in sep.items()}
     rec["attn_decode_graph"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out,
-                                               ws, nbytes[2])
+                                               ws, nbytes[1])
     rec["attn_decode_vector_alu"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale,
-                                                    out, ws, nbytes[2], flags=fa.ATTN_VECTOR_ALU)
+                                                    out, ws, nbytes[1], flags=fa.ATTN_VECTOR_ALU)
     if not args.no_append:
         rec["append_decode"] = append_decode(fa, w, cbk, cbv, seed, q, caches[0], out, ws, scale)
         rec["restore_bf16"] = restore_bf16(fa, w, cbk, seed, caches)

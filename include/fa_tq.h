@@ -174,6 +174,24 @@ fa_tq_status fa_tq_encode_ex(const fa_tq_codebook *cb, uint64_t seed, uint32_t f
                              uint8_t *codes, uint16_t *norms, void *stream);
 
 /*
+ * The keys and the values of the same tokens in one call (one rotation from the seed
+ * for both, [Spec] "Step 1: Random Orthogonal Rotation"; each with its own bit width,
+ * [Spec] "As-Built Notes", K4/V2 by default): codes and norms
+ * equal to fa_tq_encode_ex of k with cb_k and of v with cb_v, bit for bit.  Both
+ * inputs share x_dtype, head_dim, the sizes, t0 and t_max; each has its own layout
+ * and cache.  With 2-4 bit codebooks and no FA_TQ_WHOLE_VECTOR both run in one
+ * launch (workgroups split between them), else as two launches.  Every argument of
+ * both halves is checked before anything is launched; errors as fa_tq_encode_ex.
+ */
+fa_tq_status fa_tq_encode_kv(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
+                             uint64_t seed, uint32_t flags, int32_t head_dim, const void *k,
+                             const void *v, fa_tq_dtype x_dtype, fa_tq_layout k_layout,
+                             fa_tq_layout v_layout, int32_t batch, int32_t n_kv_heads,
+                             int32_t n_tokens, const int32_t *t0, int32_t t_max,
+                             uint8_t *k_codes, uint16_t *k_norms, uint8_t *v_codes,
+                             uint16_t *v_norms, void *stream);
+
+/*
  * Decode ([Spec] "Overview": look up reconstruction values, then rotate back; the
  * exact inverse R^T = D H / sqrt(d)):  x_hat = s * (H (n16 * c[code])) / sqrt(128)
  * per block (bits 8: c[code] = (code - 127.5)/127.5 times the block scale).

@@ -63,6 +63,11 @@ _SIGS = {
                                        ctypes.c_int32, _P, ctypes.c_int, Layout, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
                                        _P]),
+    "fa_tq_encode_kv": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.POINTER(Codebook),
+                                       ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int32, _P, _P,
+                                       ctypes.c_int, Layout, Layout, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                                       _P, _P, _P]),
     "fa_tq_decode_kv": (ctypes.c_int, [ctypes.POINTER(Codebook), ctypes.c_uint64, ctypes.c_uint32,
                                        ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int, Layout,
@@ -454,6 +459,56 @@ def encode_call(cb: Codebook, seed: int, x, codes, norms, t_max: int | None = No
         _check(fn(*args))
         return keep
     return call
+
+
+def encode_kv_call(cb_k: Codebook, cb_v: Codebook, seed: int, k, v, k_codes, k_norms, v_codes,
+                   v_norms, t_max: int | None = None, t0=None, stream=None, flags: int = 0):
+    """``encode_kv`` with its arguments marshalled once (see ``encode_call``)."""
+    import torch
+    lib = load()
+    B, H, T, d = k.shape
+    if tuple(v.shape) != (B, H, T, d) or v.dtype != k.dtype:
+        raise ValueError(f"v: expected {k.dtype} {(B, H, T, d)}, got {v.dtype} {tuple(v.shape)}")
+    if k.stride(3) != 1 or v.stride(3) != 1:
+        raise ValueError("channel stride must be 1")
+    t_max = T if t_max is None else t_max
+    whole = bool(flags & WHOLE_VECTOR)
+    nblk = (whole_length(d) if whole else d) // QK
+    if not whole and d % QK:
+        raise ValueError(f"head_dim {d} is not a multiple of {QK}")
+    for name, cb, c, n in (("k", cb_k, k_codes, k_norms), ("v", cb_v, v_codes, v_norms)):
+        _expect(c, (B, H, t_max, nblk, code_bytes(cb.bits)), torch.uint8, f"{name}_codes")
+        _expect(n, (B, H, t_max, 1 if whole else nblk), torch.int16, f"{name}_norms")
+    if t0 is not None:
+        _expect(t0, (B,), torch.int32, "t0")
+    _same_device(k, v, k_codes, k_norms, v_codes, v_norms, t0)
+    args = (ctypes.byref(cb_k), ctypes.byref(cb_v), ctypes.c_uint64(seed), ctypes.c_uint32(flags),
+            ctypes.c_int32(d), _ptr(k), _ptr(v), ctypes.c_int(_dtype_code(k)),
+            Layout(k.stride(0), k.stride(1), k.stride(2)),
+            Layout(v.stride(0), v.stride(1), v.stride(2)), ctypes.c_int32(B), ctypes.c_int32(H),
+            ctypes.c_int32(T), _ptr(t0), ctypes.c_int32(t_max), _ptr(k_codes), _ptr(k_norms),
+            _ptr(v_codes), _ptr(v_norms), _stream(stream))
+    fn = lib.fa_tq_encode_kv
+    keep = (cb_k, cb_v, k, v, k_codes, k_norms, v_codes, v_norms, t0)
+
+    def call():
+        _check(fn(*args))
+        return keep
+    return call
+
+
+def encode_kv(cb_k: Codebook, cb_v: Codebook, seed: int, k, v, t_max: int | None = None,
+              t0=None, k_cache=None, v_cache=None, stream=None, flags: int = 0):
+    """Encode K and V [B, Hkv, T, d] of the same tokens in one call (fa_tq_encode_kv);
+    returns ((k_codes, k_norms), (v_codes, v_norms)), bit for bit those of ``encode``."""
+    B, H, T, d = k.shape
+    t_max = T if t_max is None else t_max
+    if k_cache is None:
+        k_cache = cache_buffers(B, H, t_max, d, cb_k.bits, k.device, flags)
+    if v_cache is None:
+        v_cache = cache_buffers(B, H, t_max, d, cb_v.bits, v.device, flags)
+    encode_kv_call(cb_k, cb_v, seed, k, v, *k_cache, *v_cache, t_max, t0, stream, flags)()
+    return k_cache, v_cache
 
 
 def attn_decode_call(cb_k: Codebook, cb_v: Codebook, seed: int, q, k_codes, k_norms, v_codes,

@@ -913,13 +913,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
 #define FATQ_ENCODE_WGS 1024
 #endif
 constexpr int64_t kEncodeWGs = FATQ_ENCODE_WGS;
+// the workgroup budget of each half (keys, values) of an encode of both
+#ifndef FATQ_ENCODE_PAIR_WGS
+#define FATQ_ENCODE_PAIR_WGS (FATQ_ENCODE_WGS / 2)
+#endif
+constexpr int64_t kEncodePairWGs = FATQ_ENCODE_PAIR_WGS;
 
-dim3 encode_grid(const EncodeLaunch& a) {
+dim3 encode_grid(const EncodeLaunch& a, int64_t wgs = kEncodeWGs) {
   const int64_t rows = static_cast<int64_t>(a.batch) * a.heads;
   const int64_t per_row = static_cast<int64_t>(a.tokens) * a.nblk;
   const int64_t wg_row = (per_row + kEncThreads / 4 - 1) / (kEncThreads / 4);
   const int64_t gy = rows < 65535 ? rows : 65535;
-  int64_t gx = kEncodeWGs / gy;
+  int64_t gx = wgs / gy;
   if (gx > wg_row) gx = wg_row;
   if (gx < 1) gx = 1;
   int64_t g = kEncThreads / 4, n = a.nblk;   // r = nblk / gcd(quads per WG, nblk)
@@ -985,7 +990,7 @@ hipError_t launch_encode_pair(const EncodeLaunch& ak, const KTable& tk, const En
       ak.nblk != av.nblk || ak.x_is_bf16 != av.x_is_bf16 || ak.dim != QK * ak.nblk ||
       av.dim != QK * av.nblk || tk.bits == 8 || tv.bits == 8)
     return hipErrorInvalidValue;
-  const dim3 g2 = encode_grid(ak), grid(g2.x, g2.y, 2), block(kEncThreads);
+  const dim3 g2 = encode_grid(ak, kEncodePairWGs), grid(g2.x, g2.y, 2), block(kEncThreads);
   EncodeLaunch lk = ak, lv = av;
   lk.t_step = lv.t_step = static_cast<int32_t>(grid.x * (kEncThreads / 4) / ak.nblk);
 #define FATQ_PAIR(K, V, F, N) \

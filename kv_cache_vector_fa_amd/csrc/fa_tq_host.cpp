@@ -850,6 +850,50 @@ fa_tq_status fa_tq_encode_ex(const fa_tq_codebook* cb, uint64_t seed, uint32_t f
                      batch, n_kv_heads, n_tokens, t0, t_max, codes, norms, stream, false);
 }
 
+fa_tq_status fa_tq_encode_kv(const fa_tq_codebook* cb_k, const fa_tq_codebook* cb_v,
+                             uint64_t seed, uint32_t flags, int32_t head_dim, const void* k,
+                             const void* v, fa_tq_dtype x_dtype, fa_tq_layout k_layout,
+                             fa_tq_layout v_layout, int32_t batch, int32_t n_kv_heads,
+                             int32_t n_tokens, const int32_t* t0, int32_t t_max,
+                             uint8_t* k_codes, uint16_t* k_norms, uint8_t* v_codes,
+                             uint16_t* v_norms, void* stream) {
+  static const char* who = "fa_tq_encode_kv";
+  // both halves are checked before anything is launched
+  fa_tq_status st;
+  for (int half = 0; half < 2; ++half) {
+    if ((st = encode_impl(who, half ? cb_v : cb_k, seed, flags, head_dim, half ? v : k, x_dtype,
+                          half ? v_layout : k_layout, batch, n_kv_heads, n_tokens, t0, t_max,
+                          half ? v_codes : k_codes, half ? v_norms : k_norms, stream, false,
+                          true)) != FA_TQ_OK)
+      return st;
+  }
+  if (batch == 0 || n_kv_heads == 0 || n_tokens == 0) return ok();
+  if ((flags & FA_TQ_WHOLE_VECTOR) || cb_k->bits == 8 || cb_v->bits == 8) {
+    // the pair kernel takes the blocked 2-4 bit encodes: two launches otherwise
+    for (int half = 0; half < 2; ++half) {
+      if ((st = encode_impl(who, half ? cb_v : cb_k, seed, flags, head_dim, half ? v : k,
+                            x_dtype, half ? v_layout : k_layout, batch, n_kv_heads, n_tokens,
+                            t0, t_max, half ? v_codes : k_codes, half ? v_norms : k_norms,
+                            stream, false)) != FA_TQ_OK)
+        return st;
+    }
+    return ok();
+  }
+  fatq::EncodeLaunch ak, av;
+  fatq::KTable tk, tv;
+  fatq::SignWords sw;
+  if ((st = encode_impl(who, cb_k, seed, flags, head_dim, k, x_dtype, k_layout, batch, n_kv_heads,
+                        n_tokens, t0, t_max, k_codes, k_norms, stream, false, false, &ak, &tk,
+                        &sw)) != FA_TQ_OK ||
+      (st = encode_impl(who, cb_v, seed, flags, head_dim, v, x_dtype, v_layout, batch, n_kv_heads,
+                        n_tokens, t0, t_max, v_codes, v_norms, stream, false, false, &av, &tv,
+                        &sw)) != FA_TQ_OK)
+    return st;
+  return launched(fatq::launch_encode_pair(ak, tk, av, tv, sw, (flags & FA_TQ_NORM_CORRECT) != 0,
+                                           static_cast<hipStream_t>(stream)),
+                  who);
+}
+
 fa_tq_status fa_tq_decode(const fa_tq_codebook* cb, uint64_t seed, int32_t head_dim,
                           const uint8_t* codes, const uint16_t* norms, int64_t n_vec,
                           float* out, void* stream) {

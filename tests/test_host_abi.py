@@ -116,6 +116,52 @@ def test_encode_validation_before_launch(lib):
     assert "levels" in lib.fa_tq_last_error().decode()
 
 
+def _encode_kv_raw(lib, ck, cv, flags=0, k=1 << 20, v=1 << 20, B=1, T=1, t_max=1,
+                   kcodes=1 << 20, vnorms=1 << 20, head_dim=128):
+    P = ctypes.c_void_p
+    lay = fa.Layout(256, 256, 256)
+    return lib.fa_tq_encode_kv(ctypes.byref(ck), ctypes.byref(cv), 42, flags, head_dim, P(k),
+                               P(v), fa.FA_TQ_BF16, lay, lay, B, 1, T, None, t_max, P(kcodes),
+                               P(1 << 20), P(1 << 20), P(vnorms), None)
+
+
+def test_encode_kv_validation_before_launch(lib):
+    """fa_tq_encode_kv checks both halves before anything is launched (no device is
+    needed): a bad value codebook, a misaligned V input, an odd V norms pointer, a NULL
+    K cache, too many tokens, unknown flags; empty work is an OK no-op."""
+    c4, c2 = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    A = 1 << 20
+    bad = fa.codebook_init(128, 2)
+    bad.boundaries[1] = bad.boundaries[0]
+    assert _encode_kv_raw(lib, c4, bad) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, v=A + 4) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, vnorms=A + 1) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, kcodes=0) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, T=5, t_max=4) == fa.FA_TQ_EINVAL
+    assert "fa_tq_encode_kv" in lib.fa_tq_last_error().decode()
+    assert _encode_kv_raw(lib, c4, c2, flags=8) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, head_dim=100) == fa.FA_TQ_EINVAL
+    assert _encode_kv_raw(lib, c4, c2, B=0) == fa.FA_TQ_OK
+    assert _encode_kv_raw(lib, c4, c2, T=0) == fa.FA_TQ_OK
+
+
+def test_encode_kv_binding_rejects_mismatched_inputs(lib):
+    """The binding refuses V of another shape or dtype than K, and caches of the wrong
+    shape (CPU tensors: the checks run before the device check)."""
+    import torch
+    cbk, cbv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    k = torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16)
+    kc = fa.cache_buffers(1, 2, 8, 128, 4, "cpu")
+    vc = fa.cache_buffers(1, 2, 8, 128, 2, "cpu")
+    with pytest.raises(ValueError):
+        fa.encode_kv_call(cbk, cbv, 42, k, torch.zeros((1, 2, 9, 128), dtype=torch.bfloat16),
+                          *kc, *vc)
+    with pytest.raises(ValueError):
+        fa.encode_kv_call(cbk, cbv, 42, k, k.float(), *kc, *vc)
+    with pytest.raises(ValueError):   # the V cache sized for 4-bit codes
+        fa.encode_kv_call(cbk, cbv, 42, k, k.clone(), *kc, *kc)
+
+
 def _attn_raw(lib, ck, cv, hd, B, Hq, Hkv, T, ws_bytes, ptr=1 << 20):
     P = ctypes.c_void_p(ptr)
     return lib.fa_tq_attn_decode(ctypes.byref(ck), ctypes.byref(cv), 42, hd, P, 1, P, P, P, P,

@@ -190,6 +190,47 @@ def test_dense_attention(gpu_lib, d, kb, vb, flags):
     assert err <= ATTN_MAX_ABS
 
 
+def test_dense_attention_llama_full(gpu_lib):
+    """Attention over dense-rotation caches at the llama layer's full size, in the launch
+    the benchmark times (1 x 32 query / 8 KV heads x 32768 tokens, head_dim 128, K4/V2,
+    MFMA kernels): the GPU encodes the caches; for KV heads 0 and 5 (query heads 0-3
+    and 20-23) the output equals the fp64 definition over those caches' decoded
+    vectors."""
+    torch = _torch()
+    w = workloads.WORKLOADS["llama_layer"]
+    B, Hq, Hkv, T, d = w.batch, w.n_q_heads, w.n_kv_heads, w.tokens, w.head_dim
+    say("dense attention llama full")
+    k, v = workloads.make_kv(w, "cuda")
+    q = workloads.make_q(w, "cuda")
+    lens_np = workloads.make_seq_lens(w)
+    lens = torch.from_numpy(lens_np).cuda()
+    scale = 1 / np.sqrt(d)
+    cbk, cbv = gpu_lib.codebook_init(d, w.k_bits), gpu_lib.codebook_init(d, w.v_bits)
+    rot = torch.from_numpy(gpu_lib.rotation_dense(SEED, d)).cuda()
+    kc, kn = gpu_lib.encode_dense(cbk, rot, k)
+    vc, vn = gpu_lib.encode_dense(cbv, rot, v)
+    del k, v
+    out = gpu_lib.attn_decode_dense(cbk, cbv, rot, q, kc, kn, vc, vn, lens, scale)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    heads = [0, 5]
+    qh = [h for g in heads for h in range(g * G, (g + 1) * G)]
+    sel = torch.tensor(heads, device="cuda")
+    kcodes = codec.unpack(kc.index_select(1, sel).cpu().numpy(), w.k_bits)[..., :d]
+    vcodes = codec.unpack(vc.index_select(1, sel).cpu().numpy(), w.v_bits)[..., :d]
+    knorm = kn.index_select(1, sel).cpu().numpy().view(np.float16)
+    vnorm = vn.index_select(1, sel).cpu().numpy().view(np.float16)
+    _, ck = o_cb.codebook(w.k_bits, d)
+    _, cv = o_cb.codebook(w.v_bits, d)
+    qs = bf16_to_f32(q[:, qh])
+    ref = dense.attend_dense(qs, kcodes, knorm, vcodes, vnorm, lens_np,
+                             dense.rotation_f32(SEED, d), ck, cv, scale)
+    got = out[:, qh].cpu().numpy()
+    err = float(np.max(np.abs(got - ref)))
+    say(f"dense attention llama full (KV heads {heads}): max abs err {err:.3e}")
+    assert err <= ATTN_MAX_ABS
+
+
 def test_dense_attention_graph_replays(gpu_lib):
     """The dense-attention call (query kernel, attention kernels, output kernel) captured
     in a HIP graph: every replay, with eager work and synchronizations between them,

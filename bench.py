@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--cache-copies", type=int, default=32, help="packed-cache copies rotated")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-append", action="store_true", help="skip the append_decode figure")
+    p.add_argument("--no-cold-hbm", action="store_true",
+                   help="skip the cold-HBM pass (profiled runs: kernel averages of steady-state "
+                        "calls only)")
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--summarize-rocprof", metavar="DIR")
     p.add_argument("--cpu-baseline-only", action="store_true")
@@ -918,7 +921,8 @@ def main():
             rec["vectors_per_s"] = round(2 * nblk / (d // 128) / (km * 1e-3), 1)
         kern[name] = rec
     dom = max(kern, key=lambda n: kern[n]["us"])
-    kname = {"encode_kv": f"encode_pair_kernel<{w.k_bits}, {w.v_bits}, true, false>"}.get(dom, dom)
+    kname = {"encode_kv": f"encode_pair_kernel<{w.k_bits}, {w.v_bits}, true, false, false>"}.get(
+        dom, dom)
     traffic = traffic_for(kname)
     roof = {"kernel": kname, "bound": "hbm", "achieved": kern[dom]["gbps"],
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
@@ -950,7 +954,8 @@ def main():
     rec["encode_separate"] = encode_separate(enc_k, enc_v, K, C, nblk, w)
     sep = dict(zip(names, calls), encode_k=enc_k, encode_v=enc_v)
     rec["per_call"] = {n: per_call_distribution(c) for n, c in sep.items()}
-    rec["cold_hbm"] = {n: cold_hbm(c) for n, c in sep.items()}
+    if not args.no_cold_hbm:
+        rec["cold_hbm"] = {n: cold_hbm(c) for n, c in sep.items()}
     rec["attn_decode_graph"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out,
                                                ws, nbytes[1])
     rec["attn_decode_vector_alu"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale,

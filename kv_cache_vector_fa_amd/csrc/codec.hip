@@ -613,9 +613,11 @@ __global__ void __launch_bounds__(kEncThreads) encode_kernel(EncodeLaunch a, KTa
   encode_body<BITS, BF16, NC, WV, PAD>(a, tab, sw);
 }
 
-// The keys and the values of one append in one launch (the same grid over the same
-// shape): blockIdx.z = 0 encodes the keys, 1 the values.
-template <int KB, int VB, bool BF16, bool NC>
+// The keys and the values of the same tokens in one launch (the same grid over the same
+// shape): blockIdx.z = 0 encodes the keys, 1 the values.  APPEND only names the
+// instantiation, so that the few-token encodes of an append and the joint encodes of
+// whole caches show apart in kernel statistics.
+template <int KB, int VB, bool BF16, bool NC, bool APPEND>
 __global__ void __launch_bounds__(kEncThreads) encode_pair_kernel(EncodeLaunch ak, KTable tk,
                                                                EncodeLaunch av, KTable tv,
                                                                SignWords sw) {
@@ -985,7 +987,7 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
 
 hipError_t launch_encode_pair(const EncodeLaunch& ak, const KTable& tk, const EncodeLaunch& av,
                               const KTable& tv, const SignWords& sw, bool norm_correct,
-                              hipStream_t stream) {
+                              bool append, hipStream_t stream) {
   if (ak.batch != av.batch || ak.heads != av.heads || ak.tokens != av.tokens ||
       ak.nblk != av.nblk || ak.x_is_bf16 != av.x_is_bf16 || ak.dim != QK * ak.nblk ||
       av.dim != QK * av.nblk || tk.bits == 8 || tv.bits == 8)
@@ -993,8 +995,10 @@ hipError_t launch_encode_pair(const EncodeLaunch& ak, const KTable& tk, const En
   const dim3 g2 = encode_grid(ak, kEncodePairWGs), grid(g2.x, g2.y, 2), block(kEncThreads);
   EncodeLaunch lk = ak, lv = av;
   lk.t_step = lv.t_step = static_cast<int32_t>(grid.x * (kEncThreads / 4) / ak.nblk);
-#define FATQ_PAIR(K, V, F, N) \
-  hipLaunchKernelGGL((encode_pair_kernel<K, V, F, N>), grid, block, 0, stream, lk, tk, lv, tv, sw)
+#define FATQ_PAIR(K, V, F, N)                                                              \
+  hipLaunchKernelGGL((append ? encode_pair_kernel<K, V, F, N, true>                        \
+                             : encode_pair_kernel<K, V, F, N, false>),                     \
+                     grid, block, 0, stream, lk, tk, lv, tv, sw)
 #define FATQ_PAIR_V(K, F, N)                     \
   switch (tv.bits) {                             \
     case 2: FATQ_PAIR(K, 2, F, N); break;        \

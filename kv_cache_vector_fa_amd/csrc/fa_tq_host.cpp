@@ -890,7 +890,7 @@ fa_tq_status fa_tq_encode_kv(const fa_tq_codebook* cb_k, const fa_tq_codebook* c
                         &sw)) != FA_TQ_OK)
     return st;
   return launched(fatq::launch_encode_pair(ak, tk, av, tv, sw, (flags & FA_TQ_NORM_CORRECT) != 0,
-                                           static_cast<hipStream_t>(stream)),
+                                           false, static_cast<hipStream_t>(stream)),
                   who);
 }
 
@@ -1107,7 +1107,7 @@ fa_tq_status fa_tq_attn_append_ex(const fa_tq_codebook* cb_k, const fa_tq_codebo
       return st;
     if (!check_only &&
         (st = launched(fatq::launch_encode_pair(ak, tk, av, tv, sw,
-                                                (flags & FA_TQ_NORM_CORRECT) != 0,
+                                                (flags & FA_TQ_NORM_CORRECT) != 0, true,
                                                 static_cast<hipStream_t>(stream)),
                        who)) != FA_TQ_OK)
       return st;

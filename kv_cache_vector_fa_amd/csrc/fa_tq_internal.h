@@ -68,7 +68,7 @@ hipError_t launch_encode(const EncodeLaunch& a, const KTable& tab, const SignWor
 // one launch.
 hipError_t launch_encode_pair(const EncodeLaunch& ak, const KTable& tk, const EncodeLaunch& av,
                               const KTable& tv, const SignWords& sw, bool norm_correct,
-                              hipStream_t stream);
+                              bool append, hipStream_t stream);
 // Decode of tokens [0, tokens) of `rows` cache rows of t_max slots each (row =
 // b * heads + h) into out[b][h][t][:] at element strides (sb, sh, st).
 struct DecodeLaunch {

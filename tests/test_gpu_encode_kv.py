@@ -171,3 +171,32 @@ def test_encode_kv_llama_layer_full(gpu_lib):
         oc, on = _oracle_encode(bf16_to_f32(xs), bits, SEED)
         compare_codes(gc, oc.reshape(-1, 128), bits, f"llama encode_kv {bits}")
         compare_norms(gn, on, f"llama encode_kv {bits}")
+
+
+def test_encode_kv_graph_replays(gpu_lib):
+    """The joint encode captured in a HIP graph: every replay, with eager work and
+    synchronizations between them and the caches overwritten before each, equals the
+    eager result bit for bit."""
+    torch = _torch()
+    say("encode_kv graph replays")
+    B, H, T, d = 2, 4, 700, 128
+    g = torch.Generator(device="cuda").manual_seed(21)
+    k = torch.randn((B, H, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    cbk, cbv = gpu_lib.codebook_init(128, 4), gpu_lib.codebook_init(128, 2)
+    ek, ev = gpu_lib.encode_kv(cbk, cbv, SEED, k, v)
+    kc = gpu_lib.cache_buffers(B, H, T, d, 4, "cuda")
+    vc = gpu_lib.cache_buffers(B, H, T, d, 2, "cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call = gpu_lib.encode_kv_call(cbk, cbv, SEED, k, v, *kc, *vc)
+        call()
+    for i in range(3):
+        for t in (*kc, *vc):
+            t.fill_(i + 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same(kc, ek, f"keys, replay {i}")
+        _same(vc, ev, f"values, replay {i}")

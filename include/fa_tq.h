@@ -75,10 +75,10 @@ typedef enum { FA_TQ_F32 = 0, FA_TQ_BF16 = 1 } fa_tq_dtype;
  *     summed over index bits 0, 1, ... in order, the padding adding zeros;
  *     butterflies in stage order 1 .. d'/2, c = fp32(1/sqrt(d'))).
  *   FA_TQ_ATTN_VECTOR_ALU (fa_tq_attn_decode_ex and fa_tq_attn_decode_noalloc only):
- *     run the vector-ALU attention kernels (the ones used when n_q_heads / n_kv_heads
- *     is above 8) for any group size instead of the matrix-core kernels, e.g. to
- *     compare the two; the result is the same computation ([Spec] "Optimization:
- *     Fused dequant-dot") under the same accuracy bound.
+ *     run the vector-ALU attention kernels instead of the matrix-core kernels (group
+ *     sizes n_q_heads / n_kv_heads up to 16), e.g. to compare the two; the result is
+ *     the same computation ([Spec] "Optimization: Fused dequant-dot") under the same
+ *     accuracy bound.
  * Entry points without _ex use flags 0.
  */
 #define FA_TQ_TWO_SIGNS 1u
@@ -327,8 +327,12 @@ fa_tq_status fa_tq_attn_decode_dense(const fa_tq_codebook *cb_k, const fa_tq_cod
  *   holds per-split partial results (m, l and the unnormalized rotated output per
  *   split of the sequence); its contents on entry do not matter.  Calls that run
  *   concurrently must not share a workspace; calls in order on one stream may.
- * The library supports head_dim == 128, key/value bits in {2, 3, 4} and
- * n_q_heads / n_kv_heads <= 16, and t_max < 33554432 (one cache row below 2 GiB).
+ * The library supports head_dim == 128, key/value bits in {2, 3, 4}, any group size
+ * n_q_heads / n_kv_heads (the matrix-core kernels take up to 8 query heads per
+ * workgroup: a larger group of G heads is split over the smallest r dividing G with
+ * G / r <= 8 workgroups per KV head, each reading that KV head's codes, e.g. r = 2
+ * for G = 16 and 4 for G = 32; the vector-ALU kernels take G <= 16), and
+ * t_max < 33554432 (one cache row below 2 GiB).
  */
 fa_tq_status fa_tq_attn_decode(const fa_tq_codebook *cb_k, const fa_tq_codebook *cb_v,
                                uint64_t seed, int32_t head_dim,

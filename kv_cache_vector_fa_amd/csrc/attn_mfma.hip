@@ -439,8 +439,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile indices
   const int n = lane & 15, qq = lane >> 4;
+  // g: the group of G query heads g * G .. g * G + G - 1, all of KV head g / kv_div
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = GT > 0 ? GT : a.hq / a.hkv;
+  const int G = GT > 0 ? GT : a.hq / (a.hkv * a.kv_div);
   // lanes of column h < G carry hi(q'_h) and row h of the weights (hi), lanes of
   // column 15 - h the lo halves; the other columns are zero (scores) or unused rows
   const bool hi_lane = n < G;
@@ -452,7 +453,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KT
   const int len_raw = a.lens[b];
   const int c0 = split * a.chunk;
   const int ce = min(a.t_max, c0 + a.chunk);
-  const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g) * a.t_max;
+  const int64_t kvb = (static_cast<int64_t>(b) * a.hkv + g / a.kv_div) * a.t_max;
   Rows rows = make_rows<KB, VB>(a, kvb, ce > 0 ? ce : 0, lane);
   // The query: wave w < G rotates head w, lane holding elements lane and lane + 64
   // (raw bits, widened later); one load form for both dtypes (no branch on the dtype
@@ -1021,7 +1022,14 @@ __global__ void __launch_bounds__(256) attn_merge_splits_kernel(AttnLaunch a, Si
 
 }  // namespace
 
-bool attn_mfma_supported(int32_t hq, int32_t hkv) { return hq / hkv <= kMaxG; }
+// Workgroups per KV head: the smallest r dividing the group size hq / hkv with at most
+// kMaxG query heads per workgroup (each of the r reads the KV head's codes).
+int32_t attn_mfma_groups(int32_t hq, int32_t hkv) {
+  const int32_t G = hq / hkv;
+  int32_t r = (G + kMaxG - 1) / kMaxG;
+  while (G % r != 0) ++r;
+  return r;
+}
 
 // Splits per (sequence, KV head) so that the grid holds about FATQ_ATTN_WANT_WG
 // workgroups (one per compute unit), each chunk a multiple of a round of super tiles
@@ -1050,7 +1058,7 @@ size_t attn_mfma_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t
 template <int GT>
 void launch_g(const AttnLaunch& a, const KTable& tk, const KTable& tv, const SignWords& sw,
               hipStream_t stream, bool same) {
-  const dim3 g1(a.n_split, a.hkv, a.batch), b1(kThreads);
+  const dim3 g1(a.n_split, a.hkv * a.kv_div, a.batch), b1(kThreads);
 #define FATQ_ATT(K, V) \
   hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT>), g1, b1, 0, stream, a, tk, tv, sw)
 #define FATQ_ATS(K) \
@@ -1079,7 +1087,7 @@ hipError_t launch_attn_mfma(const AttnLaunch& a, const KTable& tk, const KTable&
                             const SignWords& sw, hipStream_t stream) {
   bool same = tk.bits == tv.bits && tv.bits != 2;
   for (int i = 0; same && i < (1 << tk.bits); ++i) same = tk.c[i] == tv.c[i];
-  switch (a.hq / a.hkv) {
+  switch (a.hq / (a.hkv * a.kv_div)) {
     case 1: launch_g<1>(a, tk, tv, sw, stream, same); break;
     case 2: launch_g<2>(a, tk, tv, sw, stream, same); break;
     case 4: launch_g<4>(a, tk, tv, sw, stream, same); break;

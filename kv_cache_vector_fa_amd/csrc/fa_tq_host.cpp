@@ -436,8 +436,8 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   if (n_q_heads % n_kv_heads != 0)
     return fail(FA_TQ_EINVAL, "%s: n_q_heads %d not a multiple of n_kv_heads %d", who,
                 n_q_heads, n_kv_heads);
-  if (n_q_heads / n_kv_heads > 16)
-    return fail(FA_TQ_EUNSUPPORTED, "%s: group size %d > 16", who,
+  if ((flags & FA_TQ_ATTN_VECTOR_ALU) && n_q_heads / n_kv_heads > 16)
+    return fail(FA_TQ_EUNSUPPORTED, "%s: group size %d > 16 on the vector-ALU kernels", who,
                 n_q_heads / n_kv_heads);
   if (q_dtype != FA_TQ_F32 && q_dtype != FA_TQ_BF16)
     return fail(FA_TQ_EUNSUPPORTED, "%s: query dtype %d", who, (int)q_dtype);
@@ -477,12 +477,13 @@ fa_tq_status attn_impl(const char* who, const fa_tq_codebook* cb_k,
   a.out = out;
   a.workspace = workspace;
   const fatq::SignWords sw = make_sign_words(seed, head_dim, flags & FA_TQ_TWO_SIGNS);
-  if (!(flags & FA_TQ_ATTN_VECTOR_ALU) && fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
+  if (!(flags & FA_TQ_ATTN_VECTOR_ALU)) {
     // the MFMA kernels address one (batch, KV head) row of codes with 32-bit offsets
     if (static_cast<int64_t>(t_max) * 64 >= (int64_t{1} << 31))
       return fail(FA_TQ_EUNSUPPORTED, "%s: t_max %d: a cache row spans 2 GiB or more", who,
                   t_max);
-    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &a.n_split, &a.chunk);
+    a.kv_div = fatq::attn_mfma_groups(n_q_heads, n_kv_heads);
+    fatq::attn_mfma_partition(batch, n_kv_heads * a.kv_div, t_max, &a.n_split, &a.chunk);
     if (dense) {   // the merge applies R^T and writes the caller's output
       a.dense_rot = dense->rot;
       a.dense_dim = dense->dim;
@@ -825,10 +826,9 @@ size_t fa_tq_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv
   int32_t n_split = 1, chunk = 0;
   fatq::attn_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
   size_t need = fatq::attn_workspace_bytes(batch, n_q_heads, n_split);
-  if (fatq::attn_mfma_supported(n_q_heads, n_kv_heads)) {
-    fatq::attn_mfma_partition(batch, n_kv_heads, t_max, &n_split, &chunk);
-    need = std::max(need, fatq::attn_mfma_workspace_bytes(batch, n_q_heads, n_kv_heads, n_split));
-  }
+  const int32_t r = fatq::attn_mfma_groups(n_q_heads, n_kv_heads);
+  fatq::attn_mfma_partition(batch, n_kv_heads * r, t_max, &n_split, &chunk);
+  need = std::max(need, fatq::attn_mfma_workspace_bytes(batch, n_q_heads, n_kv_heads, n_split));
   return need;
 }
 

@@ -158,6 +158,8 @@ struct AttnLaunch {
   float* out;
   void* workspace;
   int32_t n_split, chunk;
+  // MFMA family only: workgroups per KV head, each taking hq / (hkv * kv_div) query heads
+  int32_t kv_div = 1;
   // MFMA family only: when set, the merge writes out[b][h][0 .. dense_dim) = R^T o with
   // R = dense_rot (row-major dense_dim x dense_dim) in place of the inverse rotation
   // (attention over a dense-rotation cache)
@@ -173,8 +175,9 @@ size_t attn_workspace_bytes(int32_t batch, int32_t hq, int32_t n_split);
 hipError_t launch_attn(const AttnLaunch& a, const KTable& tk, const KTable& tv,
                        const SignWords& sw, hipStream_t stream);
 
-// MFMA path (query groups of up to 8 heads per KV head).
-bool attn_mfma_supported(int32_t hq, int32_t hkv);
+// MFMA path: up to 8 query heads per workgroup; a larger group of a KV head is split
+// over attn_mfma_groups(hq, hkv) workgroups (the partition then counts hkv times that).
+int32_t attn_mfma_groups(int32_t hq, int32_t hkv);
 void attn_mfma_partition(int32_t batch, int32_t hkv, int32_t t_max, int32_t* n_split,
                          int32_t* chunk);
 size_t attn_mfma_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t n_split);

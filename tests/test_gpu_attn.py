@@ -113,7 +113,11 @@ def test_attn_tiny_workload(gpu_lib):
     (2, 5, 1, 129, [129, 77]),
     (1, 12, 4, 257, [257]),       # groups of 3
     (2, 14, 2, 300, [31, 300]),   # groups of 7
-    (1, 24, 2, 200, [199]),       # groups of 12: the vector-ALU kernels
+    (1, 24, 2, 200, [199]),       # groups of 12: two workgroups of 6 per KV head
+    (2, 32, 2, 400, [400, 123]),  # groups of 16: two workgroups of 8
+    (2, 32, 1, 300, [300, 57]),   # one KV head (groups of 32): four workgroups of 8
+    (1, 64, 1, 200, [200]),       # groups of 64: eight workgroups of 8
+    (1, 22, 2, 150, [150]),       # groups of 11: eleven workgroups of 1
 ])
 def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
     torch = _torch()
@@ -128,10 +132,11 @@ def test_attn_ragged(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
 
 
 @pytest.mark.parametrize("kb,vb", [(4, 2), (3, 3), (4, 4)])
-@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [(2, 32, 8, 1500, [1500, 901]), (1, 4, 4, 300, [257])])
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [(2, 32, 8, 1500, [1500, 901]), (1, 4, 4, 300, [257]),
+                                             (1, 24, 2, 200, [199]), (2, 32, 2, 300, [300, 41])])
 def test_attn_vector_alu_kernels(gpu_lib, kb, vb, B, Hq, Hkv, T, lens):
-    """FA_TQ_ATTN_VECTOR_ALU: the vector-ALU kernels at group sizes the matrix-core
-    kernels also take, against the same oracle."""
+    """FA_TQ_ATTN_VECTOR_ALU: the vector-ALU kernels (group sizes up to 16) against the
+    same oracle."""
     torch = _torch()
     say(f"attn vector-ALU K{kb}V{vb} B={B} Hq={Hq} Hkv={Hkv} T={T} lens={lens}")
     rng = np.random.default_rng(kb * 100 + vb + T)

@@ -173,7 +173,15 @@ def test_attn_validation_before_launch(lib):
     big = 1 << 40
     assert _attn_raw(lib, ck, cv, 128, 1, 30, 8, 64, big) == fa.FA_TQ_EINVAL
     assert _attn_raw(lib, ck, cv, 256, 1, 32, 8, 64, big) == fa.FA_TQ_EUNSUPPORTED
-    assert _attn_raw(lib, ck, cv, 128, 1, 64, 2, 64, big) == fa.FA_TQ_EUNSUPPORTED
+    # group size 32: the matrix-core kernels take it (split over workgroups), the
+    # vector-ALU kernels do not
+    P = ctypes.c_void_p(1 << 20)
+    assert lib.fa_tq_attn_decode_ex(ctypes.byref(ck), ctypes.byref(cv), 42, fa.ATTN_VECTOR_ALU,
+                                    128, P, 1, P, P, P, P, P, 1, 64, 2, 64, 0.0884, P, P, big,
+                                    None) == fa.FA_TQ_EUNSUPPORTED
+    assert "vector-ALU" in lib.fa_tq_last_error().decode()
+    assert fa.attn_workspace_bytes(1, 64, 2, 64) > 0
+    assert fa.attn_workspace_bytes(2, 64, 1, 1000) >= 2 * 64 * 130 * 4
     assert _attn_raw(lib, ck, cv, 128, 1, 32, 8, 64, 16) == fa.FA_TQ_EINVAL   # workspace
     assert _attn_raw(lib, ck, cv, 128, 1, 32, 8, 64, big, ptr=(1 << 20) + 8) == fa.FA_TQ_EINVAL
     c8 = fa.codebook_init(128, 8)

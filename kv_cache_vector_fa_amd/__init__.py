@@ -119,7 +119,7 @@ for _name in ("fa_tq_attn_decode", "fa_tq_attn_append"):
 TWO_SIGNS = 1       # FA_TQ_TWO_SIGNS: R = D2 H D1 / sqrt(128)
 NORM_CORRECT = 2    # FA_TQ_NORM_CORRECT: stored norm n / ||c[codes]|| (encode)
 WHOLE_VECTOR = 4    # FA_TQ_WHOLE_VECTOR: one rotation over head_dim, one norm per vector
-ATTN_VECTOR_ALU = 8  # FA_TQ_ATTN_VECTOR_ALU: the vector-ALU attention kernels at any group size
+ATTN_VECTOR_ALU = 8  # FA_TQ_ATTN_VECTOR_ALU: the vector-ALU attention kernels (groups up to 16)
 
 
 def _with_flags(lib, name, args, flags, seed_at):

@@ -86,6 +86,15 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
+// Super tiles of codes in flight beyond the one processed (2- and 4-bit values): three
+// when a wave's share of a split is long, one when it is at most FATQ_ATTN_SHALLOW_TILES
+// super tiles (a deep prefetch there only delays every wave's first codes).
+#ifndef FATQ_ATTN_DEPTH
+#define FATQ_ATTN_DEPTH 3
+#endif
+#ifndef FATQ_ATTN_SHALLOW_TILES
+#define FATQ_ATTN_SHALLOW_TILES 16
+#endif
 #ifndef FATQ_ATTN_WANT_WG
 #define FATQ_ATTN_WANT_WG 256
 #endif
@@ -417,13 +426,13 @@ __device__ __forceinline__ Rows make_rows(const AttnLaunch& a, int64_t kvb, int 
 
 // VSH: key and value codebooks are identical 4-bit tables, so the key rows serve both.
 // GT: the group size G as a compile-time constant (1, 2, 4, 8), or 0 (runtime).
-template <int KB, int VB, bool VSH, int GT>
+template <int KB, int VB, bool VSH, int GT, int DEPTH>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnLaunch a, KTable tk,
                                                                 KTable tv, SignWords sw) {
   constexpr bool V2 = VB == 2;
   // super tiles of codes in flight beyond the one processed (3-bit values: their larger
   // register sets leave room for one)
-  constexpr int kDepth = VB == 3 ? 1 : 3;
+  constexpr int kDepth = VB == 3 ? 1 : DEPTH;
   // the rows, and afterwards the waves' partial outputs for the merge in LDS
   constexpr int kMergeBytes = sizeof(float) * kWaves * 2 * kMaxG * QK;
   constexpr int kTab = (VSH ? kVBase : 2 * kVBase) > kMergeBytes ? (VSH ? kVBase : 2 * kVBase)
@@ -1059,10 +1068,23 @@ template <int GT>
 void launch_g(const AttnLaunch& a, const KTable& tk, const KTable& tv, const SignWords& sw,
               hipStream_t stream, bool same) {
   const dim3 g1(a.n_split, a.hkv * a.kv_div, a.batch), b1(kThreads);
-#define FATQ_ATT(K, V) \
-  hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT>), g1, b1, 0, stream, a, tk, tv, sw)
-#define FATQ_ATS(K) \
-  hipLaunchKernelGGL((attn_mfma_kernel<K, K, true, GT>), g1, b1, 0, stream, a, tk, tv, sw)
+  const bool shallow = a.chunk <= FATQ_ATTN_SHALLOW_TILES * kWaves * kST;
+  constexpr int kDeep = FATQ_ATTN_DEPTH;
+  // (3-bit values take one super tile in flight either way: one instantiation)
+#define FATQ_ATT(K, V)                                                                         \
+  if ((V) == 3 || shallow)                                                                    \
+    hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT, 1>), g1, b1, 0, stream, a, tk, tv,  \
+                       sw);                                                                   \
+  else                                                                                        \
+    hipLaunchKernelGGL((attn_mfma_kernel<K, V, false, GT, (V) == 3 ? 1 : kDeep>), g1, b1, 0,  \
+                       stream, a, tk, tv, sw)
+#define FATQ_ATS(K)                                                                            \
+  if (shallow)                                                                                \
+    hipLaunchKernelGGL((attn_mfma_kernel<K, K, true, GT, 1>), g1, b1, 0, stream, a, tk, tv,   \
+                       sw);                                                                   \
+  else                                                                                        \
+    hipLaunchKernelGGL((attn_mfma_kernel<K, K, true, GT, kDeep>), g1, b1, 0, stream, a, tk,   \
+                       tv, sw)
   // shared key/value rows for identical 4-bit tables (3-bit key rows have their own layout)
   if (same && tk.bits == 4) {
     FATQ_ATS(4);

@@ -917,7 +917,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeLaunch d, KTable
 constexpr int64_t kEncodeWGs = FATQ_ENCODE_WGS;
 // the workgroup budget of each half (keys, values) of an encode of both
 #ifndef FATQ_ENCODE_PAIR_WGS
-#define FATQ_ENCODE_PAIR_WGS (FATQ_ENCODE_WGS / 2)
+#define FATQ_ENCODE_PAIR_WGS FATQ_ENCODE_WGS
 #endif
 constexpr int64_t kEncodePairWGs = FATQ_ENCODE_PAIR_WGS;
 

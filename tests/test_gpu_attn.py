@@ -326,3 +326,24 @@ def test_attn_sink_and_faint_tail(gpu_lib):
     say(f"sink + faint tail: max abs err {err:.3e} (|out| max {np.max(np.abs(ref)):.2f})")
     assert err <= ATTN_MAX_ABS, err
     assert err <= ATTN_MAX_ABS / 2, f"no margin left: {err}"
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (2, 4), (3, 4), (4, 4)])
+def test_attn_long_splits_deep_prefetch(gpu_lib, kb, vb):
+    """Splits long enough that every wave streams more than 16 super tiles (the kernels
+    then keep three super tiles of codes in flight instead of one): 4 sequences x 8 KV
+    heads x 40000 slots (chunks of 5120 tokens), ragged lengths, seeded random codes;
+    the query heads of four (sequence, KV head) slices against the fused fp64
+    attention."""
+    torch = _torch()
+    B, Hq, Hkv, T = 4, 16, 8, 40000
+    lens = [40000, 38001, 20003, 4097]
+    say(f"attn deep prefetch K{kb}V{vb}")
+    kp, kn = _random_cache(B, Hkv, T, kb, 100 + kb)
+    vp, vn = _random_cache(B, Hkv, T, vb, 200 + vb)
+    rng = np.random.default_rng(kb * 10 + vb)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32)).to(torch.bfloat16)
+    grp = Hq // Hkv
+    heads = [(b, g * grp + i) for b, g in ((0, 3), (1, 0), (2, 5), (3, 7)) for i in range(grp)]
+    _run(gpu_lib, q.cuda(), kp, kn, vp, vn, lens, kb, vb, 1 / np.sqrt(128), heads=heads,
+         where=f"deep prefetch K{kb}V{vb}")

@@ -240,6 +240,47 @@ def attention_graph(fa, cbk, cbv, seed, q, caches, lens, scale, out, ws, nbytes,
             "timing": f"median over {replays} replays of a HIP graph of {n_calls} calls"}
 
 
+def large_groups(fa, seed) -> dict:
+    """Decode attention at group sizes above the matrix-core tile's 8 query heads (the
+    group split over workgroups per KV head, each reading that KV head's codes): 1 x 8
+    KV heads x 32768 slots with 128 query heads (G = 16; also on the vector-ALU
+    kernels) and 4 x 1 KV head x 65536 slots with 32 query heads (multi-query, G = 32).
+    K4/V2 caches of seeded random codes with unit norms, copies over >= 768 MB, HIP
+    graph per call; algorithmic bytes count the cache once."""
+    import torch
+    res = {}
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    cbk, cbv = fa.codebook_init(128, 4), fa.codebook_init(128, 2)
+    for name, (B, Hq, Hkv, T) in (("g16", (1, 128, 8, 32768)), ("mqa_g32", (4, 32, 1, 65536))):
+        lens_np = np.full(B, T, np.int32)
+        nbytes = attn_bytes(lens_np, Hkv, Hq, 4, 2)
+        copies = max(1, -(-768_000_000 // nbytes))
+        caches = []
+        for _ in range(copies):
+            kc, kn = fa.cache_buffers(B, Hkv, T, 128, 4)
+            vc, vn = fa.cache_buffers(B, Hkv, T, 128, 2)
+            kc.random_(0, 256, generator=gen)
+            vc.random_(0, 256, generator=gen)
+            kn.fill_(0x3C00)   # fp16 1.0
+            vn.fill_(0x3C00)
+            caches.append((kc, kn, vc, vn))
+        q = torch.randn((B, Hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        lens = torch.from_numpy(lens_np).cuda()
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+        ws = fa.attn_workspace(B, Hq, Hkv, T, 128)
+        rec = attention_graph(fa, cbk, cbv, seed, q, caches, lens, 1 / np.sqrt(128), out, ws,
+                              nbytes)
+        rec["shape"] = f"{B} x {Hkv} KV heads x {T} slots, {Hq} query heads (G = {Hq // Hkv})"
+        rec["copies"] = copies
+        if Hq // Hkv <= 16:
+            rec["vector_alu"] = attention_graph(fa, cbk, cbv, seed, q, caches, lens,
+                                                1 / np.sqrt(128), out, ws, nbytes,
+                                                flags=fa.ATTN_VECTOR_ALU, n_calls=4, replays=3)
+        res[name] = rec
+        del caches, ws
+    return res
+
+
 def cold_hbm(calls, n=20, flush_bytes=1 << 30) -> dict:
     """Cold-HBM time per call: before each call a 1 GiB scratch buffer is written (the
     last-level cache then holds none of the call's data), and only the call itself lies
@@ -968,6 +1009,7 @@ def main():
                                                         scale)
         rec["prefill_encode_d256"] = prefill_whole(fa, seed)
         rec["attention_other_workloads"] = other_attention(fa, seed)
+        rec["attention_large_groups"] = large_groups(fa, seed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = _cpu_baseline_child(workers)
     print(json.dumps(rec), flush=True)
